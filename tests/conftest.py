@@ -1,0 +1,30 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: large CPU work (full-size oracle runs)")
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    if not os.path.exists(oracle.LIB):
+        oracle.build()
+    return oracle.Oracle(threads=1)
+
+
+@pytest.fixture(scope="session")
+def orc_mt():
+    import oracle
+    if not os.path.exists(oracle.LIB):
+        oracle.build()
+    o = oracle.Oracle(threads=min(8, os.cpu_count() or 1))
+    return o
