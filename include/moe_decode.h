@@ -1,0 +1,192 @@
+/* moe_decode.h -- C ABI of libmoe_decode, the gfx950 (MI355X) library for the
+ * decode / short-chunk prefill forward of a block-quantized feed-forward or
+ * mixture-of-experts layer.
+ *
+ * The operations follow the pages' statement of the problem:
+ *   - a quantized matrix-vector product over Q8_0 / Q4_0 blocks (the Camelid
+ *     README, "Engine" and "Supported" sections: Q8_0 weights and Q4_0
+ *     "wire GEMVs" checked against a CPU oracle) and over int8 / packed int4
+ *     weights with one scale per row (the colibri summary, "model execution
+ *     and memory tiers");
+ *   - a router with top-k expert selection whose exact ties go to the lower
+ *     expert index (the Camelid README, "Experimental lanes");
+ *   - the MoE block: router -> top-k routed experts -> gated FFN (GeGLU) per
+ *     selected expert -> combine, plus a dense shared-expert branch (the
+ *     Camelid README, "Gemma 4": 128 experts, sparse top-8 plus a dense shared
+ *     expert; the TurboFieldfare summary, "memory and expert streaming":
+ *     router-chosen experts, shared branch computed alongside, prefill in
+ *     chunks of at most 128 tokens reusing each expert across rows).
+ *
+ * Conventions (every entry point):
+ *   - Pointers marked "device" are HIP device pointers, "host" are host
+ *     pointers.  The caller allocates and owns every buffer and the stream; the
+ *     library never allocates, frees or synchronizes.  Work is enqueued on
+ *     `stream` (NULL = the null stream) and completes asynchronously.
+ *   - Every argument is validated on the host before anything is enqueued; a
+ *     call that returns an error has enqueued nothing and written nothing.
+ *     Unsupported shapes return MD_ERR_UNSUPPORTED: there is no fallback.
+ *   - Device data pointers must be 16-byte aligned (MD_ERR_ALIGNMENT).
+ *   - md_last_error_detail() returns a thread-local message describing the
+ *     last non-OK return on the calling thread.
+ *   - Asynchronous faults surface through the HIP runtime on `stream`.
+ *   - Results are deterministic: no float atomics; fixed reduction orders.
+ *   - Calls that take a workspace may not overlap on the same workspace.
+ *
+ * Supported shapes: hidden / input widths (cols) are multiples of 256 and at
+ * most 16384; rows 1..65536; E <= 256; 1 <= k <= 8; T <= 128 tokens per
+ * layer call (longer prompts are split by the caller into chunks of at most
+ * 128 tokens); batch <= 8 for md_qgemv.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MD_ABI_VERSION 1
+
+typedef enum md_status {
+    MD_OK = 0,
+    MD_ERR_INVALID_ARG = 1,   /* null pointer, bad enum value                 */
+    MD_ERR_SHAPE = 2,         /* inconsistent dimensions                      */
+    MD_ERR_UNSUPPORTED = 3,   /* valid but outside the supported set          */
+    MD_ERR_ALIGNMENT = 4,     /* a device pointer is not 16-byte aligned      */
+    MD_ERR_WORKSPACE = 5,     /* workspace missing or too small               */
+    MD_ERR_HIP = 6            /* the HIP runtime reported a launch error      */
+} md_status;
+
+/* Weight formats.  Canonical layouts (as stored in GGUF-style files; the
+ * oracle reads these):
+ *   MD_Q8_0   rows of cols/32 blocks of 34 bytes: fp16 d (little-endian) then
+ *             32 int8 q;  w = d * q.
+ *   MD_Q4_0   rows of cols/32 blocks of 18 bytes: fp16 d then 16 bytes qs;
+ *             weight j (0..15) is the low nibble n of qs[j], weight j+16 the
+ *             high nibble;  w = d * (n - 8).
+ *   MD_I8_ROW rows of cols int8 q; one fp32 scale s per row;  w = s * q.
+ *   MD_I4_ROW rows of cols/2 bytes; weight 2j is the low nibble of byte j and
+ *             2j+1 the high nibble, two's complement in [-8, 7]; one fp32
+ *             scale s per row;  w = s * v.
+ * Device layout (what every compute entry point reads; produced from the
+ * canonical layout by md_prepare_layout, same byte count, same row stride):
+ *   MD_Q8_0   per row: the cols int8 q of all blocks in order, then the
+ *             cols/32 fp16 scales in order.
+ *   MD_Q4_0   per row: the 16-byte qs of all blocks in order, then the
+ *             cols/32 fp16 scales in order.
+ *   MD_I8_ROW, MD_I4_ROW: identical to the canonical layout.
+ * Every row therefore starts a run of 16-byte quant chunks that a wavefront
+ * streams with coalesced 16-byte loads, scales kept out of the way. */
+typedef enum md_qtype { MD_Q8_0 = 1, MD_Q4_0 = 2, MD_I8_ROW = 3, MD_I4_ROW = 4 } md_qtype;
+
+typedef enum md_xtype { MD_X_F32 = 0, MD_X_BF16 = 1 } md_xtype;
+
+/* act(a) * u with act = tanh-form GELU (GeGLU) or SiLU (SwiGLU). */
+typedef enum md_act { MD_ACT_GELU_TANH = 0, MD_ACT_SILU = 1 } md_act;
+
+/* A quantized matrix (rows = outputs, cols = inputs), device layout. */
+typedef struct md_qmatrix {
+    int32_t type;              /* md_qtype                                    */
+    int32_t rows, cols;
+    const void *q;             /* device: rows * md_row_bytes(type, cols)     */
+    const float *row_scale;    /* device: rows fp32 (the *_ROW types), else NULL */
+} md_qmatrix;
+
+/* A dense gated FFN: y = down( act(gate x) * (up x) ).
+ * gate, up: F x H;  down: H x F;  all three of one type. */
+typedef struct md_ffn {
+    int32_t act;               /* md_act                                      */
+    md_qmatrix gate, up, down;
+} md_ffn;
+
+/* One MoE layer.  The E experts of each projection are stored expert-major
+ * and contiguous: expert e's gate matrix starts at gate_q + e * (F rows of
+ * md_row_bytes(type, H)), its scales (the *_ROW types) at gate_scale + e*F;
+ * likewise up (F x H) and down (H x F, scales at down_scale + e*H). */
+typedef struct md_moe_layer {
+    int32_t H, F, E, k;
+    int32_t act;               /* md_act                                      */
+    int32_t type;              /* md_qtype of the routed experts              */
+    const void *gate_q, *up_q, *down_q;                /* device              */
+    const float *gate_scale, *up_scale, *down_scale;   /* device or NULL      */
+    const float *W_r;          /* device: E x H fp32 router weights           */
+    const float *router_bias;  /* device: E fp32, or NULL                     */
+    int32_t has_shared;        /* 1: add a dense shared expert (gate 1)       */
+    md_ffn shared;             /* its gate/up F_s x H, down H x F_s           */
+} md_moe_layer;
+
+int32_t md_abi_version(void);
+const char *md_status_string(md_status s);
+const char *md_last_error_detail(void);
+
+/* Bytes of one row in either layout (scales of the *_ROW types excluded);
+ * -1 if cols is not valid for the type. */
+int64_t md_row_bytes(int32_t type, int32_t cols);
+
+/* Convert `count` consecutive matrices (rows x cols each) from the canonical
+ * layout at `src` to the device layout at `dst` (both device, same size,
+ * must not overlap).  One-time, at weight-load. */
+md_status md_prepare_layout(int32_t type, int32_t rows, int32_t cols, int32_t count,
+                            const void *src, void *dst, hipStream_t stream);
+
+/* y[b][r] = sum_c w[r][c] * x[b][c] for b < batch (batch 1..8).
+ * x: device, batch x cols, fp32 or bf16 (xtype); y: device, batch x rows fp32.
+ * Accumulation in fp32.  Needs md_qgemv_workspace_size() bytes of workspace
+ * (may be 0, then workspace may be NULL). */
+md_status md_qgemv_workspace_size(const md_qmatrix *W /*host*/, int32_t batch, size_t *bytes /*host*/);
+md_status md_qgemv(const md_qmatrix *W /*host*/, const void *x, int32_t xtype, int32_t batch, float *y,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Router for T tokens: logits l[t][e] = sum_c W_r[e][c] x[t][c] (+ bias[e]),
+ * accumulated in fp64 and rounded to fp32; idx[t][0..k-1] = the k largest
+ * logits in descending order, exact ties broken by the lower expert index
+ * (-0 equals +0); gates[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over
+ * the selected k.  idx (int32 T x k), gates (fp32 T x k) and logits (fp32
+ * T x E, may be NULL) are device buffers.  Non-finite logits are outside the
+ * contract (the selection is then unspecified). */
+md_status md_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, size_t *bytes /*host*/);
+md_status md_moe_route_topk(const float *x, int32_t T, int32_t H, const float *W_r, const float *bias,
+                            int32_t E, int32_t k, int32_t *idx, float *gates, float *logits,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense gated FFN for T tokens (1..128): x, y device T x H fp32. */
+md_status md_ffn_workspace_size(const md_ffn *f /*host*/, int32_t T, size_t *bytes /*host*/);
+md_status md_ffn_forward(const md_ffn *f /*host*/, const float *x, int32_t T, float *y,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The MoE layer for T tokens (1..128):
+ *   y[t] = sum_{j<k} gates[t][j] * FFN_{idx[t][j]}(x[t])  (+ shared FFN(x[t]))
+ * x, y: device T x H fp32.  idx_out (int32 T x k) and gates_out (fp32 T x k)
+ * receive the routing when non-NULL.  Only the selected experts' weight bytes
+ * are read; an expert selected by several tokens is read once per call. */
+md_status md_moe_workspace_size(const md_moe_layer *L /*host*/, int32_t T, size_t *bytes /*host*/);
+md_status md_moe_layer_forward(const md_moe_layer *L /*host*/, const float *x, int32_t T, float *y,
+                               int32_t *idx_out, float *gates_out,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Measurement variant of md_moe_layer_forward: identical work and results;
+ * additionally records `start` on `stream` just before the launches of stage
+ * `stage` and `stop` just after them (HIP events created by the caller), so
+ * the elapsed time between the two events is that stage's time on the
+ * stream.  A stage the call does not run (the shared expert of a layer
+ * without one) records both events back to back. */
+typedef enum md_stage {
+    MD_STAGE_SHARED = 0,      /* dense shared-expert FFN                      */
+    MD_STAGE_ROUTER = 1,      /* router logits                                */
+    MD_STAGE_SELECT = 2,      /* top-k, gates, expert dispatch                */
+    MD_STAGE_GATEUP = 3,      /* selected experts' gate/up + activation       */
+    MD_STAGE_DOWN = 4,        /* selected experts' down projection            */
+    MD_STAGE_COMBINE = 5      /* gate-weighted combine (+ shared)             */
+} md_stage;
+md_status md_moe_layer_forward_timed(const md_moe_layer *L /*host*/, const float *x, int32_t T, float *y,
+                                     int32_t *idx_out, float *gates_out,
+                                     void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                     int32_t stage, hipEvent_t start, hipEvent_t stop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,374 @@
+// abi.cpp -- the C entry points of libmoe_decode: host-side validation (every
+// check runs before anything is enqueued), workspace layout, and the launch
+// sequence of each operation.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe_decode.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+md_status fail(md_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+md_status ok() {
+  g_detail[0] = 0;
+  return MD_OK;
+}
+
+md_status hip_fail(hipError_t e, const char* what) {
+  return fail(MD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_type(int32_t t) { return t >= MD_Q8_0 && t <= MD_I4_ROW; }
+bool row_type(int32_t t) { return t == MD_I8_ROW || t == MD_I4_ROW; }
+
+constexpr int kMaxCols = 16384;
+constexpr int kMaxRows = 65536;
+constexpr int kMaxT = 128;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+constexpr int kMaxBatch = 8;
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+md_status check_width(const char* what, int32_t n) {
+  if (n <= 0) return fail(MD_ERR_SHAPE, "%s = %d must be positive", what, n);
+  if (n % 256 || n > kMaxCols)
+    return fail(MD_ERR_UNSUPPORTED, "%s = %d: supported widths are multiples of 256 up to %d", what, n, kMaxCols);
+  return MD_OK;
+}
+
+md_status check_qmatrix(const char* what, const md_qmatrix* W) {
+  if (!W) return fail(MD_ERR_INVALID_ARG, "%s: null matrix descriptor", what);
+  if (!valid_type(W->type)) return fail(MD_ERR_INVALID_ARG, "%s: unknown type %d", what, W->type);
+  if (W->rows <= 0 || W->cols <= 0) return fail(MD_ERR_SHAPE, "%s: rows %d cols %d", what, W->rows, W->cols);
+  if (W->rows > kMaxRows) return fail(MD_ERR_UNSUPPORTED, "%s: rows %d > %d", what, W->rows, kMaxRows);
+  md_status s = check_width(what, W->cols);
+  if (s != MD_OK) return s;
+  if (!W->q) return fail(MD_ERR_INVALID_ARG, "%s: null weights", what);
+  if (!aligned16(W->q)) return fail(MD_ERR_ALIGNMENT, "%s: weights not 16-byte aligned", what);
+  if (row_type(W->type)) {
+    if (!W->row_scale) return fail(MD_ERR_INVALID_ARG, "%s: per-row type without row_scale", what);
+    if (!aligned16(W->row_scale)) return fail(MD_ERR_ALIGNMENT, "%s: row_scale not 16-byte aligned", what);
+  }
+  return MD_OK;
+}
+
+md_status check_ffn(const md_ffn* f, int32_t H) {
+  if (!f) return fail(MD_ERR_INVALID_ARG, "null FFN descriptor");
+  if (f->act != MD_ACT_GELU_TANH && f->act != MD_ACT_SILU) return fail(MD_ERR_INVALID_ARG, "unknown act %d", f->act);
+  md_status s;
+  if ((s = check_qmatrix("ffn.gate", &f->gate)) != MD_OK) return s;
+  if ((s = check_qmatrix("ffn.up", &f->up)) != MD_OK) return s;
+  if ((s = check_qmatrix("ffn.down", &f->down)) != MD_OK) return s;
+  if (f->gate.type != f->up.type || f->gate.type != f->down.type)
+    return fail(MD_ERR_UNSUPPORTED, "ffn: gate/up/down must share one type");
+  const int F = f->gate.rows;
+  if (f->gate.cols != H || f->up.cols != H || f->up.rows != F || f->down.rows != H || f->down.cols != F)
+    return fail(MD_ERR_SHAPE, "ffn: gate/up must be F x H and down H x F (H=%d)", H);
+  return check_width("ffn F", F);
+}
+
+int max_active(int T, int E, int k) { return T * k < E ? T * k : E; }
+
+// ---- MoE workspace layout ------------------------------------------------
+struct MoeWs {
+  size_t part, logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
+  int S;
+};
+
+MoeWs moe_ws(const md_moe_layer* L, int T) {
+  MoeWs w{};
+  const int E = L->E, k = L->k, H = L->H, F = L->F;
+  w.S = md::router_splits(H, E);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.part = take(sizeof(double) * T * E * w.S);
+  w.logits = take(sizeof(float) * T * E);
+  w.idx = take(sizeof(int) * T * k);
+  w.gates = take(sizeof(float) * T * k);
+  w.n_active = take(sizeof(int));
+  w.active_e = take(sizeof(int) * E);
+  w.active_off = take(sizeof(int) * (E + 1));
+  w.pairs = take(sizeof(int) * T * k);
+  w.pos = take(sizeof(int) * T * k);
+  w.h = take(sizeof(float) * (size_t)T * k * F);
+  w.o = take(sizeof(float) * (size_t)T * k * H);
+  if (L->has_shared) {
+    w.h_s = take(sizeof(float) * (size_t)T * L->shared.gate.rows);
+    w.y_s = take(sizeof(float) * (size_t)T * H);
+  }
+  w.total = off;
+  return w;
+}
+
+md_status check_moe(const md_moe_layer* L, int32_t T) {
+  if (!L) return fail(MD_ERR_INVALID_ARG, "null layer descriptor");
+  if (T <= 0) return fail(MD_ERR_SHAPE, "T = %d must be positive", T);
+  if (T > kMaxT) return fail(MD_ERR_UNSUPPORTED, "T = %d: at most %d tokens per call (split longer chunks)", T, kMaxT);
+  md_status s;
+  if ((s = check_width("H", L->H)) != MD_OK) return s;
+  if ((s = check_width("F", L->F)) != MD_OK) return s;
+  if (L->E <= 0 || L->k <= 0) return fail(MD_ERR_SHAPE, "E = %d, k = %d", L->E, L->k);
+  if (L->k > L->E) return fail(MD_ERR_SHAPE, "k = %d > E = %d", L->k, L->E);
+  if (L->E > kMaxE || L->k > kMaxK) return fail(MD_ERR_UNSUPPORTED, "E <= %d and k <= %d are supported", kMaxE, kMaxK);
+  if (L->act != MD_ACT_GELU_TANH && L->act != MD_ACT_SILU) return fail(MD_ERR_INVALID_ARG, "unknown act %d", L->act);
+  if (!valid_type(L->type)) return fail(MD_ERR_INVALID_ARG, "unknown expert type %d", L->type);
+  if (!L->gate_q || !L->up_q || !L->down_q || !L->W_r) return fail(MD_ERR_INVALID_ARG, "null expert or router weights");
+  if (!aligned16(L->gate_q) || !aligned16(L->up_q) || !aligned16(L->down_q) || !aligned16(L->W_r) ||
+      (L->router_bias && !aligned16(L->router_bias)))
+    return fail(MD_ERR_ALIGNMENT, "expert/router pointers must be 16-byte aligned");
+  if (row_type(L->type)) {
+    if (!L->gate_scale || !L->up_scale || !L->down_scale) return fail(MD_ERR_INVALID_ARG, "per-row type without scales");
+    if (!aligned16(L->gate_scale) || !aligned16(L->up_scale) || !aligned16(L->down_scale))
+      return fail(MD_ERR_ALIGNMENT, "scales must be 16-byte aligned");
+  }
+  if (L->has_shared) {
+    if ((s = check_ffn(&L->shared, L->H)) != MD_OK) return s;
+    if (L->shared.act != L->act) return fail(MD_ERR_UNSUPPORTED, "shared expert must use the layer's activation");
+  }
+  return MD_OK;
+}
+
+md_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MD_OK;
+  if (!ws || have < need) return fail(MD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, have);
+  if (!aligned16(ws)) return fail(MD_ERR_ALIGNMENT, "workspace not 16-byte aligned");
+  return MD_OK;
+}
+
+// dense FFN (or shared expert) through the MoE kernels with the identity dispatch
+md_status run_ffn(const md_ffn* f, const float* x, int T, float* h, float* y, hipStream_t st) {
+  const int H = f->gate.cols, F = f->gate.rows, fmt = f->gate.type;
+  md::Disp d{nullptr, nullptr, nullptr, nullptr, 1, T};
+  md::GemvCfg cg = md::gateup_config(fmt, F, H, 1, T);
+  hipError_t e = md::launch_gateup(fmt, cg, static_cast<const uint8_t*>(f->gate.q), static_cast<const uint8_t*>(f->up.q),
+                                   f->gate.row_scale, f->up.row_scale, 0, F, H, f->act, d, x, h, st);
+  if (e != hipSuccess) return hip_fail(e, "ffn gate/up launch");
+  md::GemvCfg cd = md::down_config(fmt, H, F, 1, T);
+  e = md::launch_down(fmt, cd, static_cast<const uint8_t*>(f->down.q), f->down.row_scale, 0, H, F, d, h, y, st);
+  if (e != hipSuccess) return hip_fail(e, "ffn down launch");
+  return MD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t md_abi_version(void) { return MD_ABI_VERSION; }
+
+const char* md_status_string(md_status s) {
+  switch (s) {
+    case MD_OK: return "ok";
+    case MD_ERR_INVALID_ARG: return "invalid argument";
+    case MD_ERR_SHAPE: return "inconsistent shape";
+    case MD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MD_ERR_ALIGNMENT: return "misaligned pointer";
+    case MD_ERR_WORKSPACE: return "workspace too small";
+    case MD_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* md_last_error_detail(void) { return g_detail; }
+
+int64_t md_row_bytes(int32_t type, int32_t cols) {
+  if (!valid_type(type) || cols <= 0 || cols % 32) return -1;
+  return md::row_bytes(type, cols);
+}
+
+md_status md_prepare_layout(int32_t type, int32_t rows, int32_t cols, int32_t count, const void* src, void* dst,
+                            hipStream_t stream) {
+  if (!valid_type(type)) return fail(MD_ERR_INVALID_ARG, "unknown type %d", type);
+  if (rows <= 0 || count <= 0) return fail(MD_ERR_SHAPE, "rows %d count %d", rows, count);
+  md_status s = check_width("cols", cols);
+  if (s != MD_OK) return s;
+  if (!src || !dst) return fail(MD_ERR_INVALID_ARG, "null buffer");
+  if (!aligned16(src) || !aligned16(dst)) return fail(MD_ERR_ALIGNMENT, "buffers must be 16-byte aligned");
+  const int64_t bytes = (int64_t)rows * count * md::row_bytes(type, cols);
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (a < b + bytes && b < a + bytes) return fail(MD_ERR_INVALID_ARG, "src and dst overlap");
+  hipError_t e = md::launch_prepare_layout(type, rows, cols, count, src, dst, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "prepare_layout launch");
+}
+
+md_status md_qgemv_workspace_size(const md_qmatrix* W, int32_t batch, size_t* bytes) {
+  md_status s = check_qmatrix("W", W);
+  if (s != MD_OK) return s;
+  if (!bytes) return fail(MD_ERR_INVALID_ARG, "null bytes");
+  if (batch <= 0) return fail(MD_ERR_SHAPE, "batch %d", batch);
+  if (batch > kMaxBatch) return fail(MD_ERR_UNSUPPORTED, "batch %d > %d", batch, kMaxBatch);
+  md::GemvCfg c = md::qgemv_config(W->type, W->rows, W->cols, batch);
+  *bytes = c.S > 1 ? align256(sizeof(float) * (size_t)c.S * batch * W->rows) : 0;
+  return ok();
+}
+
+md_status md_qgemv(const md_qmatrix* W, const void* x, int32_t xtype, int32_t batch, float* y, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  md_status s = md_qgemv_workspace_size(W, batch, &need);
+  if (s != MD_OK) return s;
+  if (xtype != MD_X_F32 && xtype != MD_X_BF16) return fail(MD_ERR_INVALID_ARG, "unknown xtype %d", xtype);
+  if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
+  if (!aligned16(x) || !aligned16(y)) return fail(MD_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
+  if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
+  md::GemvCfg c = md::qgemv_config(W->type, W->rows, W->cols, batch);
+  hipError_t e = md::launch_qgemv(W->type, xtype, c, static_cast<const uint8_t*>(W->q), W->row_scale, W->rows, W->cols,
+                                  x, batch, y, static_cast<float*>(workspace), stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "qgemv launch");
+}
+
+md_status md_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, size_t* bytes) {
+  if (!bytes) return fail(MD_ERR_INVALID_ARG, "null bytes");
+  if (T <= 0 || E <= 0 || k <= 0) return fail(MD_ERR_SHAPE, "T %d E %d k %d", T, E, k);
+  if (k > E) return fail(MD_ERR_SHAPE, "k = %d > E = %d", k, E);
+  if (T > kMaxT || E > kMaxE || k > kMaxK) return fail(MD_ERR_UNSUPPORTED, "T <= %d, E <= %d, k <= %d", kMaxT, kMaxE, kMaxK);
+  md_status s = check_width("H", H);
+  if (s != MD_OK) return s;
+  *bytes = align256(sizeof(double) * (size_t)T * E * md::router_splits(H, E));
+  return ok();
+}
+
+md_status md_moe_route_topk(const float* x, int32_t T, int32_t H, const float* W_r, const float* bias, int32_t E,
+                            int32_t k, int32_t* idx, float* gates, float* logits, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  md_status s = md_route_workspace_size(T, H, E, k, &need);
+  if (s != MD_OK) return s;
+  if (!x || !W_r || !idx || !gates) return fail(MD_ERR_INVALID_ARG, "null x, W_r, idx or gates");
+  if (!aligned16(x) || !aligned16(W_r) || !aligned16(idx) || !aligned16(gates) || (bias && !aligned16(bias)) ||
+      (logits && !aligned16(logits)))
+    return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
+  const int S = md::router_splits(H, E);
+  double* part = static_cast<double*>(workspace);
+  hipError_t e = md::launch_router(x, T, H, W_r, E, S, part, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  e = md::launch_route_finalize(part, S, bias, T, E, k, logits, idx, gates, nullptr, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "route finalize launch");
+}
+
+md_status md_ffn_workspace_size(const md_ffn* f, int32_t T, size_t* bytes) {
+  if (!f) return fail(MD_ERR_INVALID_ARG, "null FFN descriptor");
+  md_status s = check_ffn(f, f->gate.cols);
+  if (s != MD_OK) return s;
+  if (!bytes) return fail(MD_ERR_INVALID_ARG, "null bytes");
+  if (T <= 0) return fail(MD_ERR_SHAPE, "T %d", T);
+  if (T > kMaxT) return fail(MD_ERR_UNSUPPORTED, "T %d > %d", T, kMaxT);
+  *bytes = align256(sizeof(float) * (size_t)T * f->gate.rows);
+  return ok();
+}
+
+md_status md_ffn_forward(const md_ffn* f, const float* x, int32_t T, float* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  md_status s = md_ffn_workspace_size(f, T, &need);
+  if (s != MD_OK) return s;
+  if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
+  if (!aligned16(x) || !aligned16(y)) return fail(MD_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
+  if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
+  s = run_ffn(f, x, T, static_cast<float*>(workspace), y, stream);
+  return s == MD_OK ? ok() : s;
+}
+
+md_status md_moe_workspace_size(const md_moe_layer* L, int32_t T, size_t* bytes) {
+  md_status s = check_moe(L, T);
+  if (s != MD_OK) return s;
+  if (!bytes) return fail(MD_ERR_INVALID_ARG, "null bytes");
+  *bytes = moe_ws(L, T).total;
+  return ok();
+}
+
+static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
+                             float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             int32_t stage, hipEvent_t ev0, hipEvent_t ev1) {
+  md_status s = check_moe(L, T);
+  if (s != MD_OK) return s;
+  if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
+  if (!aligned16(x) || !aligned16(y) || (idx_out && !aligned16(idx_out)) || (gates_out && !aligned16(gates_out)))
+    return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  if (stage >= 0 && (stage > MD_STAGE_COMBINE || !ev0 || !ev1))
+    return fail(MD_ERR_INVALID_ARG, "timed call needs a stage in 0..5 and two events");
+  const MoeWs w = moe_ws(L, T);
+  if ((s = check_ws(workspace, workspace_bytes, w.total)) != MD_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  auto P = [&](size_t off) { return static_cast<void*>(ws + off); };
+  const int H = L->H, F = L->F, E = L->E, k = L->k, fmt = L->type;
+  int* idx = idx_out ? idx_out : static_cast<int*>(P(w.idx));
+  float* gates = gates_out ? gates_out : static_cast<float*>(P(w.gates));
+  float* y_s = L->has_shared ? static_cast<float*>(P(w.y_s)) : nullptr;
+  hipError_t e = hipSuccess;
+  auto mark = [&](int st, hipEvent_t ev) -> bool {
+    if (st != stage) return true;
+    e = hipEventRecord(ev, stream);
+    return e == hipSuccess;
+  };
+
+  // shared expert: independent of the routing, enqueued first
+  if (!mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
+  if (L->has_shared) {
+    s = run_ffn(&L->shared, x, T, static_cast<float*>(P(w.h_s)), y_s, stream);
+    if (s != MD_OK) return s;
+  }
+  if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
+  e = md::launch_router(x, T, H, L->W_r, E, w.S, static_cast<double*>(P(w.part)), stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");
+  md::DispOut dout{static_cast<int*>(P(w.n_active)), static_cast<int*>(P(w.active_e)),
+                   static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos))};
+  e = md::launch_route_finalize(static_cast<double*>(P(w.part)), w.S, L->router_bias, T, E, k,
+                                static_cast<float*>(P(w.logits)), idx, gates, &dout, stream);
+  if (e != hipSuccess) return hip_fail(e, "route finalize launch");
+  if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
+
+  md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T};
+  const int A = max_active(T, E, k);
+  const int64_t gu_bytes = (int64_t)F * md::row_bytes(fmt, H);
+  const int64_t dn_bytes = (int64_t)H * md::row_bytes(fmt, F);
+  float* h = static_cast<float*>(P(w.h));
+  float* o = static_cast<float*>(P(w.o));
+  md::GemvCfg cg = md::gateup_config(fmt, F, H, A, T);
+  e = md::launch_gateup(fmt, cg, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                        L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, x, h, stream);
+  if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+  if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
+  md::GemvCfg cd = md::down_config(fmt, H, F, A, T);
+  e = md::launch_down(fmt, cd, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, d, h, o, stream);
+  if (e != hipSuccess) return hip_fail(e, "down launch");
+  if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0)) return hip_fail(e, "event record");
+  e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, y, stream);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (!mark(MD_STAGE_COMBINE, ev1)) return hip_fail(e, "event record");
+  return ok();
+}
+
+md_status md_moe_layer_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
+                               float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr);
+}
+
+md_status md_moe_layer_forward_timed(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
+                                     float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                     int32_t stage, hipEvent_t start, hipEvent_t stop) {
+  if (stage < 0) return fail(MD_ERR_INVALID_ARG, "stage %d", stage);
+  return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, stage, start, stop);
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// common.hpp -- device helpers of libmoe_decode (gfx950, wave64).
+//
+// Weight rows are streamed in 16-byte chunks (one global_load_dwordx4 per
+// lane, consecutive lanes on consecutive chunks, so a wavefront reads 1 KiB of
+// one row per instruction).  A chunk holds:
+//   Q8_0   16 int8 weights, scale = the fp16 d of block c/2
+//   Q4_0   one block: 32 nibbles (low nibbles = weights 0..15, high = 16..31)
+//   I8_ROW 16 int8 weights (scale per row)
+//   I4_ROW 32 two's-complement nibbles, low nibble of byte b = weight 2b
+// Decoding happens in VGPRs.  int8 goes through the sign-extending byte
+// convert.  A 4-bit code is made a two's-complement nibble (Q4_0: n XOR 8 is
+// n - 8) and moved into the high half of a byte with a 0xF0F0F0F0 mask, so each
+// byte holds exactly 16 * value as an int8 and converts with the same
+// sign-extending byte convert; the factor 1/16 is folded into the scale.  No
+// offset correction is needed, so an all-zero row gives exactly zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#define MD_DEV __device__ __forceinline__
+
+namespace md {
+
+enum : int { Q8_0 = 1, Q4_0 = 2, I8_ROW = 3, I4_ROW = 4 };
+enum : int { ACT_GELU_TANH = 0, ACT_SILU = 1 };
+enum : int { XF32 = 0, XBF16 = 1 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<Q8_0>   { static constexpr int WPC = 16; static constexpr bool ROW = false; };
+template <> struct Fmt<Q4_0>   { static constexpr int WPC = 32; static constexpr bool ROW = false; };
+template <> struct Fmt<I8_ROW> { static constexpr int WPC = 16; static constexpr bool ROW = true; };
+template <> struct Fmt<I4_ROW> { static constexpr int WPC = 32; static constexpr bool ROW = true; };
+
+__host__ __device__ constexpr int64_t row_bytes(int fmt, int K) {
+  return fmt == Q8_0 ? (int64_t)K / 32 * 34
+       : fmt == Q4_0 ? (int64_t)K / 32 * 18
+       : fmt == I8_ROW ? (int64_t)K
+       : (int64_t)K / 2;
+}
+__host__ __device__ constexpr int wpc(int fmt) { return (fmt == Q8_0 || fmt == I8_ROW) ? 16 : 32; }
+__host__ __device__ constexpr int nchunks(int fmt, int K) { return K / wpc(fmt); }
+
+// Hide known bits from the optimizer so each masked byte converts with one
+// sign-extending byte convert (SDWA) instead of a bit-field extract plus a
+// convert per nibble.
+MD_DEV unsigned opaque(unsigned v) { asm volatile("" : "+v"(v)); return v; }
+
+MD_DEV u32x4 ld_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+MD_DEV float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// Scale that multiplies chunk c of a row (block formats, including the 1/16
+// of the 4-bit decode); 1 for per-row formats (their scale is applied once per
+// row, times row_post<FMT>()).
+template <int FMT>
+MD_DEV float chunk_scale(const uint8_t* row, int K, int c) {
+  if constexpr (FMT == Q8_0) {
+    return h2f(*reinterpret_cast<const uint16_t*>(row + K + 2 * (c >> 1)));
+  } else if constexpr (FMT == Q4_0) {
+    return h2f(*reinterpret_cast<const uint16_t*>(row + (K / 32) * 16 + 2 * c)) * 0.0625f;
+  } else {
+    return 1.0f;
+  }
+}
+
+template <int FMT>
+constexpr float row_post() { return FMT == I4_ROW ? 0.0625f : 1.0f; }
+
+// Load the WPC activations of chunk c (fp32 or bf16 source).
+template <int FMT, int XT>
+MD_DEV void load_x(const void* xp, int c, float* xv) {
+  constexpr int W = Fmt<FMT>::WPC;
+  if constexpr (XT == XF32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xp) + c * W);
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      float4 v = p[i];
+      xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xp) + c * W);
+#pragma unroll
+    for (int i = 0; i < W / 8; ++i) {
+      uint4 v = p[i];
+      unsigned u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[8 * i + 2 * j] = __uint_as_float(u[j] << 16);
+        xv[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// Dot product of one chunk's integer codes with its activations (the block or
+// row scale is applied by the caller).  4-bit formats return 16x the value.
+template <int FMT>
+MD_DEV float dot_chunk(u32x4 w, const float* xv) {
+  float a0 = 0.f, a1 = 0.f;
+  if constexpr (FMT == Q8_0 || FMT == I8_ROW) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      unsigned u = w[m];
+      a0 = fmaf((float)(signed char)(u), xv[4 * m], a0);
+      a1 = fmaf((float)(signed char)(u >> 8), xv[4 * m + 1], a1);
+      a0 = fmaf((float)(signed char)(u >> 16), xv[4 * m + 2], a0);
+      a1 = fmaf((float)(signed char)(u >> 24), xv[4 * m + 3], a1);
+    }
+  } else if constexpr (FMT == Q4_0) {
+    // byte b of word m: low nibble = weight 4m+b, high nibble = weight 16+4m+b
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned v = w[m] ^ 0x88888888u;                 // n - 8 as two's complement
+      const unsigned lo = opaque((v << 4) & 0xF0F0F0F0u), hi = opaque(v & 0xF0F0F0F0u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        a0 = fmaf((float)(signed char)(lo >> (8 * b)), xv[4 * m + b], a0);
+        a1 = fmaf((float)(signed char)(hi >> (8 * b)), xv[16 + 4 * m + b], a1);
+      }
+    }
+  } else {  // I4_ROW: byte b of word m: low nibble = weight 8m+2b, high = 8m+2b+1
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned lo = opaque((w[m] << 4) & 0xF0F0F0F0u), hi = opaque(w[m] & 0xF0F0F0F0u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        a0 = fmaf((float)(signed char)(lo >> (8 * b)), xv[8 * m + 2 * b], a0);
+        a1 = fmaf((float)(signed char)(hi >> (8 * b)), xv[8 * m + 2 * b + 1], a1);
+      }
+    }
+  }
+  return a0 + a1;
+}
+
+// Sum over the L consecutive lanes of a lane group (L a power of two <= 64).
+template <int L>
+MD_DEV float group_sum(float v) {
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+MD_DEV double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// tanh-form GELU and SiLU in fp32.
+MD_DEV float act_f(int act, float z) {
+  if (act == ACT_SILU) return z / (1.0f + expf(-z));
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+
+}  // namespace md

@@ -1,0 +1,402 @@
+// gemv.hip -- decode-path contractions over quantized rows (gfx950, wave64).
+//
+// One engine serves every decode-shaped contraction: a wave is split into
+// G = 64/L groups of L lanes; a group owns R rows; lane t of a group walks the
+// 16-byte chunks t, t+L, t+2L, ... of those R rows (R independent 16-byte
+// loads in flight per step), decodes them in registers and accumulates in
+// fp32 against the activations of up to B tokens.  The L partial sums of a
+// row are then combined with cross-lane shuffles.  Rows are read once per
+// pass; when an expert serves more than B tokens the pass repeats.
+//
+//   k_qgemv    dense y = W x (batch <= 8), split-K across blocks for short-N
+//              shapes with a fixed-order second pass (no atomics)
+//   k_gateup   per active expert: a = W_g x, u = W_u x, h = act(a) * u
+//   k_down     per active expert: o = W_d h
+//   k_combine  y[t] = sum_j g[t][j] * o[pos(t, j)] (+ shared), slot order
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace md {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / 64;
+
+template <int FMT, int XT, int L, int R, int B>
+MD_DEV void rows_dot(const uint8_t* const (&rowp)[R], int K, int c0, int c1, int t,
+                     const void* const (&xp)[B], float (&acc)[R][B]) {
+  constexpr int W = Fmt<FMT>::WPC;
+#pragma unroll 2
+  for (int c = c0 + t; c < c1; c += L) {
+    u32x4 w[R];
+    float sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = ld_stream(rowp[r] + 16 * (int64_t)c);
+#pragma unroll
+    for (int r = 0; r < R; ++r) sc[r] = chunk_scale<FMT>(rowp[r], K, c);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      float xv[W];
+      load_x<FMT, XT>(xp[b], c, xv);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float d = dot_chunk<FMT>(w[r], xv);
+        if constexpr (Fmt<FMT>::ROW) acc[r][b] += d;
+        else acc[r][b] = fmaf(sc[r], d, acc[r][b]);
+      }
+    }
+  }
+}
+
+template <int XT>
+MD_DEV const void* xrow(const void* x, int64_t elem) {
+  if constexpr (XT == XF32) return static_cast<const float*>(x) + elem;
+  else return static_cast<const uint16_t*>(x) + elem;
+}
+
+// ------------------------------------------------------------------ qgemv
+
+template <int FMT, int XT, int L, int R, int B>
+__global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ W, const float* __restrict__ scales,
+                                                  int N, int K, const void* __restrict__ x, int nb,
+                                                  float* __restrict__ out, int S) {
+  constexpr int G = 64 / L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane / L, t = lane % L;
+  const int row0 = ((blockIdx.x * kWaves + wave) * G + g) * R;
+  if (row0 >= N) return;
+  const int nc = nchunks(FMT, K);
+  const int cs = nc / S, c0 = blockIdx.y * cs;
+  const int64_t rb = row_bytes(FMT, K);
+  const uint8_t* rowp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rowp[r] = W + (int64_t)min(row0 + r, N - 1) * rb;
+  const void* xp[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) xp[b] = xrow<XT>(x, (int64_t)min(b, nb - 1) * K);
+  float acc[R][B];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
+  rows_dot<FMT, XT, L, R, B>(rowp, K, c0, c0 + cs, t, xp, acc);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[r][b] = group_sum<L>(acc[r][b]);
+  if (t == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + r;
+      if (row >= N) break;
+      const float s = Fmt<FMT>::ROW ? scales[row] * row_post<FMT>() : 1.0f;
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if (b < nb) out[((int64_t)blockIdx.y * nb + b) * N + row] = acc[r][b] * s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_splitk_reduce(const float* __restrict__ part, int S, int64_t n,
+                                                          float* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  float a = 0.f;
+  for (int s = 0; s < S; ++s) a += part[(int64_t)s * n + i];
+  y[i] = a;
+}
+
+static int pow2_divisor_le64(int n) {
+  int L = 64;
+  while (L > 1 && n % L) L >>= 1;
+  return L;
+}
+
+GemvCfg qgemv_config(int fmt, int N, int K, int batch) {
+  GemvCfg c{};
+  const int nc = nchunks(fmt, K);
+  c.L = pow2_divisor_le64(nc);
+  c.B = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
+  c.R = c.B <= 2 ? 4 : 2;
+  const int G = 64 / c.L;
+  c.rows_per_block = kWaves * G * c.R;
+  const int bx = (N + c.rows_per_block - 1) / c.rows_per_block;
+  // split K until the grid has enough waves to keep HBM busy
+  c.S = 1;
+  while (bx * kWaves * c.S < 2048 && nc % (2 * c.S * c.L) == 0 && c.S < 16) c.S *= 2;
+  c.grid = dim3(bx, c.S);
+  return c;
+}
+
+template <int FMT, int XT>
+static hipError_t qgemv_fx(const GemvCfg& c, const uint8_t* W, const float* s, int N, int K, const void* x,
+                           int nb, float* out, hipStream_t st) {
+#define MD_Q(L_, R_, B_) \
+  if (c.L == L_ && c.R == R_ && c.B == B_) { \
+    hipLaunchKernelGGL((k_qgemv<FMT, XT, L_, R_, B_>), c.grid, dim3(kBlock), 0, st, W, s, N, K, x, nb, out, c.S); \
+    return hipGetLastError(); }
+#define MD_QL(L_) MD_Q(L_, 4, 1) MD_Q(L_, 4, 2) MD_Q(L_, 2, 4) MD_Q(L_, 2, 8)
+  MD_QL(64) MD_QL(32) MD_QL(16) MD_QL(8)
+#undef MD_QL
+#undef MD_Q
+  return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_qgemv(int fmt, int xt, const GemvCfg& c, const uint8_t* W, const float* scales, int N, int K,
+                        const void* x, int batch, float* y, float* partial, hipStream_t st) {
+  float* out = c.S > 1 ? partial : y;
+  hipError_t e = hipErrorInvalidValue;
+#define MD_F(F_) \
+  if (fmt == F_) e = xt == XF32 ? qgemv_fx<F_, XF32>(c, W, scales, N, K, x, batch, out, st) \
+                                : qgemv_fx<F_, XBF16>(c, W, scales, N, K, x, batch, out, st);
+  MD_F(Q8_0) MD_F(Q4_0) MD_F(I8_ROW) MD_F(I4_ROW)
+#undef MD_F
+  if (e != hipSuccess || c.S == 1) return e;
+  const int64_t n = (int64_t)batch * N;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, partial, c.S,
+                     n, y);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ MoE
+
+struct ExpertRange {
+  int e, p0, p1;
+};
+
+MD_DEV bool expert_range(const Disp& d, int slot, ExpertRange& r) {
+  if (d.n_active == nullptr) {  // dense FFN: one expert, positions = tokens
+    if (slot != 0) return false;
+    r.e = 0; r.p0 = 0; r.p1 = d.T;
+    return true;
+  }
+  if (slot >= *d.n_active) return false;
+  r.e = d.active_e[slot];
+  r.p0 = d.active_off[slot];
+  r.p1 = d.active_off[slot + 1];
+  return true;
+}
+
+MD_DEV int pos_token(const Disp& d, int q) { return d.n_active == nullptr ? q : d.pairs[q] / d.k; }
+
+// Gate/up with the fused activation.  A group owns P row pairs (gate row f and
+// up row f), i.e. R = 2P streamed rows.
+template <int FMT, int L, int P, int B>
+__global__ __launch_bounds__(kBlock) void k_gateup(const uint8_t* __restrict__ gq, const uint8_t* __restrict__ uq,
+                                                   const float* __restrict__ gs, const float* __restrict__ us,
+                                                   int64_t mat_bytes, int F, int H, int act, Disp d,
+                                                   const float* __restrict__ x, float* __restrict__ h) {
+  constexpr int G = 64 / L, R = 2 * P;
+  ExpertRange er;
+  if (!expert_range(d, blockIdx.y, er)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane / L, t = lane % L;
+  const int f0 = ((blockIdx.x * kWaves + wave) * G + g) * P;
+  if (f0 >= F) return;
+  const int64_t rb = row_bytes(FMT, H);
+  const uint8_t* Gm = gq + (int64_t)er.e * mat_bytes;
+  const uint8_t* Um = uq + (int64_t)er.e * mat_bytes;
+  const uint8_t* rowp[R];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int f = min(f0 + p, F - 1);
+    rowp[p] = Gm + (int64_t)f * rb;
+    rowp[P + p] = Um + (int64_t)f * rb;
+  }
+  const int nc = nchunks(FMT, H);
+  for (int q0 = er.p0; q0 < er.p1; q0 += B) {
+    const void* xp[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) xp[b] = x + (int64_t)pos_token(d, min(q0 + b, er.p1 - 1)) * H;
+    float acc[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
+    rows_dot<FMT, XF32, L, R, B>(rowp, H, 0, nc, t, xp, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[r][b] = group_sum<L>(acc[r][b]);
+    if (t == 0) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int f = f0 + p;
+        if (f >= F) break;
+        float sg = 1.f, su = 1.f;
+        if constexpr (Fmt<FMT>::ROW) {
+          sg = gs[(int64_t)er.e * F + f] * row_post<FMT>();
+          su = us[(int64_t)er.e * F + f] * row_post<FMT>();
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          if (q0 + b < er.p1) h[(int64_t)(q0 + b) * F + f] = act_f(act, acc[p][b] * sg) * (acc[P + p][b] * su);
+      }
+    }
+  }
+}
+
+template <int FMT, int L, int R, int B>
+__global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ dq, const float* __restrict__ ds,
+                                                 int64_t mat_bytes, int H, int F, Disp d,
+                                                 const float* __restrict__ h, float* __restrict__ o) {
+  constexpr int G = 64 / L;
+  ExpertRange er;
+  if (!expert_range(d, blockIdx.y, er)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane / L, t = lane % L;
+  const int i0 = ((blockIdx.x * kWaves + wave) * G + g) * R;
+  if (i0 >= H) return;
+  const int64_t rb = row_bytes(FMT, F);
+  const uint8_t* Dm = dq + (int64_t)er.e * mat_bytes;
+  const uint8_t* rowp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rowp[r] = Dm + (int64_t)min(i0 + r, H - 1) * rb;
+  const int nc = nchunks(FMT, F);
+  for (int q0 = er.p0; q0 < er.p1; q0 += B) {
+    const void* xp[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) xp[b] = h + (int64_t)min(q0 + b, er.p1 - 1) * F;
+    float acc[R][B];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
+    rows_dot<FMT, XF32, L, R, B>(rowp, F, 0, nc, t, xp, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[r][b] = group_sum<L>(acc[r][b]);
+    if (t == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = i0 + r;
+        if (i >= H) break;
+        const float s = Fmt<FMT>::ROW ? ds[(int64_t)er.e * H + i] * row_post<FMT>() : 1.0f;
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          if (q0 + b < er.p1) o[(int64_t)(q0 + b) * H + i] = acc[r][b] * s;
+      }
+    }
+  }
+}
+
+// y[t][i] = sum_j g[t][j] * o[pos(t,j)][i]  (+ y_shared[t][i]), slot order.
+__global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o, const int* __restrict__ pos_of_pair,
+                                                    const float* __restrict__ gates, int T, int k, int H,
+                                                    const float* __restrict__ ys, float* __restrict__ y) {
+  const int H4 = H / 4;
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= (int64_t)T * H4) return;
+  const int t = (int)(i / H4), c = (int)(i % H4);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float gj = gates[t * k + j];
+    const float4 v = reinterpret_cast<const float4*>(o + (int64_t)pos_of_pair[t * k + j] * H)[c];
+    a.x = fmaf(gj, v.x, a.x); a.y = fmaf(gj, v.y, a.y); a.z = fmaf(gj, v.z, a.z); a.w = fmaf(gj, v.w, a.w);
+  }
+  if (ys) {
+    const float4 v = reinterpret_cast<const float4*>(ys + (int64_t)t * H)[c];
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  }
+  reinterpret_cast<float4*>(y + (int64_t)t * H)[c] = a;
+}
+
+static int choose_R(int rows, int G, int experts, const int* opts, int nopt) {
+  for (int i = 0; i < nopt; ++i) {
+    const int per_wave = G * opts[i];
+    const int64_t waves = (int64_t)((rows + per_wave - 1) / per_wave) * experts;
+    if (waves >= 2048) return opts[i];
+  }
+  return opts[nopt - 1];
+}
+
+GemvCfg gateup_config(int fmt, int F, int H, int max_active, int T) {
+  GemvCfg c{};
+  c.L = pow2_divisor_le64(nchunks(fmt, H));
+  const int G = 64 / c.L;
+  c.B = T == 1 ? 1 : 4;
+  const int opts1[] = {2, 1};
+  const int P = c.B == 1 ? choose_R(F, G, max_active, opts1, 2) : 1;
+  c.R = 2 * P;
+  c.rows_per_block = kWaves * G * P;  // row pairs per block
+  c.grid = dim3((F + c.rows_per_block - 1) / c.rows_per_block, max_active);
+  c.S = 1;
+  return c;
+}
+
+GemvCfg down_config(int fmt, int H, int F, int max_active, int T) {
+  GemvCfg c{};
+  c.L = pow2_divisor_le64(nchunks(fmt, F));
+  const int G = 64 / c.L;
+  c.B = T == 1 ? 1 : 4;
+  const int opts[] = {4, 2, 1};
+  c.R = c.B == 1 ? choose_R(H, G, max_active, opts, 3) : 1;
+  c.rows_per_block = kWaves * G * c.R;
+  c.grid = dim3((H + c.rows_per_block - 1) / c.rows_per_block, max_active);
+  c.S = 1;
+  return c;
+}
+
+template <int FMT>
+static hipError_t gateup_f(const GemvCfg& c, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
+                           int64_t mb, int F, int H, int act, const Disp& d, const float* x, float* h,
+                           hipStream_t st) {
+  const int P = c.R / 2;
+#define MD_G(L_, P_, B_) \
+  if (c.L == L_ && P == P_ && c.B == B_) { \
+    hipLaunchKernelGGL((k_gateup<FMT, L_, P_, B_>), c.grid, dim3(kBlock), 0, st, gq, uq, gs, us, mb, F, H, act, d, \
+                       x, h); \
+    return hipGetLastError(); }
+#define MD_GL(L_) MD_G(L_, 2, 1) MD_G(L_, 1, 1) MD_G(L_, 1, 4)
+  MD_GL(64) MD_GL(32) MD_GL(16) MD_GL(8)
+#undef MD_GL
+#undef MD_G
+  return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_gateup(int fmt, const GemvCfg& c, const uint8_t* gq, const uint8_t* uq, const float* gs,
+                         const float* us, int64_t mat_bytes, int F, int H, int act, const Disp& d,
+                         const float* x, float* h, hipStream_t st) {
+  switch (fmt) {
+    case Q8_0: return gateup_f<Q8_0>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
+    case Q4_0: return gateup_f<Q4_0>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
+    case I8_ROW: return gateup_f<I8_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
+    case I4_ROW: return gateup_f<I4_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+static hipError_t down_f(const GemvCfg& c, const uint8_t* dq, const float* ds, int64_t mb, int H, int F,
+                         const Disp& d, const float* h, float* o, hipStream_t st) {
+#define MD_D(L_, R_, B_) \
+  if (c.L == L_ && c.R == R_ && c.B == B_) { \
+    hipLaunchKernelGGL((k_down<FMT, L_, R_, B_>), c.grid, dim3(kBlock), 0, st, dq, ds, mb, H, F, d, h, o); \
+    return hipGetLastError(); }
+#define MD_DL(L_) MD_D(L_, 4, 1) MD_D(L_, 2, 1) MD_D(L_, 1, 1) MD_D(L_, 1, 4)
+  MD_DL(64) MD_DL(32) MD_DL(16) MD_DL(8)
+#undef MD_DL
+#undef MD_D
+  return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_down(int fmt, const GemvCfg& c, const uint8_t* dq, const float* ds, int64_t mat_bytes, int H,
+                       int F, const Disp& d, const float* h, float* o, hipStream_t st) {
+  switch (fmt) {
+    case Q8_0: return down_f<Q8_0>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
+    case Q4_0: return down_f<Q4_0>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
+    case I8_ROW: return down_f<I8_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
+    case I4_ROW: return down_f<I4_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
+                          const float* y_shared, float* y, hipStream_t st) {
+  const int64_t n = (int64_t)T * (H / 4);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, o, pos_of_pair,
+                     gates, T, k, H, y_shared, y);
+  return hipGetLastError();
+}
+
+}  // namespace md

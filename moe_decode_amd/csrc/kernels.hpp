@@ -1,0 +1,67 @@
+// kernels.hpp -- launch interface between the host entry points (abi.cpp)
+// and the HIP kernels.  Internal to libmoe_decode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace md {
+
+// Routing hand-off in device memory.  Pair p = t*k + j is token t's slot j.
+// Pairs are grouped by expert (ascending expert id, then ascending p);
+// "position" q is a pair's index in that order.  h and o rows are indexed by
+// position.  A dense FFN uses n_active == nullptr: one expert (0) whose
+// positions are the tokens 0..T-1.
+struct Disp {
+  const int* n_active;     // [1]
+  const int* active_e;     // [n_active]
+  const int* active_off;   // [n_active + 1]  positions of each expert's pairs
+  const int* pairs;        // [T*k]  pair id at each position
+  int k;                   // slots per token (1 for a dense FFN)
+  int T;                   // tokens (dense FFN)
+};
+
+struct DispOut {
+  int* n_active;
+  int* active_e;
+  int* active_off;
+  int* pairs;
+  int* pos_of_pair;
+};
+
+struct GemvCfg {
+  int L;        // lanes per row group (8..64)
+  int R;        // rows per lane group
+  int B;        // tokens per pass (template width)
+  int S;        // K splits (qgemv only)
+  int rows_per_block;
+  dim3 grid;
+};
+
+// ---- launchers (return hipGetLastError() of the launch) -------------------
+hipError_t launch_prepare_layout(int fmt, int rows, int cols, int count, const void* src, void* dst,
+                                 hipStream_t st);
+
+GemvCfg qgemv_config(int fmt, int N, int K, int batch);
+hipError_t launch_qgemv(int fmt, int xt, const GemvCfg& c, const uint8_t* W, const float* scales, int N, int K,
+                        const void* x, int batch, float* y, float* partial, hipStream_t st);
+
+int router_splits(int H, int E);
+hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
+                         hipStream_t st);
+hipError_t launch_route_finalize(const double* part, int S, const float* bias, int T, int E, int k,
+                                 float* logits, int* idx, float* gates, const DispOut* d, hipStream_t st);
+
+GemvCfg gateup_config(int fmt, int F, int H, int max_active, int T);
+hipError_t launch_gateup(int fmt, const GemvCfg& c, const uint8_t* gq, const uint8_t* uq, const float* gs,
+                         const float* us, int64_t mat_bytes, int F, int H, int act, const Disp& d,
+                         const float* x, float* h, hipStream_t st);
+
+GemvCfg down_config(int fmt, int H, int F, int max_active, int T);
+hipError_t launch_down(int fmt, const GemvCfg& c, const uint8_t* dq, const float* ds, int64_t mat_bytes,
+                       int H, int F, const Disp& d, const float* h, float* o, hipStream_t st);
+
+hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
+                          const float* y_shared, float* y, hipStream_t st);
+
+}  // namespace md

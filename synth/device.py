@@ -1,0 +1,45 @@
+"""Upload the seeded workloads to the GPU through the library's binding.
+
+Used by the GPU tests and the benchmark only (the oracle never imports this
+module).  It moves bytes; it computes nothing."""
+import numpy as np
+import torch
+
+import moe_decode_amd as md
+from moe_decode_amd.upload import upload_stack, upload_matrix
+
+from . import workloads as W
+
+
+def device_moe(sp, device="cuda"):
+    """The whole layer of an MoE workload resident on the GPU."""
+    stacks = {}
+    for part in ("gate", "up", "down"):
+        rows, cols = (sp.H, sp.F) if part == "down" else (sp.F, sp.H)
+
+        def fetch(e, part=part):
+            m = W.moe_expert_part(sp, e, part)
+            return m.data, m.scales
+        stacks[part] = upload_stack(sp.fmt, rows, cols, sp.E, fetch, device)
+    Wr, b = W.moe_router(sp)
+    Wr_t = torch.from_numpy(Wr).to(device)
+    b_t = None if b is None else torch.from_numpy(b).to(device)
+    shared = None
+    sh = W.moe_shared(sp)
+    if sh is not None:
+        shared = md.FFN(sp.act, upload_matrix(sh["gate"], device), upload_matrix(sh["up"], device),
+                        upload_matrix(sh["down"], device))
+    return md.MoELayer(sp.H, sp.F, sp.E, sp.k, sp.act, stacks["gate"], stacks["up"], stacks["down"], Wr_t, b_t,
+                       shared)
+
+
+def device_dense(sp, name, device="cuda"):
+    return upload_matrix(W.dense_matrix(sp, name), device)
+
+
+def x_tensor(x, device="cuda"):
+    """fp32 array -> fp32 tensor; uint16 bf16 patterns -> bf16 tensor."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(x.astype(np.float32)).to(device)

@@ -132,17 +132,34 @@ def _rng(index, tag, a=0, b=0):
     return np.random.default_rng([index, tag, a, b])
 
 
+def _uniform_bytes(rng, n):
+    """n independent uniform bytes (raw 64-bit PCG64 outputs, little-endian)."""
+    words = rng.bit_generator.random_raw((n + 7) // 8)
+    return words.view(np.uint8)[:n].copy()
+
+
+def _int8_symmetric(rng, n):
+    """n independent int8 values uniform on [-127, 127]: uniform bytes with
+    every 0x80 (-128) redrawn until none is left (rejection sampling)."""
+    b = _uniform_bytes(rng, n)
+    bad = np.flatnonzero(b == 0x80)
+    while bad.size:
+        b[bad] = _uniform_bytes(rng, bad.size)
+        bad = bad[b[bad] == 0x80]
+    return b.view(np.int8)
+
+
 def _gen_qmatrix(fmt, rows, cols, rng, d_range) -> QMatrix:
     lo, hi = d_range
     if fmt == "q8_0":
         d = rng.uniform(lo, hi, (rows, cols // 32)).astype(np.float16)
-        q = rng.integers(-127, 128, (rows, cols), dtype=np.int8)
+        q = _int8_symmetric(rng, rows * cols).reshape(rows, cols)
         return pack_q8_0(d, q)
     if fmt == "q4_0":
         nb = cols // 32
         d = rng.uniform(lo, hi, (rows, nb)).astype(np.float16).view(np.uint16)
         # a uniform random byte is two independent uniform nibbles 0..15
-        qs = np.frombuffer(rng.bytes(rows * nb * 16), dtype=np.uint8).reshape(rows, nb, 16)
+        qs = _uniform_bytes(rng, rows * nb * 16).reshape(rows, nb, 16)
         out = np.empty((rows, nb, 18), dtype=np.uint8)
         out[:, :, 0] = (d & 0xFF).astype(np.uint8)
         out[:, :, 1] = (d >> 8).astype(np.uint8)
@@ -150,13 +167,13 @@ def _gen_qmatrix(fmt, rows, cols, rng, d_range) -> QMatrix:
         return QMatrix("q4_0", rows, cols, out.reshape(rows, nb * 18))
     if fmt == "i8_row":
         s = rng.uniform(lo, hi, rows).astype(np.float32)
-        q = rng.integers(-127, 128, (rows, cols), dtype=np.int8)
+        q = _int8_symmetric(rng, rows * cols).reshape(rows, cols)
         return pack_i8_row(s, q)
     if fmt == "i4_row":
         s = rng.uniform(lo, hi, rows).astype(np.float32)
         # two independent uniform signed nibbles per byte == a uniform byte
-        data = np.frombuffer(rng.bytes(rows * cols // 2), dtype=np.uint8).reshape(rows, cols // 2)
-        return QMatrix("i4_row", rows, cols, data.copy(), s)
+        data = _uniform_bytes(rng, rows * cols // 2).reshape(rows, cols // 2)
+        return QMatrix("i4_row", rows, cols, data, s)
     raise ValueError(fmt)
 
 

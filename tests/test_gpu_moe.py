@@ -1,0 +1,167 @@
+"""GPU parity of the router and the MoE layer against the oracle: expert
+indices bit-exact, gates within 1e-6, outputs within 1e-4*S + 1e-6, at the
+workloads' full sizes (decode, batch decode, 128-token chunks), plus the
+exact-tie rule through the GPU route path and invariants."""
+import numpy as np
+import pytest
+
+from synth import workloads as W
+
+from .gpu_common import assert_within, moe_layer, oracle_moe, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _t(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _route_gpu(x, Wr, b, k, E):
+    import moe_decode_amd as md
+    import torch
+    T = x.shape[0]
+    logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    idx, gates = md.moe_route_topk(_t(x), _t(Wr), None if b is None else _t(b), k, logits=logits)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), gates.cpu().numpy(), logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("key,T", [("c0", 1), ("c3", 1), ("c3", 128), ("c4_i4", 1), ("c4_i4", 4), ("c4_i4", 128)])
+def test_route_matches_oracle(orc_mt, key, T):
+    sp = W.spec(key)
+    Wr, b = W.moe_router(sp)
+    x = W.moe_x(sp, T)
+    i_ref, g_ref, l_ref, margin = orc_mt.route_topk(x, Wr, b, sp.k)
+    i_gpu, g_gpu, l_gpu = _route_gpu(x, Wr, b, sp.k, sp.E)
+    assert np.array_equal(l_gpu, l_ref), "logits differ"
+    mism = np.argwhere(i_gpu != i_ref)
+    assert mism.size == 0, f"idx mismatch at {mism[:5].tolist()}, margins {margin[mism[:5, 0]].tolist()}"
+    assert np.max(np.abs(g_gpu - g_ref)) <= 1e-6
+
+
+def _one_hot_route(logits_wanted, k, H=256):
+    l = np.asarray(logits_wanted, dtype=np.float32)
+    Wr = np.zeros((l.shape[0], H), dtype=np.float32)
+    Wr[:, 0] = l
+    x = np.zeros((1, H), dtype=np.float32)
+    x[0, 0] = 1.0
+    return x, Wr
+
+
+@pytest.mark.parametrize("case", ["all_equal", "boundary_tie", "inner_ties", "signed_zero", "k_equals_E"])
+def test_route_ties_through_gpu(orc, case):
+    E, k = 64, 8
+    if case == "all_equal":
+        l = [0.5] * E
+    elif case == "boundary_tie":
+        l = list(np.linspace(-1, 1, E))
+        l[10] = l[50] = 5.0
+        for e in range(20, 26):
+            l[e] = 3.0
+        l[40] = l[33] = 3.0                 # 8 values of 3.0 compete for 6 slots
+    elif case == "inner_ties":
+        l = [0.25 * (e % 5) for e in range(E)]
+    elif case == "signed_zero":
+        l = [-1.0] * E
+        for e in (3, 7, 9, 11):
+            l[e] = -0.0
+        for e in (4, 8, 12, 60):
+            l[e] = 0.0
+    else:
+        E = k = 8
+        l = [1.0, -2.0, 1.0, 0.0, -0.0, 3.0, 1.0, 3.0]
+    x, Wr = _one_hot_route(l, k)
+    i_ref, g_ref, _, _ = orc.route_topk(x, Wr, None, k)
+    i_gpu, g_gpu, _ = _route_gpu(x, Wr, None, k, len(l))
+    assert np.array_equal(i_gpu, i_ref), (i_gpu, i_ref)
+    assert np.max(np.abs(g_gpu - g_ref)) <= 1e-6
+
+
+def _moe_gpu(key, x):
+    import moe_decode_amd as md
+    import torch
+    sp = W.spec(key)
+    layer = moe_layer(key)
+    T = x.shape[0]
+    idx = torch.empty(T, sp.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, sp.k, dtype=torch.float32, device="cuda")
+    y = md.moe_layer_forward(layer, _t(x), idx=idx, gates=gates)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy(), gates.cpu().numpy()
+
+
+@pytest.mark.parametrize("key,T", [("c0", 1), ("c3", 1), ("c4_i4", 1), ("c4_i4", 4), ("c4_i8", 1), ("c4_i8", 4),
+                                   ("c3", 128)])
+def test_moe_layer_matches_oracle(orc_mt, key, T):
+    sp = W.spec(key)
+    x = W.moe_x(sp, T)
+    say(f"[moe] {key} T={T}")
+    y, idx, gates = _moe_gpu(key, x)
+    y_ref, i_ref, g_ref, S = oracle_moe(orc_mt, sp, x)
+    assert np.array_equal(idx, i_ref)
+    assert np.max(np.abs(gates - g_ref)) <= 1e-6
+    ratio = assert_within(y, y_ref, S, f"{key} T={T}")
+    say(f"[moe] {key} T={T} max err/S {ratio:.2e}")
+
+
+@pytest.mark.parametrize("key", ["c4_i4", "c4_i8"])
+def test_moe_prefill_chunk_sampled(orc_mt, key):
+    """128-token chunk at full size: routing of every token checked, outputs
+    of a sample of tokens checked (tokens are independent in the layer)."""
+    sp = W.spec(key)
+    x = W.moe_x(sp, 128)
+    say(f"[moe] {key} T=128")
+    y, idx, gates = _moe_gpu(key, x)
+    Wr, b = W.moe_router(sp)
+    i_ref, g_ref, _, _ = orc_mt.route_topk(x, Wr, b, sp.k)
+    assert np.array_equal(idx, i_ref)
+    assert np.max(np.abs(gates - g_ref)) <= 1e-6
+    sample = [0, 1, 37, 64, 101, 127]
+    y_ref, _, _, S = oracle_moe(orc_mt, sp, x[sample])
+    assert_within(y[sample], y_ref, S, f"{key} T=128 sampled")
+
+
+def test_prefill_equals_token_by_token():
+    sp = W.spec("c3")
+    x = W.moe_x(sp, 128)[:16]
+    y, idx, _ = _moe_gpu("c3", x)
+    for t in (0, 5, 15):
+        yt, it, _ = _moe_gpu("c3", x[t:t + 1])
+        assert np.array_equal(it[0], idx[t])
+        assert np.max(np.abs(yt[0] - y[t])) <= 1e-5 * np.max(np.abs(y[t])) + 1e-6
+
+
+def test_moe_deterministic():
+    sp = W.spec("c3")
+    x = W.moe_x(sp, 128)[:8]
+    a = _moe_gpu("c3", x)
+    b = _moe_gpu("c3", x)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_single_expert_gate_one_is_its_ffn():
+    """k = 1: the layer output is that expert's FFN (gate exactly 1)."""
+    import moe_decode_amd as md
+    import torch
+    sp = W.spec("c0")
+    base = moe_layer("c0")
+    layer = md.MoELayer(sp.H, sp.F, sp.E, 1, sp.act, base.gate, base.up, base.down, base.Wr, base.bias)
+    x = W.moe_x(sp, 4)
+    idx = torch.empty(4, 1, dtype=torch.int32, device="cuda")
+    gates = torch.empty(4, 1, dtype=torch.float32, device="cuda")
+    y = md.moe_layer_forward(layer, _t(x), idx=idx, gates=gates)
+    torch.cuda.synchronize()
+    assert torch.all(gates == 1.0)
+    for t in range(4):
+        e = int(idx[t, 0])
+        ffn = md.FFN(sp.act, base.gate.expert(e), base.up.expert(e), base.down.expert(e))
+        yf = md.ffn_forward(ffn, _t(x[t:t + 1]))
+        torch.cuda.synchronize()
+        assert torch.equal(yf[0], y[t])

@@ -1,0 +1,137 @@
+"""GPU parity of md_qgemv against the oracle: every format, ragged and
+multi-tile shapes, batches 1..8, fp32 and bf16 activations, the dense
+workloads at full size, and closed forms that must hold bitwise."""
+import numpy as np
+import pytest
+
+from synth import formats as F
+from synth import workloads as W
+
+from .gpu_common import assert_within, dense_matrix, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _random_qmatrix(rng, fmt, rows, cols):
+    if fmt == "q8_0":
+        return F.pack_q8_0(rng.uniform(1e-3, 1e-2, (rows, cols // 32)).astype(np.float16),
+                           rng.integers(-127, 128, (rows, cols)))
+    if fmt == "q4_0":
+        return F.pack_q4_0(rng.uniform(1e-3, 2e-2, (rows, cols // 32)).astype(np.float16),
+                           rng.integers(0, 16, (rows, cols)))
+    s = rng.uniform(1e-3, 1e-2, rows).astype(np.float32)
+    if fmt == "i8_row":
+        return F.pack_i8_row(s, rng.integers(-127, 128, (rows, cols)))
+    return F.pack_i4_row(s, rng.integers(-8, 8, (rows, cols)))
+
+
+def _run(m, x_np):
+    import moe_decode_amd as md
+    from moe_decode_amd.upload import upload_matrix
+    from synth.device import x_tensor
+    import torch
+    W_d = upload_matrix(m)
+    y = md.qgemv(W_d, x_tensor(x_np))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt", F.FORMATS)
+@pytest.mark.parametrize("rows,cols", [(7, 256), (33, 512), (300, 768), (129, 2048), (64, 5632)])
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_qgemv_random(orc_mt, fmt, rows, cols, batch):
+    say(f"[qgemv] {fmt} {rows}x{cols} batch {batch}")
+    rng = np.random.default_rng([F.FORMATS.index(fmt), rows, cols, batch])
+    m = _random_qmatrix(rng, fmt, rows, cols)
+    x = rng.standard_normal((batch, cols)).astype(np.float32)
+    y_ref, S = orc_mt.qgemv(m, x)
+    assert_within(_run(m, x), y_ref, S, f"{fmt} {rows}x{cols} b{batch}")
+
+
+@pytest.mark.parametrize("fmt", F.FORMATS)
+@pytest.mark.parametrize("batch", [1, 8])
+def test_qgemv_bf16(orc_mt, fmt, batch):
+    rng = np.random.default_rng([9, F.FORMATS.index(fmt), batch])
+    m = _random_qmatrix(rng, fmt, 96, 1024)
+    xb = F.f32_to_bf16_bits(rng.standard_normal((batch, 1024)))
+    y_ref, S = orc_mt.qgemv(m, xb, "bf16")
+    assert_within(_run(m, xb), y_ref, S, f"bf16 {fmt}")
+
+
+@pytest.mark.parametrize("name", ["gate", "up", "down", "q", "o", "k", "v"])
+def test_dense_q8_0_llama_shapes(orc_mt, name):
+    import moe_decode_amd as md
+    import torch
+    from synth.device import x_tensor
+    sp = W.spec("c1")
+    say(f"[c1] {name}")
+    m = W.dense_matrix(sp, name)
+    x = W.dense_x(sp, m.cols, 1)
+    y_ref, S = orc_mt.qgemv(m, x)
+    y = md.qgemv(dense_matrix("c1", name), x_tensor(x))
+    torch.cuda.synchronize()
+    assert_within(y.cpu().numpy(), y_ref, S, f"c1 {name}")
+
+
+def test_dense_swiglu_ffn(orc_mt):
+    import moe_decode_amd as md
+    import torch
+    sp = W.spec("c1")
+    g, u, d = (W.dense_matrix(sp, n) for n in ("gate", "up", "down"))
+    x = W.dense_x(sp, 2048, 1)
+    y_ref, S = orc_mt.ffn(g, u, d, "silu", x)
+    ffn = md.FFN("silu", dense_matrix("c1", "gate"), dense_matrix("c1", "up"), dense_matrix("c1", "down"))
+    y = md.ffn_forward(ffn, torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert_within(y.cpu().numpy(), y_ref, S, "c1 SwiGLU FFN")
+
+
+@pytest.mark.parametrize("name", ["w_10240x2560", "w_2560x10240"])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_dense_q4_0_bf16(orc_mt, name, batch):
+    import moe_decode_amd as md
+    import torch
+    from synth.device import x_tensor
+    sp = W.spec("c2")
+    say(f"[c2] {name} batch {batch}")
+    m = W.dense_matrix(sp, name)
+    x = W.dense_x(sp, m.cols, batch)
+    y_ref, S = orc_mt.qgemv(m, x, "bf16")
+    y = md.qgemv(dense_matrix("c2", name), x_tensor(x))
+    torch.cuda.synchronize()
+    assert_within(y.cpu().numpy(), y_ref, S, f"c2 {name} b{batch}")
+
+
+def test_q4_0_code_eight_is_exact_zero():
+    rng = np.random.default_rng(31)
+    m = F.pack_q4_0(rng.uniform(1e-3, 2e-2, (70, 16)).astype(np.float16), np.full((70, 512), 8))
+    y = _run(m, rng.standard_normal((2, 512)).astype(np.float32))
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("fmt", F.FORMATS)
+def test_one_hot_x_is_bitwise_one_weight(orc, fmt):
+    rng = np.random.default_rng([32, F.FORMATS.index(fmt)])
+    m = _random_qmatrix(rng, fmt, 40, 512)
+    for c in (0, 31, 300, 511):
+        x = np.zeros((1, 512), dtype=np.float32)
+        x[0, c] = 1.0
+        y_ref, _ = orc.qgemv(m, x)
+        assert np.array_equal(_run(m, x), y_ref), (fmt, c)
+
+
+def test_deterministic_repeat():
+    import moe_decode_amd as md
+    import torch
+    from synth.device import x_tensor
+    sp = W.spec("c1")
+    x = x_tensor(W.dense_x(sp, 2048, 1))
+    a = md.qgemv(dense_matrix("c1", "k"), x)      # split-K path
+    b = md.qgemv(dense_matrix("c1", "k"), x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
