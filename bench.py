@@ -75,16 +75,21 @@ def run_mode(layer, sp, T, steps, warmup, stage="gateup"):
     for i in range(warmup):
         md.moe_layer_forward(layer, xs[i % pool], y=y, idx=idx[i % pool], gates=gates, workspace=ws)
     torch.cuda.synchronize()
+    # timed region: plain forwards
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        a, b = ev[i]
-        md.moe_layer_forward_timed(layer, xs[i % pool], stage, a, b, y=y, idx=idx[i % pool], gates=gates,
-                                   workspace=ws)
+        md.moe_layer_forward(layer, xs[i % pool], y=y, idx=idx[i % pool], gates=gates, workspace=ws)
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    # the same steps again with HIP events around one stage on the kernels' stream
+    for i in range(steps):
+        a, b = ev[i]
+        md.moe_layer_forward_timed(layer, xs[i % pool], stage, a, b, y=y, idx=idx[i % pool], gates=gates,
+                                   workspace=ws)
+    torch.cuda.synchronize()
     stage_ms = [a.elapsed_time(b) for a, b in ev]
     idx_np = idx.cpu().numpy()
     wb = [step_weight_bytes(sp, idx_np[i % pool]) for i in range(steps)]

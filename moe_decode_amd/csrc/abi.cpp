@@ -43,6 +43,9 @@ constexpr int kMaxT = 128;
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 8;
 constexpr int kMaxBatch = 8;
+// Up to this many tokens, every (token, slot) pair runs as its own one-token
+// problem in one launch; above it the pairs are grouped by expert.
+constexpr int kMaxPairT = 8;
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -88,17 +91,14 @@ int max_active(int T, int E, int k) { return T * k < E ? T * k : E; }
 
 // ---- MoE workspace layout ------------------------------------------------
 struct MoeWs {
-  size_t part, logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
-  int S;
+  size_t logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
 };
 
 MoeWs moe_ws(const md_moe_layer* L, int T) {
   MoeWs w{};
   const int E = L->E, k = L->k, H = L->H, F = L->F;
-  w.S = md::router_splits(H, E);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  w.part = take(sizeof(double) * T * E * w.S);
   w.logits = take(sizeof(float) * T * E);
   w.idx = take(sizeof(int) * T * k);
   w.gates = take(sizeof(float) * T * k);
@@ -108,7 +108,7 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
   w.pairs = take(sizeof(int) * T * k);
   w.pos = take(sizeof(int) * T * k);
   w.h = take(sizeof(float) * (size_t)T * k * F);
-  w.o = take(sizeof(float) * (size_t)T * k * H);
+  if (T > kMaxPairT) w.o = take(sizeof(float) * (size_t)T * k * H);
   if (L->has_shared) {
     w.h_s = take(sizeof(float) * (size_t)T * L->shared.gate.rows);
     w.y_s = take(sizeof(float) * (size_t)T * H);
@@ -155,6 +155,16 @@ md_status check_ws(void* ws, size_t have, size_t need) {
 // dense FFN (or shared expert) through the MoE kernels with the identity dispatch
 md_status run_ffn(const md_ffn* f, const float* x, int T, float* h, float* y, hipStream_t st) {
   const int H = f->gate.cols, F = f->gate.rows, fmt = f->gate.type;
+  if (T <= kMaxPairT && md::t1_supported(fmt, H, F)) {
+    hipError_t e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(f->gate.q),
+                                        static_cast<const uint8_t*>(f->up.q), f->gate.row_scale, f->up.row_scale, 0,
+                                        F, H, f->act, 1, 1, T, nullptr, x, h, nullptr, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "ffn gate/up launch");
+    e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(f->down.q), f->down.row_scale, 0, H, F, 1, T, nullptr,
+                           nullptr, h, nullptr, y, st);
+    if (e != hipSuccess) return hip_fail(e, "ffn down launch");
+    return MD_OK;
+  }
   md::Disp d{nullptr, nullptr, nullptr, nullptr, 1, T};
   md::GemvCfg cg = md::gateup_config(fmt, F, H, 1, T);
   hipError_t e = md::launch_gateup(fmt, cg, static_cast<const uint8_t*>(f->gate.q), static_cast<const uint8_t*>(f->up.q),
@@ -241,7 +251,7 @@ md_status md_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, si
   if (T > kMaxT || E > kMaxE || k > kMaxK) return fail(MD_ERR_UNSUPPORTED, "T <= %d, E <= %d, k <= %d", kMaxT, kMaxE, kMaxK);
   md_status s = check_width("H", H);
   if (s != MD_OK) return s;
-  *bytes = align256(sizeof(double) * (size_t)T * E * md::router_splits(H, E));
+  *bytes = align256(sizeof(float) * (size_t)T * E);
   return ok();
 }
 
@@ -256,11 +266,10 @@ md_status md_moe_route_topk(const float* x, int32_t T, int32_t H, const float* W
       (logits && !aligned16(logits)))
     return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
-  const int S = md::router_splits(H, E);
-  double* part = static_cast<double*>(workspace);
-  hipError_t e = md::launch_router(x, T, H, W_r, E, S, part, stream);
+  float* l = logits ? logits : static_cast<float*>(workspace);
+  hipError_t e = md::launch_router_rows(x, T, H, W_r, bias, E, l, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
-  e = md::launch_route_finalize(part, S, bias, T, E, k, logits, idx, gates, nullptr, stream);
+  e = md::launch_route_finalize(l, T, E, k, idx, gates, nullptr, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "route finalize launch");
 }
 
@@ -321,6 +330,13 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     return e == hipSuccess;
   };
 
+  const int64_t gu_bytes = (int64_t)F * md::row_bytes(fmt, H);
+  const int64_t dn_bytes = (int64_t)H * md::row_bytes(fmt, F);
+  float* logits = static_cast<float*>(P(w.logits));
+  float* h = static_cast<float*>(P(w.h));
+  const bool t1 = T <= kMaxPairT && md::t1_supported(fmt, H, F) &&
+                  (!L->has_shared || md::t1_supported(L->shared.gate.type, H, L->shared.gate.rows));
+
   // shared expert: independent of the routing, enqueued first
   if (!mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
   if (L->has_shared) {
@@ -328,21 +344,36 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     if (s != MD_OK) return s;
   }
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
-  e = md::launch_router(x, T, H, L->W_r, E, w.S, static_cast<double*>(P(w.part)), stream);
+  e = md::launch_router_rows(x, T, H, L->W_r, L->router_bias, E, logits, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");
+
+  if (t1) {
+    // few tokens: selection happens inside the gate/up kernel, the combine
+    // inside the down kernel; each (token, slot) pair is an independent
+    // one-token problem
+    if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
+    e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                             L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, logits, x, h, idx, gates,
+                             stream);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
+    e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
+                           gates, h, y_s, y, stream);
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+    if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
+      return hip_fail(e, "event record");
+    return ok();
+  }
+
   md::DispOut dout{static_cast<int*>(P(w.n_active)), static_cast<int*>(P(w.active_e)),
                    static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos))};
-  e = md::launch_route_finalize(static_cast<double*>(P(w.part)), w.S, L->router_bias, T, E, k,
-                                static_cast<float*>(P(w.logits)), idx, gates, &dout, stream);
+  e = md::launch_route_finalize(logits, T, E, k, idx, gates, &dout, stream);
   if (e != hipSuccess) return hip_fail(e, "route finalize launch");
   if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
 
   md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T};
   const int A = max_active(T, E, k);
-  const int64_t gu_bytes = (int64_t)F * md::row_bytes(fmt, H);
-  const int64_t dn_bytes = (int64_t)H * md::row_bytes(fmt, F);
-  float* h = static_cast<float*>(P(w.h));
   float* o = static_cast<float*>(P(w.o));
   md::GemvCfg cg = md::gateup_config(fmt, F, H, A, T);
   e = md::launch_gateup(fmt, cg, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),

@@ -49,8 +49,15 @@ __host__ __device__ constexpr int nchunks(int fmt, int K) { return K / wpc(fmt);
 // convert per nibble.
 MD_DEV unsigned opaque(unsigned v) { asm volatile("" : "+v"(v)); return v; }
 
+#ifndef MD_NT_LOADS
+#define MD_NT_LOADS 1
+#endif
 MD_DEV u32x4 ld_stream(const uint8_t* p) {
+#if MD_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
 }
 
 MD_DEV float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }

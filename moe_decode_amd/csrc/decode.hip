@@ -1,0 +1,452 @@
+// decode.hip -- the one-token decode path of the MoE layer (gfx950, wave64).
+//
+// Three launches per layer call (five with a shared expert):
+//   k_router_rows  one workgroup per expert: logits = W_r x (+ b), fp64
+//                  accumulation, rounded once to fp32.
+//   k_gateup_t1    each workgroup first selects the top-k experts from the
+//                  logits (64-bit order keys: larger logit, then lower index),
+//                  then streams gate and up rows of its slot's expert against
+//                  the activations held in VGPRs, and writes h = act(a) * u.
+//   k_down_t1      each workgroup owns a tile of output rows; wave j streams
+//                  the down rows of slot j's expert against h_j held in VGPRs;
+//                  the per-slot partials meet in LDS and are combined in slot
+//                  order with the gates (+ the shared expert's output).
+// The shared expert (a dense gated FFN) runs through the same two kernels in
+// dense mode before the routed ones.
+//
+// Streaming: a lane group of L lanes owns a row; each lane owns one 16-byte
+// chunk position per K-slice, so the activations it multiplies never change
+// and stay in registers for every row the wave visits.  Row loads run in a
+// rolling window (several rows in flight while one is decoded).  Partial sums of the rows a lane group visited are reduced with
+// one transposed butterfly (N-1 exchanges for N rows instead of N log L).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace md {
+
+#ifndef MD_GU_WINDOW
+#define MD_GU_WINDOW 2
+#endif
+#ifndef MD_DN_WINDOW
+#define MD_DN_WINDOW 8
+#endif
+#ifndef MD_DN_ROWS
+#define MD_DN_ROWS 8
+#endif
+#ifndef MD_GU_MAXNP
+#define MD_GU_MAXNP 8
+#endif
+constexpr int kNRW = MD_DN_ROWS;   // output rows per workgroup in k_down_t1
+
+// Sum over the L lanes of a group for N rows at once.  On return lane t holds
+// the full sum of row (t / (L/N)) % N.
+template <int N, int L>
+MD_DEV float butterfly(float (&v)[N], int t) {
+  static_assert(N <= L, "more rows than lanes");
+#pragma unroll
+  for (int s = 0; (N >> s) > 1; ++s) {
+    const int n = N >> s, half = n / 2, off = L >> (s + 1);
+    const bool up = (t & off) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = up ? v[i] : v[i + half];
+      const float keep = up ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, off, 64);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int off = L / (2 * N); off > 0; off >>= 1) r += __shfl_xor(r, off, 64);
+  return r;
+}
+
+template <int FMT, int CPL>
+struct RowBuf {
+  u32x4 w[CPL];
+  float s[CPL];
+};
+
+template <int FMT, int L, int CPL>
+MD_DEV void load_row(RowBuf<FMT, CPL>& b, const uint8_t* row, int K, int c0) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) b.w[i] = ld_stream(row + 16 * (int64_t)(c0 + L * i));
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) b.s[i] = chunk_scale<FMT>(row, K, c0 + L * i);
+}
+
+template <int FMT, int CPL>
+MD_DEV float row_dot(const RowBuf<FMT, CPL>& b, const float (&xv)[CPL][Fmt<FMT>::WPC]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const float d = dot_chunk<FMT>(b.w[i], xv[i]);
+    acc = Fmt<FMT>::ROW ? acc + d : fmaf(b.s[i], d, acc);
+  }
+  return acc;
+}
+
+template <int FMT, int L, int CPL>
+MD_DEV void load_xv(float (&xv)[CPL][Fmt<FMT>::WPC], const float* x, int c0) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) load_x<FMT, XF32>(x, c0 + L * i, xv[i]);
+}
+
+// ------------------------------------------------------------------ router
+
+// One workgroup (4 waves) per expert e; the waves split K in four, each lane
+// accumulates its slice in fp64 for up to 4 tokens at a time; the four wave
+// sums are added in a fixed order.
+__global__ __launch_bounds__(256) void k_router_rows(const float* __restrict__ x, int T, int H,
+                                                     const float* __restrict__ Wr, const float* __restrict__ bias,
+                                                     int E, float* __restrict__ logits) {
+  __shared__ double red[4][4];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = H / 4;                 // a multiple of 64
+  const float* w = Wr + (int64_t)e * H + wave * ks;
+  const bool vec = (ks % 256) == 0;
+  for (int t0 = 0; t0 < T; t0 += 4) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    if (vec) {
+      for (int j = lane; j < ks / 4; j += 64) {
+        const float4 wv = reinterpret_cast<const float4*>(w)[j];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (t0 + b < T) {
+            const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)(t0 + b) * H + wave * ks)[j];
+            acc[b] = fma((double)wv.x, (double)xv.x, acc[b]);
+            acc[b] = fma((double)wv.y, (double)xv.y, acc[b]);
+            acc[b] = fma((double)wv.z, (double)xv.z, acc[b]);
+            acc[b] = fma((double)wv.w, (double)xv.w, acc[b]);
+          }
+        }
+      }
+    } else {
+      for (int j = lane; j < ks; j += 64) {
+        const double wv = (double)w[j];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (t0 + b < T) acc[b] = fma(wv, (double)x[(int64_t)(t0 + b) * H + wave * ks + j], acc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const double v = wave_sum_f64(acc[b]);
+      if (lane == 0) red[wave][b] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 4 && t0 + (int)threadIdx.x < T) {
+      const int b = threadIdx.x;
+      double a = ((red[0][b] + red[1][b]) + red[2][b]) + red[3][b];
+      if (bias) a += (double)bias[e];
+      logits[(int64_t)(t0 + b) * E + e] = (float)a;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_router_rows(const float* x, int T, int H, const float* Wr, const float* bias, int E,
+                              float* logits, hipStream_t st) {
+  hipLaunchKernelGGL(k_router_rows, dim3(E), dim3(256), 0, st, x, T, H, Wr, bias, E, logits);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ top-k
+
+MD_DEV uint32_t order_key32(float l) {
+  uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wave-level top-k of one token's E logits (E <= 256).  All lanes return the
+// same k experts in selection order and, when asked, their gates.
+MD_DEV void wave_topk(const float* __restrict__ logits, int E, int k, int lane, int (&sel)[8], float (&gts)[8],
+                      bool want_gates) {
+  uint64_t key[4];
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = 0;
+    lv[i] = 0.f;
+    if (e < E) {
+      lv[i] = logits[e];
+      key[i] = ((uint64_t)order_key32(lv[i]) << 32) | (uint32_t)(~(uint32_t)e);
+    }
+  }
+  float sl[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint64_t o = __shfl_xor(best, off, 64);
+      best = o > best ? o : best;
+    }
+    const int e = (int)(~(uint32_t)best);
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == e) { key[i] = 0; l = lv[i]; }
+    sl[j] = __shfl(l, e & 63, 64);
+    sel[j] = e;
+  }
+  if (want_gates) {
+    const double m = (double)sl[0];
+    double ex[8], z = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) { ex[j] = exp((double)sl[j] - m); z += ex[j]; }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) gts[j] = (float)(ex[j] / z);
+  }
+}
+
+// ------------------------------------------------------------------ gate/up
+
+struct GateUpT1 {
+  const uint8_t* gq;
+  const uint8_t* uq;
+  const float* gs;
+  const float* us;
+  int64_t mat_bytes;
+  int F, H, act, E, k;
+  const float* logits;   // [T][E]; nullptr: dense mode (expert 0, one slot per token)
+  const float* x;        // [T][H]
+  float* h;              // [T*slots][F]
+  int* idx_out;          // [T][k], written by the blocks with blockIdx.x == 0 and slot 0
+  float* gates_out;
+  int KS, RGW;           // K-slices per row, row-group waves per block
+};
+
+// Block = KS * RGW waves.  Wave (rg, ks) streams kNP row pairs (gate row f
+// and up row f) per lane group over K-slice ks.  With KS > 1 the slices meet
+// in LDS.  blockIdx.y = t * slots + j: token t's slot j (each pair of a
+// several-token call is an independent one-token problem).
+template <int FMT, int L, int kNP>
+__global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
+  constexpr int G = 64 / L, W = Fmt<FMT>::WPC;
+  extern __shared__ float lds[];  // [RGW][G][kNP][KS][2]
+  __shared__ int s_sel[8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane / L, t = lane % L;
+  const int ks = wave % a.KS, rg = wave / a.KS;
+  const int c0 = ks * L + t;  // this lane's chunk (one chunk per lane per slice)
+  const int slots = a.logits ? a.k : 1;
+  const int tok = blockIdx.y / slots, slot = blockIdx.y % slots;
+  float xv[1][W];
+  load_xv<FMT, L, 1>(xv, a.x + (int64_t)tok * a.H, c0);
+
+  int e = 0;
+  if (a.logits) {
+    if (wave == 0) {
+      int sel[8];
+      float gts[8];
+      const bool first = blockIdx.x == 0 && slot == 0;
+      wave_topk(a.logits + (int64_t)tok * a.E, a.E, a.k, lane, sel, gts, first);
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j < a.k) {
+            s_sel[j] = sel[j];
+            if (first) { a.idx_out[tok * a.k + j] = sel[j]; a.gates_out[tok * a.k + j] = gts[j]; }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    e = s_sel[slot];
+  }
+
+  const int fb = ((blockIdx.x * a.RGW + rg) * G + g) * kNP;
+  const int64_t rb = row_bytes(FMT, a.H);
+  const uint8_t* Gm = a.gq + (int64_t)e * a.mat_bytes;
+  const uint8_t* Um = a.uq + (int64_t)e * a.mat_bytes;
+  float pg[kNP], pu[kNP];
+  {
+    // rolling window: kD row pairs in flight while one pair is decoded
+    constexpr int kD = kNP < MD_GU_WINDOW ? kNP : MD_GU_WINDOW;
+    RowBuf<FMT, 1> bg[kD], bu[kD];
+    auto rowp = [&](const uint8_t* M, int p) { return M + (int64_t)min(fb + p, a.F - 1) * rb; };
+#pragma unroll
+    for (int p = 0; p < kD; ++p) {
+      load_row<FMT, L, 1>(bg[p], rowp(Gm, p), a.H, c0);
+      load_row<FMT, L, 1>(bu[p], rowp(Um, p), a.H, c0);
+    }
+#pragma unroll
+    for (int p = 0; p < kNP; ++p) {
+      pg[p] = row_dot<FMT, 1>(bg[p % kD], xv);
+      pu[p] = row_dot<FMT, 1>(bu[p % kD], xv);
+      if (p + kD < kNP) {
+        load_row<FMT, L, 1>(bg[p % kD], rowp(Gm, p + kD), a.H, c0);
+        load_row<FMT, L, 1>(bu[p % kD], rowp(Um, p + kD), a.H, c0);
+      }
+    }
+  }
+  const float sa = butterfly<kNP, L>(pg, t);
+  const float su = butterfly<kNP, L>(pu, t);
+  const int r = (t / (L / kNP)) % kNP;
+  const bool writer = (t % (L / kNP)) == 0;
+  auto finish = [&](int f, float av, float uv) {
+    if (f >= a.F) return;
+    float sg = 1.f, sv = 1.f;
+    if constexpr (Fmt<FMT>::ROW) {
+      sg = a.gs[(int64_t)e * a.F + f] * row_post<FMT>();
+      sv = a.us[(int64_t)e * a.F + f] * row_post<FMT>();
+    }
+    a.h[(int64_t)blockIdx.y * a.F + f] = act_f(a.act, av * sg) * (uv * sv);
+  };
+  if (a.KS == 1) {
+    if (writer) finish(fb + r, sa, su);
+    return;
+  }
+  float* red = lds + ((((rg * G + g) * kNP + r) * a.KS + ks) * 2);
+  if (writer) { red[0] = sa; red[1] = su; }
+  __syncthreads();
+  const int npairs = a.RGW * G * kNP;
+  for (int q = threadIdx.x; q < npairs; q += blockDim.x) {
+    const float* rq = lds + (int64_t)q * a.KS * 2;
+    float av = 0.f, uv = 0.f;
+    for (int s = 0; s < a.KS; ++s) { av += rq[2 * s]; uv += rq[2 * s + 1]; }
+    const int rgq = q / (G * kNP), gq_ = (q / kNP) % G, rq_ = q % kNP;
+    finish(((blockIdx.x * a.RGW + rgq) * G + gq_) * kNP + rq_, av, uv);
+  }
+}
+
+// ------------------------------------------------------------------ down
+
+struct DownT1 {
+  const uint8_t* dq;
+  const float* ds;
+  int64_t mat_bytes;
+  int H, F, k;
+  const int* idx;        // [T][k]; nullptr: dense mode (expert 0, gate 1, one slot)
+  const float* gates;    // [T][k]
+  const float* h;        // [T*k][F]
+  const float* y_add;    // [T][H], nullable: added to the combined result
+  float* y;              // [T][H]
+};
+
+// Block = k waves; wave j streams kNRW output rows of token t's slot j
+// expert (t = blockIdx.y).
+template <int FMT, int L, int CPL>
+__global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
+  constexpr int G = 64 / L, W = Fmt<FMT>::WPC, NR = kNRW / G;
+  __shared__ float red[8][kNRW];
+  static_assert(kNRW % G == 0, "rows per block");
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int g = lane / L, t = lane % L;
+  const int tok = blockIdx.y, p = tok * a.k + j;
+  const int e = a.idx ? a.idx[p] : 0;
+  float xv[CPL][W];
+  load_xv<FMT, L, CPL>(xv, a.h + (int64_t)p * a.F, t);
+  const int ib = blockIdx.x * kNRW + g * NR;
+  const int64_t rb = row_bytes(FMT, a.F);
+  const uint8_t* Dm = a.dq + (int64_t)e * a.mat_bytes;
+  float part[NR];
+  {
+    // rolling window: kD rows in flight while one row is decoded
+    constexpr int kD = NR < MD_DN_WINDOW ? NR : MD_DN_WINDOW;
+    RowBuf<FMT, CPL> b[kD];
+    auto rowp = [&](int r) { return Dm + (int64_t)min(ib + r, a.H - 1) * rb; };
+#pragma unroll
+    for (int r = 0; r < kD; ++r) load_row<FMT, L, CPL>(b[r], rowp(r), a.F, t);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      part[r] = row_dot<FMT, CPL>(b[r % kD], xv);
+      if (r + kD < NR) load_row<FMT, L, CPL>(b[r % kD], rowp(r + kD), a.F, t);
+    }
+  }
+  const float s = butterfly<NR, L>(part, t);
+  const int r = (t / (L / NR)) % NR;
+  if ((t % (L / NR)) == 0) {
+    const int i = ib + r;
+    float v = s;
+    if constexpr (Fmt<FMT>::ROW) v *= a.ds[(int64_t)e * a.H + min(i, a.H - 1)] * row_post<FMT>();
+    red[j][g * NR + r] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < kNRW) {
+    const int i = blockIdx.x * kNRW + threadIdx.x;
+    if (i < a.H) {
+      float v = 0.f;
+      if (a.idx) {
+        for (int q = 0; q < a.k; ++q) v = fmaf(a.gates[tok * a.k + q], red[q][threadIdx.x], v);
+      } else {
+        v = red[0][threadIdx.x];
+      }
+      if (a.y_add) v += a.y_add[(int64_t)tok * a.H + i];
+      a.y[(int64_t)tok * a.H + i] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+static int pow2_div(int n) {
+  int L = 64;
+  while (L > 1 && n % L) L >>= 1;
+  return L;
+}
+
+bool t1_supported(int fmt, int H, int F) {
+  const int ncg = nchunks(fmt, H), ncd = nchunks(fmt, F);
+  const int Lg = pow2_div(ncg), Ld = pow2_div(ncd);
+  if (Lg < 8 || Ld < 8) return false;
+  if (ncg / Lg > 16) return false;          // K-slices per block
+  const int cpl = ncd / Ld;
+  return cpl == 1 || cpl == 2 || cpl == 3;
+}
+
+hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
+                            int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const float* logits,
+                            const float* x, float* h, int* idx_out, float* gates_out, hipStream_t st) {
+  const int nc = nchunks(fmt, H);
+  const int L = pow2_div(nc), G = 64 / L;
+  GateUpT1 a{gq, uq, gs, us, mat_bytes, F, H, act, E, k, logits, x, h, idx_out, gates_out, nc / L, 1};
+  // row-group waves per block: fill up to 4 waves when one slice suffices
+  a.RGW = a.KS >= 4 ? 1 : 4 / a.KS;
+  // row pairs per lane group: as many as keep >= 2048 waves in flight
+  const int slots = (logits ? k : 1) * T;
+  int NP = MD_GU_MAXNP;
+  while (NP > 2 && (int64_t)((F + a.RGW * G * NP - 1) / (a.RGW * G * NP)) * slots * a.KS * a.RGW < 2048) NP /= 2;
+  const int pairs_per_block = a.RGW * G * NP;
+  const dim3 grid((F + pairs_per_block - 1) / pairs_per_block, slots);
+  const dim3 block(64 * a.KS * a.RGW);
+  const size_t lds = a.KS > 1 ? sizeof(float) * 2 * a.KS * pairs_per_block : 0;
+#define MD_GU(F_, L_, N_) \
+  if (fmt == F_ && L == L_ && NP == N_) { \
+    hipLaunchKernelGGL((k_gateup_t1<F_, L_, N_>), grid, block, lds, st, a); return hipGetLastError(); }
+#define MD_GUL(F_) MD_GU(F_, 64, 8) MD_GU(F_, 32, 8) MD_GU(F_, 16, 8) MD_GU(F_, 8, 8) \
+                   MD_GU(F_, 64, 4) MD_GU(F_, 32, 4) MD_GU(F_, 16, 4) MD_GU(F_, 8, 4) \
+                   MD_GU(F_, 64, 2) MD_GU(F_, 32, 2) MD_GU(F_, 16, 2) MD_GU(F_, 8, 2)
+  MD_GUL(Q8_0) MD_GUL(Q4_0) MD_GUL(I8_ROW) MD_GUL(I4_ROW)
+#undef MD_GUL
+#undef MD_GU
+  return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t mat_bytes, int H, int F, int k, int T,
+                          const int* idx, const float* gates, const float* h, const float* y_add, float* y,
+                          hipStream_t st) {
+  const int nc = nchunks(fmt, F);
+  const int L = pow2_div(nc), CPL = nc / L;
+  DownT1 a{dq, ds, mat_bytes, H, F, idx ? k : 1, idx, gates, h, y_add, y};
+  const dim3 grid((H + kNRW - 1) / kNRW, T), block(64 * a.k);
+#define MD_DN(F_, L_, C_) \
+  if (fmt == F_ && L == L_ && CPL == C_) { \
+    hipLaunchKernelGGL((k_down_t1<F_, L_, C_>), grid, block, 0, st, a); return hipGetLastError(); }
+#define MD_DNL(F_, L_) MD_DN(F_, L_, 1) MD_DN(F_, L_, 2) MD_DN(F_, L_, 3)
+#define MD_DNF(F_) MD_DNL(F_, 64) MD_DNL(F_, 32) MD_DNL(F_, 16) MD_DNL(F_, 8)
+  MD_DNF(Q8_0) MD_DNF(Q4_0) MD_DNF(I8_ROW) MD_DNF(I4_ROW)
+#undef MD_DNF
+#undef MD_DNL
+#undef MD_DN
+  return hipErrorInvalidConfiguration;
+}
+
+}  // namespace md

@@ -1,9 +1,8 @@
-// route.hip -- router logits, top-k selection with softmax gates, and the
-// expert dispatch (gfx950, wave64).
+// route.hip -- top-k selection with softmax gates for many tokens, the expert
+// dispatch, and the weight layout pass (gfx950, wave64).
 //
-// Logits are accumulated in fp64 (so the rounding to fp32 is independent of
-// the summation order except in vanishingly rare cases) and rounded once.
-// Selection uses 64-bit keys: the order-preserving image of the fp32 logit in
+// The logits come from k_router_rows (fp64 accumulation rounded once to
+// fp32).  Selection uses 64-bit keys: the order-preserving image of the fp32 logit in
 // the high word (with -0 folded onto +0) and the complemented expert index in
 // the low word, so one integer maximum picks the largest logit and, among
 // exact ties, the lower expert index -- the tie rule of the Camelid README,
@@ -12,56 +11,6 @@
 #include "kernels.hpp"
 
 namespace md {
-
-// -------------------------------------------------------------- logits
-
-// One wave per (expert e, K split s); every token of the call.  Partial sums
-// part[t][e][s] are reduced in a fixed order by the finalize kernel.
-__global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int T, int H,
-                                                const float* __restrict__ Wr, int E, int S,
-                                                double* __restrict__ part) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int e = gw / S, s = gw % S;
-  if (e >= E) return;
-  const int ks4 = H / S / 4;  // float4 per split (a multiple of 64)
-  const float4* w = reinterpret_cast<const float4*>(Wr + (int64_t)e * H) + s * ks4;
-  constexpr int TB = 4;
-  for (int t0 = 0; t0 < T; t0 += TB) {
-    double acc[TB] = {0.0, 0.0, 0.0, 0.0};
-    for (int j = lane; j < ks4; j += 64) {
-      const float4 wv = w[j];
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        if (t0 + b < T) {
-          const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)(t0 + b) * H)[s * ks4 + j];
-          acc[b] = fma((double)wv.x, (double)xv.x, acc[b]);
-          acc[b] = fma((double)wv.y, (double)xv.y, acc[b]);
-          acc[b] = fma((double)wv.z, (double)xv.z, acc[b]);
-          acc[b] = fma((double)wv.w, (double)xv.w, acc[b]);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < TB; ++b) {
-      const double v = wave_sum_f64(acc[b]);
-      if (lane == 0 && t0 + b < T) part[((int64_t)(t0 + b) * E + e) * S + s] = v;
-    }
-  }
-}
-
-int router_splits(int H, int E) {
-  int S = 1;
-  while (E * S < 1024 && (H / 256) % (2 * S) == 0) S *= 2;
-  return S;
-}
-
-hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
-                         hipStream_t st) {
-  const int waves = E * S;
-  hipLaunchKernelGGL(k_router, dim3((waves + 3) / 4), dim3(256), 0, st, x, T, H, Wr, E, S, part);
-  return hipGetLastError();
-}
 
 // -------------------------------------------------------------- select
 
@@ -85,10 +34,9 @@ MD_DEV uint64_t wave_max_u64(uint64_t v) {
 // expert (pairs of one expert are ordered by token, and a token selects an
 // expert at most once), exclusive scans give the offsets and the list of
 // active experts in ascending order.
-__global__ __launch_bounds__(1024) void k_route_finalize(const double* __restrict__ part, int S,
-                                                         const float* __restrict__ bias, int T, int E, int k,
-                                                         float* __restrict__ logits, int* __restrict__ idx,
-                                                         float* __restrict__ gates, DispOut d, int do_disp) {
+__global__ __launch_bounds__(1024) void k_route_finalize(const float* __restrict__ logits, int T, int E, int k,
+                                                         int* __restrict__ idx, float* __restrict__ gates, DispOut d,
+                                                         int do_disp) {
   __shared__ uint32_t mask[256][4];
   __shared__ int sel[128 * 8];
   __shared__ int cnt[256], poff[256], apos[256];
@@ -105,18 +53,16 @@ __global__ __launch_bounds__(1024) void k_route_finalize(const double* __restric
       key[i] = 0;
       lv[i] = 0.f;
       if (e < E) {
-        double a = 0.0;
-        for (int s = 0; s < S; ++s) a += part[((int64_t)t * E + e) * S + s];
-        if (bias) a += (double)bias[e];
-        const float l = (float)a;
+        const float l = logits[(int64_t)t * E + e];
         lv[i] = l;
-        if (logits) logits[(int64_t)t * E + e] = l;
         key[i] = ((uint64_t)order_key(l) << 32) | (uint32_t)(~(uint32_t)e);
       }
     }
     float sl[8];
     int se[8];
-    for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
       uint64_t best = key[0];
 #pragma unroll
       for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
@@ -133,16 +79,22 @@ __global__ __launch_bounds__(1024) void k_route_finalize(const double* __restric
     if (lane == 0) {
       const double m = (double)sl[0];
       double z = 0.0, ex[8];
-      for (int j = 0; j < k; ++j) { ex[j] = exp((double)sl[j] - m); z += ex[j]; }
-      for (int j = 0; j < k; ++j) {
-        idx[t * k + j] = se[j];
-        gates[t * k + j] = (float)(ex[j] / z);
-        sel[t * k + j] = se[j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) { ex[j] = exp((double)sl[j] - m); z += ex[j]; }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < k) {
+          idx[t * k + j] = se[j];
+          gates[t * k + j] = (float)(ex[j] / z);
+          sel[t * k + j] = se[j];
+        }
       }
     }
     if (do_disp && lane < k) {
       int e = 0;
-      for (int j = 0; j < k; ++j)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
         if (j == lane) e = se[j];
       atomicOr(&mask[e][t >> 5], 1u << (t & 31));
     }
@@ -194,11 +146,10 @@ __global__ __launch_bounds__(1024) void k_route_finalize(const double* __restric
   }
 }
 
-hipError_t launch_route_finalize(const double* part, int S, const float* bias, int T, int E, int k, float* logits,
-                                 int* idx, float* gates, const DispOut* d, hipStream_t st) {
+hipError_t launch_route_finalize(const float* logits, int T, int E, int k, int* idx, float* gates, const DispOut* d,
+                                 hipStream_t st) {
   DispOut dd = d ? *d : DispOut{nullptr, nullptr, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(k_route_finalize, dim3(1), dim3(1024), 0, st, part, S, bias, T, E, k, logits, idx, gates, dd,
-                     d ? 1 : 0);
+  hipLaunchKernelGGL(k_route_finalize, dim3(1), dim3(1024), 0, st, logits, T, E, k, idx, gates, dd, d ? 1 : 0);
   return hipGetLastError();
 }
 
