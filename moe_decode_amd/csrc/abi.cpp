@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/moe_decode.h"
+#include "moe_decode.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -91,14 +91,23 @@ int max_active(int T, int E, int k) { return T * k < E ? T * k : E; }
 
 // ---- MoE workspace layout ------------------------------------------------
 struct MoeWs {
-  size_t logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
+  size_t part, logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
+  size_t x_hi, x_lo, h_hi, h_lo, hs_hi, hs_lo;  // bf16 pairs of the prefill path
 };
+
+// Few tokens on shapes the one-token kernels cover: independent (token, slot)
+// pairs; otherwise the grouped GEMM on the matrix cores.
+bool use_pairs(const md_moe_layer* L, int T) {
+  return T <= kMaxPairT && md::t1_supported(L->type, L->H, L->F) &&
+         (!L->has_shared || md::t1_supported(L->shared.gate.type, L->H, L->shared.gate.rows));
+}
 
 MoeWs moe_ws(const md_moe_layer* L, int T) {
   MoeWs w{};
   const int E = L->E, k = L->k, H = L->H, F = L->F;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.part = take(sizeof(double) * (size_t)T * E * md::router_splits(H, E));
   w.logits = take(sizeof(float) * T * E);
   w.idx = take(sizeof(int) * T * k);
   w.gates = take(sizeof(float) * T * k);
@@ -108,10 +117,20 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
   w.pairs = take(sizeof(int) * T * k);
   w.pos = take(sizeof(int) * T * k);
   w.h = take(sizeof(float) * (size_t)T * k * F);
-  if (T > kMaxPairT) w.o = take(sizeof(float) * (size_t)T * k * H);
   if (L->has_shared) {
     w.h_s = take(sizeof(float) * (size_t)T * L->shared.gate.rows);
     w.y_s = take(sizeof(float) * (size_t)T * H);
+  }
+  if (!use_pairs(L, T)) {
+    w.o = take(sizeof(float) * (size_t)T * k * H);
+    w.x_hi = take(2 * (size_t)T * H);
+    w.x_lo = take(2 * (size_t)T * H);
+    w.h_hi = take(2 * (size_t)T * k * F);
+    w.h_lo = take(2 * (size_t)T * k * F);
+    if (L->has_shared) {
+      w.hs_hi = take(2 * (size_t)T * L->shared.gate.rows);
+      w.hs_lo = take(2 * (size_t)T * L->shared.gate.rows);
+    }
   }
   w.total = off;
   return w;
@@ -152,13 +171,31 @@ md_status check_ws(void* ws, size_t have, size_t need) {
   return MD_OK;
 }
 
+typedef unsigned short u16;
+
+// dense FFN (or shared expert) for a chunk of tokens on the matrix cores:
+// x_hi/x_lo hold x as bf16 pairs; h and its pair buffers are scratch
+md_status run_ffn_mfma(const md_ffn* f, const u16* x_hi, const u16* x_lo, int T, float* h, u16* h_hi, u16* h_lo,
+                       float* y, hipStream_t st) {
+  const int H = f->gate.cols, F = f->gate.rows, fmt = f->gate.type;
+  md::Disp d{nullptr, nullptr, nullptr, nullptr, 1, T};
+  hipError_t e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(f->gate.q),
+                                     static_cast<const uint8_t*>(f->up.q), f->gate.row_scale, f->up.row_scale, 0, F,
+                                     H, f->act, d, 1, x_hi, x_lo, true, h, h_hi, h_lo, st);
+  if (e != hipSuccess) return hip_fail(e, "ffn gate/up launch");
+  e = md::launch_moe_mfma(fmt, false, static_cast<const uint8_t*>(f->down.q), nullptr, f->down.row_scale, nullptr, 0,
+                          H, F, f->act, d, 1, h_hi, h_lo, false, y, nullptr, nullptr, st);
+  if (e != hipSuccess) return hip_fail(e, "ffn down launch");
+  return MD_OK;
+}
+
 // dense FFN (or shared expert) through the MoE kernels with the identity dispatch
 md_status run_ffn(const md_ffn* f, const float* x, int T, float* h, float* y, hipStream_t st) {
   const int H = f->gate.cols, F = f->gate.rows, fmt = f->gate.type;
   if (T <= kMaxPairT && md::t1_supported(fmt, H, F)) {
     hipError_t e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(f->gate.q),
                                         static_cast<const uint8_t*>(f->up.q), f->gate.row_scale, f->up.row_scale, 0,
-                                        F, H, f->act, 1, 1, T, nullptr, x, h, nullptr, nullptr, st);
+                                        F, H, f->act, 1, 1, T, nullptr, 1, nullptr, x, h, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "ffn gate/up launch");
     e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(f->down.q), f->down.row_scale, 0, H, F, 1, T, nullptr,
                            nullptr, h, nullptr, y, st);
@@ -251,7 +288,7 @@ md_status md_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, si
   if (T > kMaxT || E > kMaxE || k > kMaxK) return fail(MD_ERR_UNSUPPORTED, "T <= %d, E <= %d, k <= %d", kMaxT, kMaxE, kMaxK);
   md_status s = check_width("H", H);
   if (s != MD_OK) return s;
-  *bytes = align256(sizeof(float) * (size_t)T * E);
+  *bytes = align256(sizeof(double) * (size_t)T * E * md::router_splits(H, E)) + align256(sizeof(float) * (size_t)T * E);
   return ok();
 }
 
@@ -266,11 +303,19 @@ md_status md_moe_route_topk(const float* x, int32_t T, int32_t H, const float* W
       (logits && !aligned16(logits)))
     return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
-  float* l = logits ? logits : static_cast<float*>(workspace);
-  hipError_t e = md::launch_router_rows(x, T, H, W_r, bias, E, l, stream);
+  const int S = md::router_splits(H, E);
+  double* part = static_cast<double*>(workspace);
+  hipError_t e = md::launch_router_part(x, T, H, W_r, E, S, part, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
-  e = md::launch_route_finalize(l, T, E, k, idx, gates, nullptr, stream);
+  e = md::launch_route_finalize(part, S, bias, T, E, k, logits, idx, gates, nullptr, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "route finalize launch");
+}
+
+static size_t ffn_ws_bytes(const md_ffn* f, int T) {
+  const size_t H = f->gate.cols, F = f->gate.rows;
+  size_t b = align256(sizeof(float) * T * F);
+  if (T > kMaxPairT) b += 2 * align256(2 * T * H) + 2 * align256(2 * T * F);
+  return b;
 }
 
 md_status md_ffn_workspace_size(const md_ffn* f, int32_t T, size_t* bytes) {
@@ -280,7 +325,7 @@ md_status md_ffn_workspace_size(const md_ffn* f, int32_t T, size_t* bytes) {
   if (!bytes) return fail(MD_ERR_INVALID_ARG, "null bytes");
   if (T <= 0) return fail(MD_ERR_SHAPE, "T %d", T);
   if (T > kMaxT) return fail(MD_ERR_UNSUPPORTED, "T %d > %d", T, kMaxT);
-  *bytes = align256(sizeof(float) * (size_t)T * f->gate.rows);
+  *bytes = ffn_ws_bytes(f, T);
   return ok();
 }
 
@@ -292,7 +337,21 @@ md_status md_ffn_forward(const md_ffn* f, const float* x, int32_t T, float* y, v
   if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
   if (!aligned16(x) || !aligned16(y)) return fail(MD_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
-  s = run_ffn(f, x, T, static_cast<float*>(workspace), y, stream);
+  char* ws = static_cast<char*>(workspace);
+  float* h = reinterpret_cast<float*>(ws);
+  if (T <= kMaxPairT) {
+    s = run_ffn(f, x, T, h, y, stream);
+    return s == MD_OK ? ok() : s;
+  }
+  const size_t H = f->gate.cols, F = f->gate.rows;
+  size_t off = align256(sizeof(float) * T * F);
+  u16* x_hi = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * H);
+  u16* x_lo = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * H);
+  u16* h_hi = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * F);
+  u16* h_lo = reinterpret_cast<u16*>(ws + off);
+  hipError_t e = md::launch_split_bf16(x, (int64_t)T * H, x_hi, x_lo, stream);
+  if (e != hipSuccess) return hip_fail(e, "split launch");
+  s = run_ffn_mfma(f, x_hi, x_lo, T, h, h_hi, h_lo, y, stream);
   return s == MD_OK ? ok() : s;
 }
 
@@ -334,17 +393,26 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   const int64_t dn_bytes = (int64_t)H * md::row_bytes(fmt, F);
   float* logits = static_cast<float*>(P(w.logits));
   float* h = static_cast<float*>(P(w.h));
-  const bool t1 = T <= kMaxPairT && md::t1_supported(fmt, H, F) &&
-                  (!L->has_shared || md::t1_supported(L->shared.gate.type, H, L->shared.gate.rows));
+  const bool t1 = use_pairs(L, T);
 
   // shared expert: independent of the routing, enqueued first
+  u16* x_hi = t1 ? nullptr : static_cast<u16*>(P(w.x_hi));
+  u16* x_lo = t1 ? nullptr : static_cast<u16*>(P(w.x_lo));
   if (!mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
+  if (!t1) {
+    e = md::launch_split_bf16(x, (int64_t)T * H, x_hi, x_lo, stream);
+    if (e != hipSuccess) return hip_fail(e, "split launch");
+  }
   if (L->has_shared) {
-    s = run_ffn(&L->shared, x, T, static_cast<float*>(P(w.h_s)), y_s, stream);
+    if (t1) s = run_ffn(&L->shared, x, T, static_cast<float*>(P(w.h_s)), y_s, stream);
+    else s = run_ffn_mfma(&L->shared, x_hi, x_lo, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
+                          static_cast<u16*>(P(w.hs_lo)), y_s, stream);
     if (s != MD_OK) return s;
   }
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
-  e = md::launch_router_rows(x, T, H, L->W_r, L->router_bias, E, logits, stream);
+  const int S = md::router_splits(H, E);
+  double* part = static_cast<double*>(P(w.part));
+  e = md::launch_router_part(x, T, H, L->W_r, E, S, part, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");
 
@@ -354,8 +422,8 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     // one-token problem
     if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
     e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
-                             L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, logits, x, h, idx, gates,
-                             stream);
+                             L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, part, S, L->router_bias, x,
+                             h, idx, gates, stream);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
     if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
     e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
@@ -366,22 +434,26 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     return ok();
   }
 
+  // a chunk of tokens: group the (token, slot) pairs by expert, then one
+  // grouped GEMM per stage on the matrix cores, each expert read once
   md::DispOut dout{static_cast<int*>(P(w.n_active)), static_cast<int*>(P(w.active_e)),
                    static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos))};
-  e = md::launch_route_finalize(logits, T, E, k, idx, gates, &dout, stream);
+  e = md::launch_route_finalize(part, S, L->router_bias, T, E, k, logits, idx, gates, &dout, stream);
   if (e != hipSuccess) return hip_fail(e, "route finalize launch");
   if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
 
   md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T};
   const int A = max_active(T, E, k);
   float* o = static_cast<float*>(P(w.o));
-  md::GemvCfg cg = md::gateup_config(fmt, F, H, A, T);
-  e = md::launch_gateup(fmt, cg, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
-                        L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, x, h, stream);
+  u16* h_hi = static_cast<u16*>(P(w.h_hi));
+  u16* h_lo = static_cast<u16*>(P(w.h_lo));
+  e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                          L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, A, x_hi, x_lo, true, h, h_hi, h_lo,
+                          stream);
   if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
-  md::GemvCfg cd = md::down_config(fmt, H, F, A, T);
-  e = md::launch_down(fmt, cd, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, d, h, o, stream);
+  e = md::launch_moe_mfma(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
+                          dn_bytes, H, F, L->act, d, A, h_hi, h_lo, false, o, nullptr, nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "down launch");
   if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0)) return hip_fail(e, "event record");
   e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, y, stream);

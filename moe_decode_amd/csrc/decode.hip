@@ -1,10 +1,12 @@
 // decode.hip -- the one-token decode path of the MoE layer (gfx950, wave64).
 //
 // Three launches per layer call (five with a shared expert):
-//   k_router_rows  one workgroup per expert: logits = W_r x (+ b), fp64
-//                  accumulation, rounded once to fp32.
-//   k_gateup_t1    each workgroup first selects the top-k experts from the
-//                  logits (64-bit order keys: larger logit, then lower index),
+//   k_router_part  logits = W_r x (+ b) with fp64 accumulation, K split in S
+//                  slices across workgroups (fp64 partials).
+//   k_gateup_t1    each workgroup first forms the logits (partials added in a
+//                  fixed order, plus the bias, rounded once to fp32) and
+//                  selects the top-k experts (64-bit order keys: larger
+//                  logit, then lower index),
 //                  then streams gate and up rows of its slot's expert against
 //                  the activations held in VGPRs, and writes h = act(a) * u.
 //   k_down_t1      each workgroup owns a tile of output rows; wave j streams
@@ -93,17 +95,19 @@ MD_DEV void load_xv(float (&xv)[CPL][Fmt<FMT>::WPC], const float* x, int c0) {
 
 // ------------------------------------------------------------------ router
 
-// One workgroup (4 waves) per expert e; the waves split K in four, each lane
-// accumulates its slice in fp64 for up to 4 tokens at a time; the four wave
-// sums are added in a fixed order.
-__global__ __launch_bounds__(256) void k_router_rows(const float* __restrict__ x, int T, int H,
-                                                     const float* __restrict__ Wr, const float* __restrict__ bias,
-                                                     int E, float* __restrict__ logits) {
+// Block (e, s): expert e, K-slice s of S; the four waves split the slice,
+// each lane accumulates in fp64 for up to 4 tokens at a time, and the wave
+// sums are added in a fixed order into part[t][e][s].  The consumer adds the
+// S partials in order, then the bias, and rounds once to fp32.
+__global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x, int T, int H,
+                                                     const float* __restrict__ Wr, int E, int S,
+                                                     double* __restrict__ part) {
   __shared__ double red[4][4];
-  const int e = blockIdx.x;
+  const int e = blockIdx.x / S, sl = blockIdx.x % S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ks = H / 4;                 // a multiple of 64
-  const float* w = Wr + (int64_t)e * H + wave * ks;
+  const int ks = H / S / 4;             // elements per wave, a multiple of 64
+  const int k0 = sl * (H / S) + wave * ks;
+  const float* w = Wr + (int64_t)e * H + k0;
   const bool vec = (ks % 256) == 0;
   for (int t0 = 0; t0 < T; t0 += 4) {
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256) void k_router_rows(const float* __restrict__ x
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           if (t0 + b < T) {
-            const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)(t0 + b) * H + wave * ks)[j];
+            const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)(t0 + b) * H + k0)[j];
             acc[b] = fma((double)wv.x, (double)xv.x, acc[b]);
             acc[b] = fma((double)wv.y, (double)xv.y, acc[b]);
             acc[b] = fma((double)wv.z, (double)xv.z, acc[b]);
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(256) void k_router_rows(const float* __restrict__ x
         const double wv = (double)w[j];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          if (t0 + b < T) acc[b] = fma(wv, (double)x[(int64_t)(t0 + b) * H + wave * ks + j], acc[b]);
+          if (t0 + b < T) acc[b] = fma(wv, (double)x[(int64_t)(t0 + b) * H + k0 + j], acc[b]);
       }
     }
 #pragma unroll
@@ -137,17 +141,27 @@ __global__ __launch_bounds__(256) void k_router_rows(const float* __restrict__ x
     __syncthreads();
     if (threadIdx.x < 4 && t0 + (int)threadIdx.x < T) {
       const int b = threadIdx.x;
-      double a = ((red[0][b] + red[1][b]) + red[2][b]) + red[3][b];
-      if (bias) a += (double)bias[e];
-      logits[(int64_t)(t0 + b) * E + e] = (float)a;
+      part[((int64_t)(t0 + b) * E + e) * S + sl] = ((red[0][b] + red[1][b]) + red[2][b]) + red[3][b];
     }
     __syncthreads();
   }
 }
 
-hipError_t launch_router_rows(const float* x, int T, int H, const float* Wr, const float* bias, int E,
-                              float* logits, hipStream_t st) {
-  hipLaunchKernelGGL(k_router_rows, dim3(E), dim3(256), 0, st, x, T, H, Wr, bias, E, logits);
+#ifndef MD_ROUTER_BLOCKS
+#define MD_ROUTER_BLOCKS 256
+#endif
+// K-slices per expert: the fewest that give at least MD_ROUTER_BLOCKS blocks
+int router_splits(int H, int E) {
+  const int units = H / 256;  // K-slices stay multiples of 256
+  int S = 1;
+  for (int c = 1; c <= 8; ++c)
+    if (units % c == 0) { S = c; if (E * c >= MD_ROUTER_BLOCKS) break; }
+  return S;
+}
+
+hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_router_part, dim3(E * S), dim3(256), 0, st, x, T, H, Wr, E, S, part);
   return hipGetLastError();
 }
 
@@ -160,8 +174,8 @@ MD_DEV uint32_t order_key32(float l) {
 
 // Wave-level top-k of one token's E logits (E <= 256).  All lanes return the
 // same k experts in selection order and, when asked, their gates.
-MD_DEV void wave_topk(const float* __restrict__ logits, int E, int k, int lane, int (&sel)[8], float (&gts)[8],
-                      bool want_gates) {
+MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __restrict__ bias, int E, int k, int lane,
+                      int (&sel)[8], float (&gts)[8], bool want_gates) {
   uint64_t key[4];
   float lv[4];
 #pragma unroll
@@ -170,7 +184,10 @@ MD_DEV void wave_topk(const float* __restrict__ logits, int E, int k, int lane, 
     key[i] = 0;
     lv[i] = 0.f;
     if (e < E) {
-      lv[i] = logits[e];
+      double a = 0.0;
+      for (int s = 0; s < S; ++s) a += part[(int64_t)e * S + s];
+      if (bias) a += (double)bias[e];
+      lv[i] = (float)a;
       key[i] = ((uint64_t)order_key32(lv[i]) << 32) | (uint32_t)(~(uint32_t)e);
     }
   }
@@ -215,7 +232,9 @@ struct GateUpT1 {
   const float* us;
   int64_t mat_bytes;
   int F, H, act, E, k;
-  const float* logits;   // [T][E]; nullptr: dense mode (expert 0, one slot per token)
+  const double* part;    // router partials [T][E][S]; nullptr: dense mode (expert 0, one slot per token)
+  const float* bias;     // router bias [E] or nullptr
+  int S;
   const float* x;        // [T][H]
   float* h;              // [T*slots][F]
   int* idx_out;          // [T][k], written by the blocks with blockIdx.x == 0 and slot 0
@@ -236,18 +255,18 @@ __global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
   const int g = lane / L, t = lane % L;
   const int ks = wave % a.KS, rg = wave / a.KS;
   const int c0 = ks * L + t;  // this lane's chunk (one chunk per lane per slice)
-  const int slots = a.logits ? a.k : 1;
+  const int slots = a.part ? a.k : 1;
   const int tok = blockIdx.y / slots, slot = blockIdx.y % slots;
   float xv[1][W];
   load_xv<FMT, L, 1>(xv, a.x + (int64_t)tok * a.H, c0);
 
   int e = 0;
-  if (a.logits) {
+  if (a.part) {
     if (wave == 0) {
       int sel[8];
       float gts[8];
       const bool first = blockIdx.x == 0 && slot == 0;
-      wave_topk(a.logits + (int64_t)tok * a.E, a.E, a.k, lane, sel, gts, first);
+      wave_topk(a.part + (int64_t)tok * a.E * a.S, a.S, a.bias, a.E, a.k, lane, sel, gts, first);
       if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -403,15 +422,16 @@ bool t1_supported(int fmt, int H, int F) {
 }
 
 hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
-                            int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const float* logits,
-                            const float* x, float* h, int* idx_out, float* gates_out, hipStream_t st) {
+                            int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const double* part, int S,
+                            const float* bias, const float* x, float* h, int* idx_out, float* gates_out,
+                            hipStream_t st) {
   const int nc = nchunks(fmt, H);
   const int L = pow2_div(nc), G = 64 / L;
-  GateUpT1 a{gq, uq, gs, us, mat_bytes, F, H, act, E, k, logits, x, h, idx_out, gates_out, nc / L, 1};
+  GateUpT1 a{gq, uq, gs, us, mat_bytes, F, H, act, E, k, part, bias, S, x, h, idx_out, gates_out, nc / L, 1};
   // row-group waves per block: fill up to 4 waves when one slice suffices
   a.RGW = a.KS >= 4 ? 1 : 4 / a.KS;
   // row pairs per lane group: as many as keep >= 2048 waves in flight
-  const int slots = (logits ? k : 1) * T;
+  const int slots = (part ? k : 1) * T;
   int NP = MD_GU_MAXNP;
   while (NP > 2 && (int64_t)((F + a.RGW * G * NP - 1) / (a.RGW * G * NP)) * slots * a.KS * a.RGW < 2048) NP /= 2;
   const int pairs_per_block = a.RGW * G * NP;

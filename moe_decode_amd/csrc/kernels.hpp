@@ -46,19 +46,29 @@ GemvCfg qgemv_config(int fmt, int N, int K, int batch);
 hipError_t launch_qgemv(int fmt, int xt, const GemvCfg& c, const uint8_t* W, const float* scales, int N, int K,
                         const void* x, int batch, float* y, float* partial, hipStream_t st);
 
-hipError_t launch_router_rows(const float* x, int T, int H, const float* Wr, const float* bias, int E,
-                              float* logits, hipStream_t st);
-hipError_t launch_route_finalize(const float* logits, int T, int E, int k, int* idx, float* gates,
-                                 const DispOut* d, hipStream_t st);
+int router_splits(int H, int E);
+hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
+                              hipStream_t st);
+hipError_t launch_route_finalize(const double* part, int S, const float* bias, int T, int E, int k, float* logits,
+                                 int* idx, float* gates, const DispOut* d, hipStream_t st);
 
 // one-token decode path (decode.hip)
 bool t1_supported(int fmt, int H, int F);
 hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
-                            int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const float* logits,
-                            const float* x, float* h, int* idx_out, float* gates_out, hipStream_t st);
+                            int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const double* part, int S,
+                            const float* bias, const float* x, float* h, int* idx_out, float* gates_out,
+                            hipStream_t st);
 hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t mat_bytes, int H, int F, int k, int T,
                           const int* idx, const float* gates, const float* h, const float* y_add, float* y,
                           hipStream_t st);
+
+// prefill grouped GEMM on the matrix cores (prefill.hip)
+hipError_t launch_split_bf16(const float* x, int64_t n, unsigned short* hi, unsigned short* lo, hipStream_t st);
+bool mfma_supported(int K);
+hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
+                           const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d, int max_active,
+                           const unsigned short* a_hi, const unsigned short* a_lo, bool act_by_token, float* out,
+                           unsigned short* out_hi, unsigned short* out_lo, hipStream_t st);
 
 GemvCfg gateup_config(int fmt, int F, int H, int max_active, int T);
 hipError_t launch_gateup(int fmt, const GemvCfg& c, const uint8_t* gq, const uint8_t* uq, const float* gs,

@@ -1,2 +1,335 @@
-// prefill.hip -- placeholder, filled in with the MFMA grouped GEMM
+// prefill.hip -- grouped GEMM of a token chunk through its experts on the
+// bf16 matrix cores (gfx950 v_mfma_f32_16x16x32_bf16).
+//
+// Every expert's weight rows are read from HBM once per call and reused for
+// all the tokens routed to it (the TurboFieldfare summary, "memory and expert
+// streaming": prefill in chunks of at most 128 tokens reusing each loaded
+// expert across the prompt rows).
+//
+// A block owns 64 weight rows of one active expert (gate/up stage: gate rows
+// f0..f0+31 and up rows f0..f0+31, so the activation fuses in the epilogue;
+// down stage: 64 output rows) and one tile of 16 of the expert's tokens
+// (blockIdx.z); an expert with more tokens has its rows streamed once per
+// tile, the repeats served mostly from the on-chip caches.  K runs in tiles of
+// 256 weights: the next two tiles' weights, scales and activations are loaded
+// with coalesced 16-byte loads into registers while the current tile,
+// double-buffered in LDS, feeds the matrix cores.
+//
+// Exactness: every weight code is an integer of at most 8 significant bits
+// (4-bit codes are taken as 16 * value, see common.hpp), so its bf16 image is
+// exact; activations enter as a bf16 pair hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi) (16 significant bits); the MFMA accumulates in fp32.
+// A 32-wide MFMA step covers exactly one Q8_0/Q4_0 block, so the block scale
+// is applied to the step's partial sums before they join the accumulator;
+// per-row scales are applied once at the end.
 #include "common.hpp"
+#include "kernels.hpp"
+
+namespace md {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+constexpr int kRows = 64;         // weight rows per block
+constexpr int kKT = 256;          // K tile (8 MFMA steps of 32)
+constexpr int kTok = 16;          // tokens per MFMA tile
+constexpr int kAST = kKT + 8;     // LDS row stride of an activation tile (16-byte pad: the 16
+                                  // token rows of one operand read land in distinct banks)
+
+// -------------------------------------------------------- activations -> bf16 pair
+
+__global__ __launch_bounds__(256) void k_split_bf16(const float* __restrict__ x, int64_t n, u16* __restrict__ hi,
+                                                    u16* __restrict__ lo) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float v = x[i];
+  const __bf16 h = (__bf16)v;
+  const __bf16 l = (__bf16)(v - (float)h);
+  hi[i] = __builtin_bit_cast(u16, h);
+  lo[i] = __builtin_bit_cast(u16, l);
+}
+
+hipError_t launch_split_bf16(const float* x, int64_t n, u16* hi, u16* lo, hipStream_t st) {
+  hipLaunchKernelGGL(k_split_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, n, hi, lo);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------- grouped GEMM
+
+template <int FMT>
+struct Tile {
+  static constexpr bool B8 = (FMT == Q8_0 || FMT == I8_ROW);
+  static constexpr int WB = B8 ? kKT : kKT / 2;       // weight bytes per row per K tile
+  static constexpr int WSTR = WB + 16;                 // LDS row stride (bank spread)
+  static constexpr int WCH = kRows * WB / 16;          // 16-byte weight chunks per tile
+  static constexpr int WPT = WCH / 256;                // chunks per thread (2 or 4)
+  static constexpr bool BLK = (FMT == Q8_0 || FMT == Q4_0);
+};
+
+struct MfmaArgs {
+  const uint8_t* wq;     // gate (gate/up stage) or down weights, expert-major
+  const uint8_t* wq2;    // up weights (gate/up stage)
+  const float* ws;       // per-row scales of wq (per-row formats)
+  const float* ws2;
+  int64_t mat_bytes;     // bytes per expert matrix
+  int M, K;              // rows per matrix (F or H), columns
+  int act;
+  Disp d;
+  const u16* a_hi;       // activation pairs, rows of K
+  const u16* a_lo;
+  int act_by_token;      // activation row = token of the position (x) or the position (h)
+  float* out;            // h [pos][F] or o [pos][H]
+  u16* out_hi;           // h as a bf16 pair for the next stage (gate/up stage)
+  u16* out_lo;
+};
+
+template <int FMT>
+MD_DEV bf16x8 decode_a(const uint8_t* p) {
+  bf16x8 a;
+  if constexpr (Tile<FMT>::B8) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const unsigned w[2] = {u.x, u.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) a[4 * h + b] = (__bf16)(float)(signed char)(w[h] >> (8 * b));
+  } else if constexpr (FMT == Q4_0) {
+    // bytes b: low nibble = step weight 4q+b, high = 16+4q+b; elements [lo0..3, hi0..3]
+    const unsigned v = *reinterpret_cast<const unsigned*>(p) ^ 0x88888888u;
+    const unsigned lo = opaque((v << 4) & 0xF0F0F0F0u), hi = opaque(v & 0xF0F0F0F0u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      a[b] = (__bf16)(float)(signed char)(lo >> (8 * b));
+      a[4 + b] = (__bf16)(float)(signed char)(hi >> (8 * b));
+    }
+  } else {  // I4_ROW: byte b holds step weights 8q+2b (low) and 8q+2b+1 (high)
+    const unsigned u = *reinterpret_cast<const unsigned*>(p);
+    const unsigned lo = opaque((u << 4) & 0xF0F0F0F0u), hi = opaque(u & 0xF0F0F0F0u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      a[2 * b] = (__bf16)(float)(signed char)(lo >> (8 * b));
+      a[2 * b + 1] = (__bf16)(float)(signed char)(hi >> (8 * b));
+    }
+  }
+  return a;
+}
+
+// Activation operand: the 8 values of token j that pair with decode_a's
+// elements for lane group q in step s.
+template <int FMT>
+MD_DEV bf16x8 load_b(const u16* tile, int j, int s, int q) {
+  const u16* r = tile + j * kAST + 32 * s;
+  if constexpr (FMT == Q4_0) {
+    const uint2 a = *reinterpret_cast<const uint2*>(r + 4 * q);
+    const uint2 b = *reinterpret_cast<const uint2*>(r + 16 + 4 * q);
+    const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(r + 8 * q);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+template <int FMT, int GU>
+__global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
+  using TL = Tile<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kRows * TL::WSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][kRows * 8];
+  __shared__ __attribute__((aligned(16))) u16 s_hi[2][kTok * kAST];
+  __shared__ __attribute__((aligned(16))) u16 s_lo[2][kTok * kAST];
+  __shared__ float s_up[32][kTok];
+
+  struct { int e, p0, p1; } er;
+  if (a.d.n_active == nullptr) {  // dense FFN: one expert, positions = tokens
+    if (blockIdx.y != 0) return;
+    er.e = 0; er.p0 = 0; er.p1 = a.d.T;
+  } else {
+    if ((int)blockIdx.y >= *a.d.n_active) return;
+    er.e = a.d.active_e[blockIdx.y];
+    er.p0 = a.d.active_off[blockIdx.y];
+    er.p1 = a.d.active_off[blockIdx.y + 1];
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, li = lane & 15;
+  const int64_t rb = row_bytes(FMT, a.K);
+  const int nkt = a.K / kKT;
+  // block rows: gate/up stage -> 32 gate + 32 up rows of f0..f0+31
+  const int r0 = GU ? blockIdx.x * 32 : blockIdx.x * kRows;
+
+  auto row_ptr = [&](int r) -> const uint8_t* {  // r: block row 0..63
+    if (GU) {
+      const int f = min(r0 + (r & 31), a.M - 1);
+      const uint8_t* base = (r < 32 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes;
+      return base + (int64_t)f * rb;
+    }
+    return a.wq + (int64_t)er.e * a.mat_bytes + (int64_t)min(r0 + r, a.M - 1) * rb;
+  };
+  auto pos_token = [&](int pos) { return a.d.n_active == nullptr ? pos : a.d.pairs[pos] / a.d.k; };
+
+  {
+    const int t0 = er.p0 + (int)blockIdx.z * kTok;  // this block's 16-token tile
+    if (t0 >= er.p1) return;
+    const int nt = min(kTok, er.p1 - t0);
+    // this thread's activation rows for staging: token slot jj = tid / 16, piece pp = tid % 16
+    const int jj = tid >> 4, pp = tid & 15;
+    const u16* ahi = nullptr;
+    const u16* alo = nullptr;
+    if (jj < nt) {
+      const int row = a.act_by_token ? pos_token(t0 + jj) : t0 + jj;
+      ahi = a.a_hi + (int64_t)row * a.K;
+      alo = a.a_lo + (int64_t)row * a.K;
+    }
+    // two register sets: tile kt+1 waits in one while tile kt+2 is in flight
+    u32x4 rw[2][TL::WPT];
+    u32x4 rs[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    uint4 rh[2][2], rl[2][2];
+    auto gload = [&](int kt, int set) {
+#pragma unroll
+      for (int i = 0; i < TL::WPT; ++i) {
+        const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
+        rw[set][i] = ld_stream(row_ptr(r) + (int64_t)kt * TL::WB + 16 * piece);
+      }
+      if constexpr (TL::BLK) {
+        if (tid < kRows) {
+          const int scoff = FMT == Q8_0 ? a.K : (a.K / 32) * 16;
+          rs[set] = *reinterpret_cast<const u32x4*>(row_ptr(tid) + scoff + 16 * kt);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (ahi) {
+          rh[set][i] = *reinterpret_cast<const uint4*>(ahi + kt * kKT + 16 * pp + 8 * i);
+          rl[set][i] = *reinterpret_cast<const uint4*>(alo + kt * kKT + 16 * pp + 8 * i);
+        } else {
+          rh[set][i] = make_uint4(0u, 0u, 0u, 0u);
+          rl[set][i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    };
+    auto lstore = [&](int buf, int set) {
+#pragma unroll
+      for (int i = 0; i < TL::WPT; ++i) {
+        const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
+        *reinterpret_cast<u32x4*>(&s_w[buf][r * TL::WSTR + 16 * piece]) = rw[set][i];
+      }
+      if constexpr (TL::BLK) {
+        if (tid < kRows) *reinterpret_cast<u32x4*>(&s_sc[buf][tid * 8]) = rs[set];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        *reinterpret_cast<uint4*>(&s_hi[buf][jj * kAST + 16 * pp + 8 * i]) = rh[set][i];
+        *reinterpret_cast<uint4*>(&s_lo[buf][jj * kAST + 16 * pp + 8 * i]) = rl[set][i];
+      }
+    };
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int wr = wave * 16;  // this wave's first block row
+    auto compute = [&](int buf) {
+#pragma unroll
+      for (int s = 0; s < kKT / 32; ++s) {
+        const uint8_t* wp = &s_w[buf][(wr + li) * TL::WSTR + (TL::B8 ? 32 * s + 8 * q : 16 * s + 4 * q)];
+        const bf16x8 av = decode_a<FMT>(wp);
+        const bf16x8 bh = load_b<FMT>(s_hi[buf], li, s, q);
+        const bf16x8 bl = load_b<FMT>(s_lo[buf], li, s, q);
+        if constexpr (TL::BLK) {
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float d = h2f(s_sc[buf][(wr + 4 * q + v) * 8 + s]);
+            if constexpr (FMT == Q4_0) d *= 0.0625f;
+            acc[v] = fmaf(d, z[v], acc[v]);
+          }
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc, 0, 0, 0);
+        }
+      }
+    };
+    // iteration kt: LDS buffer kt&1 holds tile kt, register set (kt+1)&1
+    // holds tile kt+1, tile kt+2 is loaded into set kt&1
+    gload(0, 0);
+    if (nkt > 1) gload(1, 1);
+    lstore(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+      if (kt + 2 < nkt) gload(kt + 2, 0);
+      compute(0);
+      if (kt + 1 < nkt) lstore(1, 1);
+      __syncthreads();
+      if (kt + 1 >= nkt) break;
+      if (kt + 3 < nkt) gload(kt + 3, 1);
+      compute(1);
+      if (kt + 2 < nkt) lstore(0, 0);
+      __syncthreads();
+    }
+
+    // epilogue: lane holds rows wr + 4q + v (v < 4) of token column li
+    const int j = li;
+    if constexpr (GU) {
+      if (wave >= 2) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_up[wr - 32 + 4 * q + v][j] = acc[v];
+      }
+      __syncthreads();
+      if (wave < 2 && j < nt) {
+        const int pos = t0 + j;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int rr = wr + 4 * q + v, f = r0 + rr;
+          if (f < a.M) {
+            float av = acc[v], uv = s_up[rr][j];
+            if constexpr (Fmt<FMT>::ROW) {
+              av *= a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
+              uv *= a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
+            }
+            const float hv = act_f(a.act, av) * uv;
+            const int64_t o = (int64_t)pos * a.M + f;
+            a.out[o] = hv;
+            const __bf16 hh = (__bf16)hv;
+            a.out_hi[o] = __builtin_bit_cast(u16, hh);
+            a.out_lo[o] = __builtin_bit_cast(u16, (__bf16)(hv - (float)hh));
+          }
+        }
+      }
+    } else {
+      if (j < nt) {
+        const int pos = t0 + j;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = r0 + wr + 4 * q + v;
+          if (i < a.M) {
+            float ov = acc[v];
+            if constexpr (Fmt<FMT>::ROW) ov *= a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
+            a.out[(int64_t)pos * a.M + i] = ov;
+          }
+        }
+      }
+    }
+  }
+}
+
+bool mfma_supported(int K) { return K % kKT == 0; }
+
+hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
+                           const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d, int max_active,
+                           const u16* a_hi, const u16* a_lo, bool act_by_token, float* out, u16* out_hi,
+                           u16* out_lo, hipStream_t st) {
+  MfmaArgs a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, a_hi, a_lo, act_by_token ? 1 : 0, out, out_hi, out_lo};
+  const int rows_per_block = gateup ? 32 : kRows;
+  // token tiles: an expert holds at most T tokens (one per token)
+  const int tiles = (d.T + kTok - 1) / kTok;
+  const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.n_active ? max_active : 1, tiles);
+#define MD_MF(F_) \
+  if (fmt == F_) { \
+    if (gateup) hipLaunchKernelGGL((k_moe_mfma<F_, 1>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((k_moe_mfma<F_, 0>), grid, dim3(256), 0, st, a); \
+    return hipGetLastError(); }
+  MD_MF(Q8_0) MD_MF(Q4_0) MD_MF(I8_ROW) MD_MF(I4_ROW)
+#undef MD_MF
+  return hipErrorInvalidValue;
+}
+
+}  // namespace md

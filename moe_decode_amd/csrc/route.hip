@@ -1,8 +1,8 @@
 // route.hip -- top-k selection with softmax gates for many tokens, the expert
 // dispatch, and the weight layout pass (gfx950, wave64).
 //
-// The logits come from k_router_rows (fp64 accumulation rounded once to
-// fp32).  Selection uses 64-bit keys: the order-preserving image of the fp32 logit in
+// The logits are formed from k_router_part's fp64 partials (added in a fixed
+// order, plus the bias, rounded once to fp32).  Selection uses 64-bit keys: the order-preserving image of the fp32 logit in
 // the high word (with -0 folded onto +0) and the complemented expert index in
 // the low word, so one integer maximum picks the largest logit and, among
 // exact ties, the lower expert index -- the tie rule of the Camelid README,
@@ -34,9 +34,10 @@ MD_DEV uint64_t wave_max_u64(uint64_t v) {
 // expert (pairs of one expert are ordered by token, and a token selects an
 // expert at most once), exclusive scans give the offsets and the list of
 // active experts in ascending order.
-__global__ __launch_bounds__(1024) void k_route_finalize(const float* __restrict__ logits, int T, int E, int k,
-                                                         int* __restrict__ idx, float* __restrict__ gates, DispOut d,
-                                                         int do_disp) {
+__global__ __launch_bounds__(1024) void k_route_finalize(const double* __restrict__ part, int S,
+                                                         const float* __restrict__ bias, int T, int E, int k,
+                                                         float* __restrict__ logits, int* __restrict__ idx,
+                                                         float* __restrict__ gates, DispOut d, int do_disp) {
   __shared__ uint32_t mask[256][4];
   __shared__ int sel[128 * 8];
   __shared__ int cnt[256], poff[256], apos[256];
@@ -53,7 +54,11 @@ __global__ __launch_bounds__(1024) void k_route_finalize(const float* __restrict
       key[i] = 0;
       lv[i] = 0.f;
       if (e < E) {
-        const float l = logits[(int64_t)t * E + e];
+        double a = 0.0;
+        for (int s = 0; s < S; ++s) a += part[((int64_t)t * E + e) * S + s];
+        if (bias) a += (double)bias[e];
+        const float l = (float)a;
+        if (logits) logits[(int64_t)t * E + e] = l;
         lv[i] = l;
         key[i] = ((uint64_t)order_key(l) << 32) | (uint32_t)(~(uint32_t)e);
       }
@@ -146,10 +151,11 @@ __global__ __launch_bounds__(1024) void k_route_finalize(const float* __restrict
   }
 }
 
-hipError_t launch_route_finalize(const float* logits, int T, int E, int k, int* idx, float* gates, const DispOut* d,
-                                 hipStream_t st) {
+hipError_t launch_route_finalize(const double* part, int S, const float* bias, int T, int E, int k, float* logits,
+                                 int* idx, float* gates, const DispOut* d, hipStream_t st) {
   DispOut dd = d ? *d : DispOut{nullptr, nullptr, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(k_route_finalize, dim3(1), dim3(1024), 0, st, logits, T, E, k, idx, gates, dd, d ? 1 : 0);
+  hipLaunchKernelGGL(k_route_finalize, dim3(1), dim3(1024), 0, st, part, S, bias, T, E, k, logits, idx, gates, dd,
+                     d ? 1 : 0);
   return hipGetLastError();
 }
 

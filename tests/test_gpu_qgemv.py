@@ -135,3 +135,18 @@ def test_deterministic_repeat():
     b = md.qgemv(dense_matrix("c1", "k"), x)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T", [9, 32, 128])
+def test_dense_swiglu_ffn_chunk(orc_mt, T):
+    """A chunk of tokens through the dense FFN (grouped GEMM on the matrix cores)."""
+    import moe_decode_amd as md
+    import torch
+    sp = W.spec("c1")
+    g, u, d = (W.dense_matrix(sp, n) for n in ("gate", "up", "down"))
+    x = np.concatenate([W.dense_x(sp, 2048, 1, salt=s) for s in range(T)])
+    y_ref, S = orc_mt.ffn(g, u, d, "silu", x)
+    ffn = md.FFN("silu", dense_matrix("c1", "gate"), dense_matrix("c1", "up"), dense_matrix("c1", "down"))
+    y = md.ffn_forward(ffn, torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert_within(y.cpu().numpy(), y_ref, S, f"c1 SwiGLU FFN T={T}")
