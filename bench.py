@@ -162,6 +162,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4_i4")
+    ap.add_argument("--tokens", type=int, default=1, help="tokens per step (1 = decode; up to 128 = a prefill chunk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--modes", action="store_true", help="also time the other layer shapes")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -191,15 +192,18 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {sp.key} resident in HBM ({time.time() - t:.1f} s to generate and upload)")
 
-    r = run_mode(layer, sp, 1, args.steps, args.warmup)
-    log(f"[bench] decode T=1: {r['ms_per_step'] * 1e3:.1f} us/step, gate/up {r['stage_ms_avg'] * 1e3:.1f} us")
+    T = args.tokens
+    r = run_mode(layer, sp, T, args.steps, args.warmup)
+    log(f"[bench] {sp.key} T={T}: {r['ms_per_step'] * 1e3:.1f} us/step, gate/up {r['stage_ms_avg'] * 1e3:.1f} us")
 
     modes = {}
     if args.modes:
-        for T in (4, 128):
-            m = run_mode(layer, sp, T, max(10, args.steps // (4 if T > 1 else 1)), 5)
-            modes[f"{sp.key}_T{T}"] = m
-            log(f"[bench] {sp.key} T={T}: {m['ms_per_step'] * 1e3:.1f} us/step")
+        for Tm in (1, 4, 128):
+            if Tm == T:
+                continue
+            m = run_mode(layer, sp, Tm, max(10, args.steps // (4 if Tm > 1 else 1)), 5)
+            modes[f"{sp.key}_T{Tm}"] = m
+            log(f"[bench] {sp.key} T={Tm}: {m['ms_per_step'] * 1e3:.1f} us/step")
         del layer
         torch.cuda.empty_cache()
         for key, Ts in (("c4_i8", (1, 4, 128)), ("c3", (1, 128))):
@@ -213,7 +217,7 @@ def main():
             torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and T == 1:
         cpu = cpu_baseline(sp)
         log(f"[bench] oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
 
@@ -232,9 +236,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{sp.key}: MoE layer decode, 1 token/step, {sp.E} experts top-{sp.k}, hidden {sp.H}, "
-                        f"expert FFN {sp.F}, {sp.fmt} weights (GeGLU), whole expert set resident in HBM",
-            "tokens_per_step": 1,
+            "workload": f"{sp.key}: MoE layer {'decode' if T == 1 else 'forward'}, {T} token(s)/step, {sp.E} experts "
+                        f"top-{sp.k}, hidden {sp.H}, expert FFN {sp.F}, {sp.fmt} weights (GeGLU), whole expert set "
+                        f"resident in HBM",
+            "tokens_per_step": T,
             "weight_bytes_per_step": r["weight_bytes_per_step"],
             "weight_GBps": r["weight_GBps"],
             "weight_frac_of_8TBps": r["weight_GBps"] / HBM_PEAK_GBS,

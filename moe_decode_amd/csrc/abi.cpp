@@ -92,7 +92,9 @@ int max_active(int T, int E, int k) { return T * k < E ? T * k : E; }
 // ---- MoE workspace layout ------------------------------------------------
 struct MoeWs {
   size_t part, logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
-  size_t x_hi, x_lo, h_hi, h_lo, hs_hi, hs_lo;  // bf16 pairs of the prefill path
+  size_t x_hi, x_lo, h_hi, h_lo, hs_hi, hs_lo;  // bf16 pairs of the prefill path (block formats)
+  size_t x_dig, x_exp, h_dig, h_exp, hs_dig, hs_exp;  // int8 digit planes (per-row formats)
+  size_t xs_dig, xs_exp;  // x digits in the shared expert's order
 };
 
 // Few tokens on shapes the one-token kernels cover: independent (token, slot)
@@ -125,11 +127,20 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
     w.o = take(sizeof(float) * (size_t)T * k * H);
     w.x_hi = take(2 * (size_t)T * H);
     w.x_lo = take(2 * (size_t)T * H);
+    w.x_dig = take(4 * (size_t)T * H);
+    w.x_exp = take(sizeof(int) * (size_t)T);
     w.h_hi = take(2 * (size_t)T * k * F);
     w.h_lo = take(2 * (size_t)T * k * F);
+    w.h_dig = take(4 * (size_t)T * k * F);
+    w.h_exp = take(sizeof(int) * (size_t)T * k);
     if (L->has_shared) {
-      w.hs_hi = take(2 * (size_t)T * L->shared.gate.rows);
-      w.hs_lo = take(2 * (size_t)T * L->shared.gate.rows);
+      const size_t Fs = L->shared.gate.rows;
+      w.hs_hi = take(2 * (size_t)T * Fs);
+      w.hs_lo = take(2 * (size_t)T * Fs);
+      w.hs_dig = take(4 * (size_t)T * Fs);
+      w.hs_exp = take(sizeof(int) * (size_t)T);
+      w.xs_dig = take(4 * (size_t)T * H);
+      w.xs_exp = take(sizeof(int) * (size_t)T);
     }
   }
   w.total = off;
@@ -175,10 +186,33 @@ typedef unsigned short u16;
 
 // dense FFN (or shared expert) for a chunk of tokens on the matrix cores:
 // x_hi/x_lo hold x as bf16 pairs; h and its pair buffers are scratch
-md_status run_ffn_mfma(const md_ffn* f, const u16* x_hi, const u16* x_lo, int T, float* h, u16* h_hi, u16* h_lo,
-                       float* y, hipStream_t st) {
+// Activation buffers of the chunk path: bf16 pairs feed the block formats,
+// int8 digit planes the per-row formats.
+struct ChunkAct {
+  const u16* hi;
+  const u16* lo;
+  const int8_t* dig;
+  const int* expo;
+};
+
+md_status run_ffn_mfma(const md_ffn* f, const ChunkAct& xa, int T, float* h, u16* h_hi, u16* h_lo, int8_t* h_dig,
+                       int* h_exp, float* y, hipStream_t st) {
   const int H = f->gate.cols, F = f->gate.rows, fmt = f->gate.type;
   md::Disp d{nullptr, nullptr, nullptr, nullptr, 1, T};
+  if (row_type(fmt)) {
+    hipError_t e = md::launch_moe_mfma_i8(fmt, true, static_cast<const uint8_t*>(f->gate.q),
+                                          static_cast<const uint8_t*>(f->up.q), f->gate.row_scale, f->up.row_scale, 0,
+                                          F, H, f->act, d, 1, xa.dig, xa.expo, true, h, st);
+    if (e != hipSuccess) return hip_fail(e, "ffn gate/up launch");
+    e = md::launch_limbs(h, T, F, fmt == MD_I4_ROW, h_dig, h_exp, st);
+    if (e != hipSuccess) return hip_fail(e, "digit launch");
+    e = md::launch_moe_mfma_i8(fmt, false, static_cast<const uint8_t*>(f->down.q), nullptr, f->down.row_scale, nullptr,
+                               0, H, F, f->act, d, 1, h_dig, h_exp, false, y, st);
+    if (e != hipSuccess) return hip_fail(e, "ffn down launch");
+    return MD_OK;
+  }
+  const u16* x_hi = xa.hi;
+  const u16* x_lo = xa.lo;
   hipError_t e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(f->gate.q),
                                      static_cast<const uint8_t*>(f->up.q), f->gate.row_scale, f->up.row_scale, 0, F,
                                      H, f->act, d, 1, x_hi, x_lo, true, h, h_hi, h_lo, st);
@@ -314,7 +348,9 @@ md_status md_moe_route_topk(const float* x, int32_t T, int32_t H, const float* W
 static size_t ffn_ws_bytes(const md_ffn* f, int T) {
   const size_t H = f->gate.cols, F = f->gate.rows;
   size_t b = align256(sizeof(float) * T * F);
-  if (T > kMaxPairT) b += 2 * align256(2 * T * H) + 2 * align256(2 * T * F);
+  if (T > kMaxPairT)
+    b += 2 * align256(2 * T * H) + 2 * align256(2 * T * F) + align256(4 * T * H) + align256(4 * T * F) +
+         2 * align256(sizeof(int) * T);
   return b;
 }
 
@@ -348,10 +384,15 @@ md_status md_ffn_forward(const md_ffn* f, const float* x, int32_t T, float* y, v
   u16* x_hi = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * H);
   u16* x_lo = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * H);
   u16* h_hi = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * F);
-  u16* h_lo = reinterpret_cast<u16*>(ws + off);
-  hipError_t e = md::launch_split_bf16(x, (int64_t)T * H, x_hi, x_lo, stream);
-  if (e != hipSuccess) return hip_fail(e, "split launch");
-  s = run_ffn_mfma(f, x_hi, x_lo, T, h, h_hi, h_lo, y, stream);
+  u16* h_lo = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * F);
+  int8_t* x_dig = reinterpret_cast<int8_t*>(ws + off); off += align256(4 * T * H);
+  int8_t* h_dig = reinterpret_cast<int8_t*>(ws + off); off += align256(4 * T * F);
+  int* x_exp = reinterpret_cast<int*>(ws + off); off += align256(sizeof(int) * T);
+  int* h_exp = reinterpret_cast<int*>(ws + off);
+  hipError_t e = row_type(f->gate.type) ? md::launch_limbs(x, T, H, f->gate.type == MD_I4_ROW, x_dig, x_exp, stream)
+                                        : md::launch_split_bf16(x, (int64_t)T * H, x_hi, x_lo, stream);
+  if (e != hipSuccess) return hip_fail(e, "activation split launch");
+  s = run_ffn_mfma(f, ChunkAct{x_hi, x_lo, x_dig, x_exp}, T, h, h_hi, h_lo, h_dig, h_exp, y, stream);
   return s == MD_OK ? ok() : s;
 }
 
@@ -396,17 +437,43 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   const bool t1 = use_pairs(L, T);
 
   // shared expert: independent of the routing, enqueued first
-  u16* x_hi = t1 ? nullptr : static_cast<u16*>(P(w.x_hi));
-  u16* x_lo = t1 ? nullptr : static_cast<u16*>(P(w.x_lo));
+  ChunkAct xa{nullptr, nullptr, nullptr, nullptr};
   if (!mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
   if (!t1) {
-    e = md::launch_split_bf16(x, (int64_t)T * H, x_hi, x_lo, stream);
-    if (e != hipSuccess) return hip_fail(e, "split launch");
+    // the activation forms the chunk path's kernels need
+    const bool need_pair = !row_type(fmt) || (L->has_shared && !row_type(L->shared.gate.type));
+    const bool need_dig = row_type(fmt);
+    if (need_pair) {
+      e = md::launch_split_bf16(x, (int64_t)T * H, static_cast<u16*>(P(w.x_hi)), static_cast<u16*>(P(w.x_lo)), stream);
+      if (e != hipSuccess) return hip_fail(e, "split launch");
+      xa.hi = static_cast<u16*>(P(w.x_hi));
+      xa.lo = static_cast<u16*>(P(w.x_lo));
+    }
+    if (need_dig) {
+      e = md::launch_limbs(x, T, H, fmt == MD_I4_ROW, static_cast<int8_t*>(P(w.x_dig)), static_cast<int*>(P(w.x_exp)),
+                           stream);
+      if (e != hipSuccess) return hip_fail(e, "digit launch");
+      xa.dig = static_cast<int8_t*>(P(w.x_dig));
+      xa.expo = static_cast<int*>(P(w.x_exp));
+    }
   }
   if (L->has_shared) {
-    if (t1) s = run_ffn(&L->shared, x, T, static_cast<float*>(P(w.h_s)), y_s, stream);
-    else s = run_ffn_mfma(&L->shared, x_hi, x_lo, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
-                          static_cast<u16*>(P(w.hs_lo)), y_s, stream);
+    if (t1) {
+      s = run_ffn(&L->shared, x, T, static_cast<float*>(P(w.h_s)), y_s, stream);
+    } else {
+      ChunkAct xs = xa;
+      const int sfmt = L->shared.gate.type;
+      if (row_type(sfmt)) {  // x digits in the shared expert's own column order
+        e = md::launch_limbs(x, T, H, sfmt == MD_I4_ROW, static_cast<int8_t*>(P(w.xs_dig)),
+                             static_cast<int*>(P(w.xs_exp)), stream);
+        if (e != hipSuccess) return hip_fail(e, "digit launch");
+        xs.dig = static_cast<int8_t*>(P(w.xs_dig));
+        xs.expo = static_cast<int*>(P(w.xs_exp));
+      }
+      s = run_ffn_mfma(&L->shared, xs, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
+                       static_cast<u16*>(P(w.hs_lo)), static_cast<int8_t*>(P(w.hs_dig)), static_cast<int*>(P(w.hs_exp)),
+                       y_s, stream);
+    }
     if (s != MD_OK) return s;
   }
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
@@ -445,16 +512,31 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T};
   const int A = max_active(T, E, k);
   float* o = static_cast<float*>(P(w.o));
-  u16* h_hi = static_cast<u16*>(P(w.h_hi));
-  u16* h_lo = static_cast<u16*>(P(w.h_lo));
-  e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
-                          L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, A, x_hi, x_lo, true, h, h_hi, h_lo,
-                          stream);
-  if (e != hipSuccess) return hip_fail(e, "gate/up launch");
-  if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
-  e = md::launch_moe_mfma(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
-                          dn_bytes, H, F, L->act, d, A, h_hi, h_lo, false, o, nullptr, nullptr, stream);
-  if (e != hipSuccess) return hip_fail(e, "down launch");
+  if (row_type(fmt)) {
+    int8_t* h_dig = static_cast<int8_t*>(P(w.h_dig));
+    int* h_exp = static_cast<int*>(P(w.h_exp));
+    e = md::launch_moe_mfma_i8(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                               L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, A, xa.dig, xa.expo, true, h,
+                               stream);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
+    e = md::launch_limbs(h, T * k, F, fmt == MD_I4_ROW, h_dig, h_exp, stream);
+    if (e != hipSuccess) return hip_fail(e, "digit launch");
+    e = md::launch_moe_mfma_i8(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
+                               dn_bytes, H, F, L->act, d, A, h_dig, h_exp, false, o, stream);
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+  } else {
+    u16* h_hi = static_cast<u16*>(P(w.h_hi));
+    u16* h_lo = static_cast<u16*>(P(w.h_lo));
+    e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                            L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, A, xa.hi, xa.lo, true, h, h_hi,
+                            h_lo, stream);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
+    e = md::launch_moe_mfma(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
+                            dn_bytes, H, F, L->act, d, A, h_hi, h_lo, false, o, nullptr, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+  }
   if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0)) return hip_fail(e, "event record");
   e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");

@@ -70,6 +70,12 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
                            const unsigned short* a_hi, const unsigned short* a_lo, bool act_by_token, float* out,
                            unsigned short* out_hi, unsigned short* out_lo, hipStream_t st);
 
+hipError_t launch_limbs(const float* a, int R, int K, bool perm4, int8_t* digits, int* expo, hipStream_t st);
+hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
+                              const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d,
+                              int max_active, const int8_t* digits, const int* expo, bool act_by_token, float* out,
+                              hipStream_t st);
+
 GemvCfg gateup_config(int fmt, int F, int H, int max_active, int T);
 hipError_t launch_gateup(int fmt, const GemvCfg& c, const uint8_t* gq, const uint8_t* uq, const float* gs,
                          const float* us, int64_t mat_bytes, int F, int H, int act, const Disp& d,

@@ -332,4 +332,242 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
   return hipErrorInvalidValue;
 }
 
+// ================================================================ int8 path
+//
+// For the per-row-scale formats the codes feed v_mfma_i32_16x16x64_i8 as they
+// are (int8 codes directly; 4-bit codes as the exact bytes 16 * value).  Each
+// activation row a (a token's x or a position's h) is written as a 30-bit
+// fixed-point integer X = rint(a * 2^(30 - E)), E the binary exponent that
+// bounds max|a| (|X| < 2^30), split into four balanced int8 digits,
+// X = d0 + 256 d1 + 65536 d2 + 2^24 d3 (d_i in [-128, 127]).  One MFMA per
+// digit accumulates exact int32 sums; the epilogue forms
+// (2^24 acc3 + 2^16 acc2 + 2^8 acc1 + acc0) * 2^(E - 30) in fp32.  The digits
+// resolve |a| to 2^-31 of the row maximum, so the only rounding left is the
+// fp32 combine.
+
+constexpr int kLST = kKT + 16;    // LDS stride of a digit plane row (bank spread)
+
+// Digit planes [R][4][K] (int8) and exponents [R].  Within every 8 columns
+// the 4-bit layout stores the even columns first (the order in which a
+// packed-int4 word's low and high nibbles are laid out as bytes).
+__global__ __launch_bounds__(256) void k_limbs(const float* __restrict__ a, int K, int perm4,
+                                               int8_t* __restrict__ digits, int* __restrict__ expo) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* row = a + (int64_t)r * K;
+  float m = 0.f;
+  for (int c = tid; c < K; c += 256) m = fmaxf(m, fabsf(row[c]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int E = 0;
+  if (m > 0.f) frexpf(m, &E);  // m = f * 2^E, f in [0.5, 1): |a| < 2^E
+  if (tid == 0) expo[r] = E;
+  int8_t* out = digits + (int64_t)r * 4 * K;
+  for (int c = tid; c < K; c += 256) {
+    const int X = (int)rintf(ldexpf(row[c], 30 - E));
+    const unsigned Y = (unsigned)X + 0x00808080u;
+    int p = c;
+    if (perm4) {
+      const int w = c & 7;
+      p = (c & ~7) + ((w & 1) ? 4 + (w >> 1) : (w >> 1));
+    }
+    out[p] = (int8_t)((Y & 0xFFu) ^ 0x80u);
+    out[K + p] = (int8_t)(((Y >> 8) & 0xFFu) ^ 0x80u);
+    out[2 * K + p] = (int8_t)(((Y >> 16) & 0xFFu) ^ 0x80u);
+    out[3 * K + p] = (int8_t)(Y >> 24);
+  }
+}
+
+hipError_t launch_limbs(const float* a, int R, int K, bool perm4, int8_t* digits, int* expo, hipStream_t st) {
+  hipLaunchKernelGGL(k_limbs, dim3(R), dim3(256), 0, st, a, K, perm4 ? 1 : 0, digits, expo);
+  return hipGetLastError();
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+struct MfmaI8Args {
+  const uint8_t* wq;
+  const uint8_t* wq2;
+  const float* ws;
+  const float* ws2;
+  int64_t mat_bytes;
+  int M, K, act;
+  Disp d;
+  const int8_t* digits;  // activation digit planes [rows][4][K]
+  const int* expo;       // [rows]
+  int act_by_token;
+  float* out;            // h [pos][F] or o [pos][H]
+};
+
+template <int FMT>
+MD_DEV i32x4 decode_a8(const uint8_t* p) {
+  if constexpr (FMT == I8_ROW) {
+    return *reinterpret_cast<const i32x4*>(p);
+  } else {  // I4_ROW: 8 bytes = 16 weights; bytes 16*v, even weights first in every 8
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    i32x4 r;
+    r[0] = (int)opaque((u.x << 4) & 0xF0F0F0F0u);
+    r[1] = (int)opaque(u.x & 0xF0F0F0F0u);
+    r[2] = (int)opaque((u.y << 4) & 0xF0F0F0F0u);
+    r[3] = (int)opaque(u.y & 0xF0F0F0F0u);
+    return r;
+  }
+}
+
+template <int FMT, int GU>
+__global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
+  using TL = Tile<FMT>;
+  constexpr int KB = TL::B8 ? 16 : 8;  // weight bytes per lane per 64-wide step
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kRows * TL::WSTR];
+  __shared__ __attribute__((aligned(16))) int8_t s_d[2][4 * kTok * kLST];
+  __shared__ float s_up[32][kTok];
+  __shared__ int s_e[kTok];
+
+  struct { int e, p0, p1; } er;
+  if (a.d.n_active == nullptr) {
+    if (blockIdx.y != 0) return;
+    er.e = 0; er.p0 = 0; er.p1 = a.d.T;
+  } else {
+    if ((int)blockIdx.y >= *a.d.n_active) return;
+    er.e = a.d.active_e[blockIdx.y];
+    er.p0 = a.d.active_off[blockIdx.y];
+    er.p1 = a.d.active_off[blockIdx.y + 1];
+  }
+  const int t0 = er.p0 + (int)blockIdx.z * kTok;
+  if (t0 >= er.p1) return;
+  const int nt = min(kTok, er.p1 - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, li = lane & 15;
+  const int64_t rb = row_bytes(FMT, a.K);
+  const int nkt = a.K / kKT;
+  const int r0 = GU ? blockIdx.x * 32 : blockIdx.x * kRows;
+  auto row_ptr = [&](int r) -> const uint8_t* {
+    if (GU) {
+      const int f = min(r0 + (r & 31), a.M - 1);
+      return (r < 32 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes + (int64_t)f * rb;
+    }
+    return a.wq + (int64_t)er.e * a.mat_bytes + (int64_t)min(r0 + r, a.M - 1) * rb;
+  };
+  auto act_row = [&](int jj) {
+    const int pos = t0 + jj;
+    return a.act_by_token ? (a.d.n_active == nullptr ? pos : a.d.pairs[pos] / a.d.k) : pos;
+  };
+  // staging: thread (jj, pp) moves bytes [16 pp, 16 pp + 16) of each digit plane of token slot jj
+  const int jj = tid >> 4, pp = tid & 15;
+  const int8_t* dsrc = jj < nt ? a.digits + (int64_t)act_row(jj) * 4 * a.K : nullptr;
+  if (tid < kTok) s_e[tid] = tid < nt ? a.expo[act_row(tid)] : 0;
+
+  u32x4 rw[2][TL::WPT];
+  uint4 rd[2][4];
+  auto gload = [&](int kt, int set) {
+#pragma unroll
+    for (int i = 0; i < TL::WPT; ++i) {
+      const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
+      rw[set][i] = ld_stream(row_ptr(r) + (int64_t)kt * TL::WB + 16 * piece);
+    }
+#pragma unroll
+    for (int l = 0; l < 4; ++l)
+      rd[set][l] = dsrc ? *reinterpret_cast<const uint4*>(dsrc + (int64_t)l * a.K + kt * kKT + 16 * pp)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto lstore = [&](int buf, int set) {
+#pragma unroll
+    for (int i = 0; i < TL::WPT; ++i) {
+      const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
+      *reinterpret_cast<u32x4*>(&s_w[buf][r * TL::WSTR + 16 * piece]) = rw[set][i];
+    }
+#pragma unroll
+    for (int l = 0; l < 4; ++l)
+      *reinterpret_cast<uint4*>(&s_d[buf][(l * kTok + jj) * kLST + 16 * pp]) = rd[set][l];
+  };
+  i32x4 acc[4];
+#pragma unroll
+  for (int l = 0; l < 4; ++l) acc[l] = i32x4{0, 0, 0, 0};
+  const int wr = wave * 16;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < kKT / 64; ++s) {
+      const i32x4 av = decode_a8<FMT>(&s_w[buf][(wr + li) * TL::WSTR + KB * (4 * s + q)]);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) {
+        const i32x4 bv = *reinterpret_cast<const i32x4*>(&s_d[buf][(l * kTok + li) * kLST + 64 * s + 16 * q]);
+        acc[l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[l], 0, 0, 0);
+      }
+    }
+  };
+  gload(0, 0);
+  if (nkt > 1) gload(1, 1);
+  lstore(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    if (kt + 2 < nkt) gload(kt + 2, 0);
+    compute(0);
+    if (kt + 1 < nkt) lstore(1, 1);
+    __syncthreads();
+    if (kt + 1 >= nkt) break;
+    if (kt + 3 < nkt) gload(kt + 3, 1);
+    compute(1);
+    if (kt + 2 < nkt) lstore(0, 0);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows wr + 4q + v of token column li
+  const int j = li;
+  const float ex = ldexpf(1.0f, s_e[j] - 30);
+  float val[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    val[v] = (fmaf((float)acc[3][v], 16777216.0f, (float)acc[2][v] * 65536.0f) +
+              fmaf((float)acc[1][v], 256.0f, (float)acc[0][v])) * ex;
+  if constexpr (GU) {
+    if (wave >= 2) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_up[wr - 32 + 4 * q + v][j] = val[v];
+    }
+    __syncthreads();
+    if (wave < 2 && j < nt) {
+      const int pos = t0 + j;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = wr + 4 * q + v, f = r0 + rr;
+        if (f < a.M) {
+          const float av = val[v] * a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
+          const float uv = s_up[rr][j] * a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
+          a.out[(int64_t)pos * a.M + f] = act_f(a.act, av) * uv;
+        }
+      }
+    }
+  } else {
+    if (j < nt) {
+      const int pos = t0 + j;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = r0 + wr + 4 * q + v;
+        if (i < a.M) a.out[(int64_t)pos * a.M + i] = val[v] * a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
+      }
+    }
+  }
+}
+
+hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
+                              const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d,
+                              int max_active, const int8_t* digits, const int* expo, bool act_by_token, float* out,
+                              hipStream_t st) {
+  MfmaI8Args a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, digits, expo, act_by_token ? 1 : 0, out};
+  const int rows_per_block = gateup ? 32 : kRows;
+  const int tiles = (d.T + kTok - 1) / kTok;
+  const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.n_active ? max_active : 1, tiles);
+#define MD_MF8(F_) \
+  if (fmt == F_) { \
+    if (gateup) hipLaunchKernelGGL((k_moe_mfma_i8<F_, 1>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((k_moe_mfma_i8<F_, 0>), grid, dim3(256), 0, st, a); \
+    return hipGetLastError(); }
+  MD_MF8(I8_ROW) MD_MF8(I4_ROW)
+#undef MD_MF8
+  return hipErrorInvalidValue;
+}
+
 }  // namespace md
