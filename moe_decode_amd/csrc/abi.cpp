@@ -9,6 +9,7 @@
 
 #include "moe_decode.h"
 #include "common.hpp"
+#include "digits.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -89,12 +90,29 @@ md_status check_ffn(const md_ffn* f, int32_t H) {
 
 int max_active(int T, int E, int k) { return T * k < E ? T * k : E; }
 
+// Digit planes of an R x K activation matrix (one-token kernels): planes,
+// then scales.
+struct DigBuf {
+  void* planes;
+  float* scales;
+};
+size_t dig_buf_bytes(int fmt, int R, int K) {
+  return align256((size_t)R * md::dig_bytes(fmt, K)) + align256(sizeof(float) * (size_t)R * (K / md::dig_nv(fmt)));
+}
+DigBuf dig_buf_at(char* base, int fmt, int R, int K) {
+  return DigBuf{base, reinterpret_cast<float*>(base + align256((size_t)R * md::dig_bytes(fmt, K)))};
+}
+md::DigJob dig_job(const float* x, int R, int K, int fmt, const DigBuf& b) {
+  return md::DigJob{x, R, K, fmt, static_cast<md::u32x4*>(b.planes), b.scales};
+}
+
 // ---- MoE workspace layout ------------------------------------------------
 struct MoeWs {
   size_t part, logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
   size_t x_hi, x_lo, h_hi, h_lo, hs_hi, hs_lo;  // bf16 pairs of the prefill path (block formats)
   size_t x_dig, x_exp, h_dig, h_exp, hs_dig, hs_exp;  // int8 digit planes (per-row formats)
   size_t xs_dig, xs_exp;  // x digits in the shared expert's order
+  size_t xd, sxd, hd, shd;  // digit planes of x and h for the one-token kernels (routed, shared formats)
 };
 
 // Few tokens on shapes the one-token kernels cover: independent (token, slot)
@@ -109,7 +127,7 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
   const int E = L->E, k = L->k, H = L->H, F = L->F;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  w.part = take(sizeof(double) * (size_t)T * E * md::router_splits(H, E));
+  w.part = take(sizeof(double) * (size_t)T * E * md::router_plan(T, H, E).S);
   w.logits = take(sizeof(float) * T * E);
   w.idx = take(sizeof(int) * T * k);
   w.gates = take(sizeof(float) * T * k);
@@ -123,7 +141,14 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
     w.h_s = take(sizeof(float) * (size_t)T * L->shared.gate.rows);
     w.y_s = take(sizeof(float) * (size_t)T * H);
   }
-  if (!use_pairs(L, T)) {
+  if (use_pairs(L, T)) {
+    w.xd = take(dig_buf_bytes(L->type, T, H));
+    w.hd = take(dig_buf_bytes(L->type, T * k, F));
+    if (L->has_shared) {
+      w.sxd = take(dig_buf_bytes(L->shared.gate.type, T, H));
+      w.shd = take(dig_buf_bytes(L->shared.gate.type, T, L->shared.gate.rows));
+    }
+  } else {
     w.o = take(sizeof(float) * (size_t)T * k * H);
     w.x_hi = take(2 * (size_t)T * H);
     w.x_lo = take(2 * (size_t)T * H);
@@ -223,16 +248,26 @@ md_status run_ffn_mfma(const md_ffn* f, const ChunkAct& xa, int T, float* h, u16
   return MD_OK;
 }
 
-// dense FFN (or shared expert) through the MoE kernels with the identity dispatch
-md_status run_ffn(const md_ffn* f, const float* x, int T, float* h, float* y, hipStream_t st) {
+// dense FFN (or shared expert) through the MoE kernels with the identity
+// dispatch.  One-token kernels: x digit planes come ready (xd_ready) or are
+// made into xd; hd receives those of h.  Otherwise h (fp32) is the scratch.
+md_status run_ffn(const md_ffn* f, const float* x, int T, const DigBuf* xd_ready, const DigBuf& xd, const DigBuf& hd,
+                  float* h, float* y, hipStream_t st) {
   const int H = f->gate.cols, F = f->gate.rows, fmt = f->gate.type;
   if (T <= kMaxPairT && md::t1_supported(fmt, H, F)) {
-    hipError_t e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(f->gate.q),
-                                        static_cast<const uint8_t*>(f->up.q), f->gate.row_scale, f->up.row_scale, 0,
-                                        F, H, f->act, 1, 1, T, nullptr, 1, nullptr, x, h, nullptr, nullptr, st);
+    hipError_t e = hipSuccess;
+    const DigBuf* xa = xd_ready;
+    if (!xa) {
+      e = md::launch_digits(dig_job(x, T, H, fmt, xd), st);
+      if (e != hipSuccess) return hip_fail(e, "digit launch");
+      xa = &xd;
+    }
+    e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(f->gate.q), static_cast<const uint8_t*>(f->up.q),
+                             f->gate.row_scale, f->up.row_scale, 0, F, H, f->act, 1, 1, T, nullptr, 1, nullptr,
+                             xa->planes, xa->scales, hd.planes, hd.scales, nullptr, nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "ffn gate/up launch");
     e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(f->down.q), f->down.row_scale, 0, H, F, 1, T, nullptr,
-                           nullptr, h, nullptr, y, st);
+                           nullptr, hd.planes, hd.scales, nullptr, y, st);
     if (e != hipSuccess) return hip_fail(e, "ffn down launch");
     return MD_OK;
   }
@@ -322,7 +357,7 @@ md_status md_route_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, si
   if (T > kMaxT || E > kMaxE || k > kMaxK) return fail(MD_ERR_UNSUPPORTED, "T <= %d, E <= %d, k <= %d", kMaxT, kMaxE, kMaxK);
   md_status s = check_width("H", H);
   if (s != MD_OK) return s;
-  *bytes = align256(sizeof(double) * (size_t)T * E * md::router_splits(H, E)) + align256(sizeof(float) * (size_t)T * E);
+  *bytes = align256(sizeof(double) * (size_t)T * E * md::router_plan(T, H, E).S) + align256(sizeof(float) * (size_t)T * E);
   return ok();
 }
 
@@ -337,17 +372,18 @@ md_status md_moe_route_topk(const float* x, int32_t T, int32_t H, const float* W
       (logits && !aligned16(logits)))
     return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
-  const int S = md::router_splits(H, E);
+  const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(workspace);
-  hipError_t e = md::launch_router_part(x, T, H, W_r, E, S, part, stream);
+  hipError_t e = md::launch_router(x, T, H, W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
-  e = md::launch_route_finalize(part, S, bias, T, E, k, logits, idx, gates, nullptr, stream);
-  return e == hipSuccess ? ok() : hip_fail(e, "route finalize launch");
+  e = md::launch_select(part, rp, bias, T, E, k, logits, idx, gates, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "select launch");
 }
 
 static size_t ffn_ws_bytes(const md_ffn* f, int T) {
   const size_t H = f->gate.cols, F = f->gate.rows;
   size_t b = align256(sizeof(float) * T * F);
+  if (T <= kMaxPairT) b += dig_buf_bytes(f->gate.type, T, H) + dig_buf_bytes(f->gate.type, T, F);
   if (T > kMaxPairT)
     b += 2 * align256(2 * T * H) + 2 * align256(2 * T * F) + align256(4 * T * H) + align256(4 * T * F) +
          2 * align256(sizeof(int) * T);
@@ -375,11 +411,14 @@ md_status md_ffn_forward(const md_ffn* f, const float* x, int32_t T, float* y, v
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
   char* ws = static_cast<char*>(workspace);
   float* h = reinterpret_cast<float*>(ws);
+  const size_t H = f->gate.cols, F = f->gate.rows;
   if (T <= kMaxPairT) {
-    s = run_ffn(f, x, T, h, y, stream);
+    char* p = ws + align256(sizeof(float) * T * F);
+    const DigBuf xd = dig_buf_at(p, f->gate.type, T, (int)H);
+    const DigBuf hd = dig_buf_at(p + dig_buf_bytes(f->gate.type, T, (int)H), f->gate.type, T, (int)F);
+    s = run_ffn(f, x, T, nullptr, xd, hd, h, y, stream);
     return s == MD_OK ? ok() : s;
   }
-  const size_t H = f->gate.cols, F = f->gate.rows;
   size_t off = align256(sizeof(float) * T * F);
   u16* x_hi = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * H);
   u16* x_lo = reinterpret_cast<u16*>(ws + off); off += align256(2 * T * H);
@@ -436,10 +475,51 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   float* h = static_cast<float*>(P(w.h));
   const bool t1 = use_pairs(L, T);
 
+  if (t1) {
+    // few tokens: the router kernel also writes x's digit planes; selection
+    // happens inside the gate/up kernel, the combine inside the down kernel;
+    // each (token, slot) pair is an independent one-token problem
+    const md::RouterPlan rp = md::router_plan(T, H, E);
+    if (rp.gemm) return fail(MD_ERR_UNSUPPORTED, "router partial layout does not match the one-token kernels");
+    double* part = static_cast<double*>(P(w.part));
+    const DigBuf xd = dig_buf_at(ws + w.xd, fmt, T, H);
+    const DigBuf hd = dig_buf_at(ws + w.hd, fmt, T * k, F);
+    DigBuf sxd{}, shd{};
+    md::DigJob js{};
+    if (L->has_shared) {
+      const int sfmt = L->shared.gate.type;
+      sxd = dig_buf_at(ws + w.sxd, sfmt, T, H);
+      shd = dig_buf_at(ws + w.shd, sfmt, T, L->shared.gate.rows);
+      js = dig_job(x, T, H, sfmt, sxd);
+    }
+    if (!mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
+    e = md::launch_router(x, T, H, L->W_r, E, rp, part, dig_job(x, T, H, fmt, xd), js, stream);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
+    if (L->has_shared) {
+      s = run_ffn(&L->shared, x, T, &sxd, sxd, shd, static_cast<float*>(P(w.h_s)), y_s, stream);
+      if (s != MD_OK) return s;
+    }
+    if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_SELECT, ev0) || !mark(MD_STAGE_SELECT, ev1) ||
+        !mark(MD_STAGE_GATEUP, ev0))
+      return hip_fail(e, "event record");
+    e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                             L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, part, rp.S, L->router_bias,
+                             xd.planes, xd.scales, hd.planes, hd.scales, idx, gates, stream);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
+    e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
+                           gates, hd.planes, hd.scales, y_s, y, stream);
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+    if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
+      return hip_fail(e, "event record");
+    return ok();
+  }
+
   // shared expert: independent of the routing, enqueued first
   ChunkAct xa{nullptr, nullptr, nullptr, nullptr};
   if (!mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
-  if (!t1) {
+  {
     // the activation forms the chunk path's kernels need
     const bool need_pair = !row_type(fmt) || (L->has_shared && !row_type(L->shared.gate.type));
     const bool need_dig = row_type(fmt);
@@ -458,55 +538,35 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     }
   }
   if (L->has_shared) {
-    if (t1) {
-      s = run_ffn(&L->shared, x, T, static_cast<float*>(P(w.h_s)), y_s, stream);
-    } else {
-      ChunkAct xs = xa;
-      const int sfmt = L->shared.gate.type;
-      if (row_type(sfmt)) {  // x digits in the shared expert's own column order
-        e = md::launch_limbs(x, T, H, sfmt == MD_I4_ROW, static_cast<int8_t*>(P(w.xs_dig)),
-                             static_cast<int*>(P(w.xs_exp)), stream);
-        if (e != hipSuccess) return hip_fail(e, "digit launch");
-        xs.dig = static_cast<int8_t*>(P(w.xs_dig));
-        xs.expo = static_cast<int*>(P(w.xs_exp));
-      }
-      s = run_ffn_mfma(&L->shared, xs, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
-                       static_cast<u16*>(P(w.hs_lo)), static_cast<int8_t*>(P(w.hs_dig)), static_cast<int*>(P(w.hs_exp)),
-                       y_s, stream);
+    ChunkAct xs = xa;
+    const int sfmt = L->shared.gate.type;
+    if (row_type(sfmt)) {  // x digits in the shared expert's own column order
+      e = md::launch_limbs(x, T, H, sfmt == MD_I4_ROW, static_cast<int8_t*>(P(w.xs_dig)),
+                           static_cast<int*>(P(w.xs_exp)), stream);
+      if (e != hipSuccess) return hip_fail(e, "digit launch");
+      xs.dig = static_cast<int8_t*>(P(w.xs_dig));
+      xs.expo = static_cast<int*>(P(w.xs_exp));
     }
+    s = run_ffn_mfma(&L->shared, xs, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
+                     static_cast<u16*>(P(w.hs_lo)), static_cast<int8_t*>(P(w.hs_dig)), static_cast<int*>(P(w.hs_exp)),
+                     y_s, stream);
     if (s != MD_OK) return s;
   }
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
-  const int S = md::router_splits(H, E);
+  const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(P(w.part));
-  e = md::launch_router_part(x, T, H, L->W_r, E, S, part, stream);
+  e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");
-
-  if (t1) {
-    // few tokens: selection happens inside the gate/up kernel, the combine
-    // inside the down kernel; each (token, slot) pair is an independent
-    // one-token problem
-    if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
-    e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
-                             L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, part, S, L->router_bias, x,
-                             h, idx, gates, stream);
-    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
-    if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
-    e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
-                           gates, h, y_s, y, stream);
-    if (e != hipSuccess) return hip_fail(e, "down launch");
-    if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
-      return hip_fail(e, "event record");
-    return ok();
-  }
 
   // a chunk of tokens: group the (token, slot) pairs by expert, then one
   // grouped GEMM per stage on the matrix cores, each expert read once
   md::DispOut dout{static_cast<int*>(P(w.n_active)), static_cast<int*>(P(w.active_e)),
                    static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos))};
-  e = md::launch_route_finalize(part, S, L->router_bias, T, E, k, logits, idx, gates, &dout, stream);
-  if (e != hipSuccess) return hip_fail(e, "route finalize launch");
+  e = md::launch_select(part, rp, L->router_bias, T, E, k, logits, idx, gates, stream);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  e = md::launch_dispatch(idx, T, E, k, dout, stream);
+  if (e != hipSuccess) return hip_fail(e, "dispatch launch");
   if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
 
   md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T};

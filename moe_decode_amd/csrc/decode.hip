@@ -18,10 +18,15 @@
 //
 // Streaming: a lane group of L lanes owns a row; each lane owns one 16-byte
 // chunk position per K-slice, so the activations it multiplies never change
-// and stay in registers for every row the wave visits.  Row loads run in a
+// and stay in registers for every row the wave visits.  Activations enter as
+// integer digit planes (digits.hpp): one v_dot8 (4-bit weights) or v_dot4
+// (8-bit) per weight word and digit plane, exact int32 sums, one fp32 combine
+// per chunk.  The router kernel writes the digit planes of x; the gate/up
+// kernel writes those of h (each workgroup covers whole digit groups).  Row loads run in a
 // rolling window (several rows in flight while one is decoded).  Partial sums of the rows a lane group visited are reduced with
 // one transposed butterfly (N-1 exchanges for N rows instead of N log L).
 #include "common.hpp"
+#include "digits.hpp"
 #include "kernels.hpp"
 
 namespace md {
@@ -73,24 +78,90 @@ MD_DEV void load_row(RowBuf<FMT, CPL>& b, const uint8_t* row, int K, int c0) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i) b.w[i] = ld_stream(row + 16 * (int64_t)(c0 + L * i));
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) b.s[i] = chunk_scale<FMT>(row, K, c0 + L * i);
+  for (int i = 0; i < CPL; ++i) b.s[i] = dig_block_scale<FMT>(row, K, c0 + L * i);
+}
+
+// Activation digit planes of the CPL chunks a lane owns.
+template <int FMT, int CPL>
+struct ActDig {
+  u32x4 d[CPL][Dig<FMT>::NPL];
+  float sc[CPL];
+};
+
+template <int FMT, int L, int CPL>
+MD_DEV void load_act(ActDig<FMT, CPL>& x, const u32x4* planes, const float* scales, int c0) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+    for (int j = 0; j < Dig<FMT>::NPL; ++j) x.d[i][j] = planes[(int64_t)(c0 + L * i) * Dig<FMT>::NPL + j];
+    x.sc[i] = scales[c0 + L * i];
+  }
 }
 
 template <int FMT, int CPL>
-MD_DEV float row_dot(const RowBuf<FMT, CPL>& b, const float (&xv)[CPL][Fmt<FMT>::WPC]) {
+MD_DEV float row_dot(const RowBuf<FMT, CPL>& b, const ActDig<FMT, CPL>& x) {
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const float d = dot_chunk<FMT>(b.w[i], xv[i]);
-    acc = Fmt<FMT>::ROW ? acc + d : fmaf(b.s[i], d, acc);
+    const float v = dig_chunk<FMT>(b.w[i], x.d[i], x.sc[i]);
+    acc = Fmt<FMT>::ROW ? acc + v : fmaf(b.s[i], v, acc);
   }
   return acc;
 }
 
-template <int FMT, int L, int CPL>
-MD_DEV void load_xv(float (&xv)[CPL][Fmt<FMT>::WPC], const float* x, int c0) {
+// Digit planes of n values held one per thread (thread q: value q; n a
+// multiple of NV and at most blockDim.x): group g's planes go to
+// planes[g * NPL .. ] and its scale to scales[g].  ys: LDS scratch of n words.
+// Every thread of the block must call it (it synchronises).
+template <int FMT>
+MD_DEV void dig_block(float v, int n, uint32_t* ys, u32x4* planes, float* scales) {
+  using D = Dig<FMT>;
+  const int q = threadIdx.x;
+  float m = q < n ? fabsf(v) : 0.f;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) load_x<FMT, XF32>(x, c0 + L * i, xv[i]);
+  for (int off = D::NV / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const int s = dig_shift<FMT>(m);
+  if (q < n) {
+    ys[q] = dig_biased<FMT>(v, s);
+    if (q % D::NV == 0) scales[q / D::NV] = ldexpf(1.0f, -s);
+  }
+  __syncthreads();
+  uint32_t* out = reinterpret_cast<uint32_t*>(planes);
+  const int nw = n / D::NV * D::NPL * 4;
+  for (int i = q; i < nw; i += blockDim.x) {
+    const int g = i / (D::NPL * 4), w = i % (D::NPL * 4);
+    out[i] = dig_word<FMT>(w / 4, w % 4, [&](int p) { return ys[g * D::NV + p]; });
+  }
+  __syncthreads();
+}
+
+// The digit planes of rows [0, R) of a row-major R x K fp32 matrix (K a
+// multiple of 256), 256 values per block iteration; grid-stride over blocks.
+MD_DEV void dig_rows(const DigJob& j, uint32_t* ys) {
+  if (!j.x) return;
+  const int64_t n = (int64_t)j.R * j.K;
+  for (int64_t base = (int64_t)blockIdx.x * 256; base < n; base += (int64_t)gridDim.x * 256) {
+    const float v = j.x[base + threadIdx.x];
+    const int64_t g0 = base / dig_nv(j.fmt);
+    switch (j.fmt) {
+      case Q8_0: dig_block<Q8_0>(v, 256, ys, j.planes + g0 * Dig<Q8_0>::NPL, j.scales + g0); break;
+      case Q4_0: dig_block<Q4_0>(v, 256, ys, j.planes + g0 * Dig<Q4_0>::NPL, j.scales + g0); break;
+      case I8_ROW: dig_block<I8_ROW>(v, 256, ys, j.planes + g0 * Dig<I8_ROW>::NPL, j.scales + g0); break;
+      default: dig_block<I4_ROW>(v, 256, ys, j.planes + g0 * Dig<I4_ROW>::NPL, j.scales + g0); break;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_digits(DigJob j) {
+  __shared__ uint32_t ys[256];
+  dig_rows(j, ys);
+}
+
+hipError_t launch_digits(const DigJob& j, hipStream_t st) {
+  const int64_t n = (int64_t)j.R * j.K;
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_digits, dim3(blocks), dim3(256), 0, st, j);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ router
@@ -101,8 +172,12 @@ MD_DEV void load_xv(float (&xv)[CPL][Fmt<FMT>::WPC], const float* x, int c0) {
 // S partials in order, then the bias, and rounds once to fp32.
 __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr, int E, int S,
-                                                     double* __restrict__ part) {
+                                                     double* __restrict__ part, DigJob j0, DigJob j1) {
   __shared__ double red[4][4];
+  __shared__ uint32_t ys[256];
+  // the activations' digit planes for the expert kernels (independent of the routing)
+  dig_rows(j0, ys);
+  dig_rows(j1, ys);
   const int e = blockIdx.x / S, sl = blockIdx.x % S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ks = H / S / 4;             // elements per wave, a multiple of 64
@@ -160,8 +235,8 @@ int router_splits(int H, int E) {
 }
 
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(k_router_part, dim3(E * S), dim3(256), 0, st, x, T, H, Wr, E, S, part);
+                              const DigJob& j0, const DigJob& j1, hipStream_t st) {
+  hipLaunchKernelGGL(k_router_part, dim3(E * S), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1);
   return hipGetLastError();
 }
 
@@ -235,8 +310,10 @@ struct GateUpT1 {
   const double* part;    // router partials [T][E][S]; nullptr: dense mode (expert 0, one slot per token)
   const float* bias;     // router bias [E] or nullptr
   int S;
-  const float* x;        // [T][H]
-  float* h;              // [T*slots][F]
+  const u32x4* xd;       // x digit planes [T][H/NV][NPL]
+  const float* xsc;      // x digit scales [T][H/NV]
+  u32x4* hd;             // h digit planes [T*slots][F/NV][NPL]
+  float* hsc;            // h digit scales [T*slots][F/NV]
   int* idx_out;          // [T][k], written by the blocks with blockIdx.x == 0 and slot 0
   float* gates_out;
   int KS, RGW;           // K-slices per row, row-group waves per block
@@ -245,20 +322,25 @@ struct GateUpT1 {
 // Block = KS * RGW waves.  Wave (rg, ks) streams kNP row pairs (gate row f
 // and up row f) per lane group over K-slice ks.  With KS > 1 the slices meet
 // in LDS.  blockIdx.y = t * slots + j: token t's slot j (each pair of a
-// several-token call is an independent one-token problem).
+// several-token call is an independent one-token problem).  The block's rows
+// are whole digit groups of h, whose planes it writes for the down kernel.
 template <int FMT, int L, int kNP>
 __global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
-  constexpr int G = 64 / L, W = Fmt<FMT>::WPC;
-  extern __shared__ float lds[];  // [RGW][G][kNP][KS][2]
+  using D = Dig<FMT>;
+  constexpr int G = 64 / L;
+  extern __shared__ float lds[];  // [npairs] h values, then [RGW][G][kNP][KS][2] slice sums
   __shared__ int s_sel[8];
+  __shared__ uint32_t ys[256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane / L, t = lane % L;
   const int ks = wave % a.KS, rg = wave / a.KS;
   const int c0 = ks * L + t;  // this lane's chunk (one chunk per lane per slice)
   const int slots = a.part ? a.k : 1;
   const int tok = blockIdx.y / slots, slot = blockIdx.y % slots;
-  float xv[1][W];
-  load_xv<FMT, L, 1>(xv, a.x + (int64_t)tok * a.H, c0);
+  const int npairs = a.RGW * G * kNP;
+  ActDig<FMT, 1> xa;
+  const int ngx = a.H / D::NV;
+  load_act<FMT, L, 1>(xa, a.xd + (int64_t)tok * ngx * D::NPL, a.xsc + (int64_t)tok * ngx, c0);
 
   int e = 0;
   if (a.part) {
@@ -281,7 +363,8 @@ __global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
     e = s_sel[slot];
   }
 
-  const int fb = ((blockIdx.x * a.RGW + rg) * G + g) * kNP;
+  const int f0 = blockIdx.x * npairs;
+  const int fb = f0 + ((rg * G + g) * kNP);
   const int64_t rb = row_bytes(FMT, a.H);
   const uint8_t* Gm = a.gq + (int64_t)e * a.mat_bytes;
   const uint8_t* Um = a.uq + (int64_t)e * a.mat_bytes;
@@ -298,8 +381,8 @@ __global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
     }
 #pragma unroll
     for (int p = 0; p < kNP; ++p) {
-      pg[p] = row_dot<FMT, 1>(bg[p % kD], xv);
-      pu[p] = row_dot<FMT, 1>(bu[p % kD], xv);
+      pg[p] = row_dot<FMT, 1>(bg[p % kD], xa);
+      pu[p] = row_dot<FMT, 1>(bu[p % kD], xa);
       if (p + kD < kNP) {
         load_row<FMT, L, 1>(bg[p % kD], rowp(Gm, p + kD), a.H, c0);
         load_row<FMT, L, 1>(bu[p % kD], rowp(Um, p + kD), a.H, c0);
@@ -310,30 +393,37 @@ __global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
   const float su = butterfly<kNP, L>(pu, t);
   const int r = (t / (L / kNP)) % kNP;
   const bool writer = (t % (L / kNP)) == 0;
-  auto finish = [&](int f, float av, float uv) {
-    if (f >= a.F) return;
+  float* hv = lds;
+  auto finish = [&](int q, float av, float uv) {
+    const int f = f0 + q;
     float sg = 1.f, sv = 1.f;
     if constexpr (Fmt<FMT>::ROW) {
-      sg = a.gs[(int64_t)e * a.F + f] * row_post<FMT>();
-      sv = a.us[(int64_t)e * a.F + f] * row_post<FMT>();
+      if (f < a.F) {
+        sg = a.gs[(int64_t)e * a.F + f];
+        sv = a.us[(int64_t)e * a.F + f];
+      }
     }
-    a.h[(int64_t)blockIdx.y * a.F + f] = act_f(a.act, av * sg) * (uv * sv);
+    hv[q] = f < a.F ? act_f(a.act, av * sg) * (uv * sv) : 0.f;
   };
   if (a.KS == 1) {
-    if (writer) finish(fb + r, sa, su);
-    return;
+    if (writer) finish((rg * G + g) * kNP + r, sa, su);
+  } else {
+    float* red = lds + npairs + ((((rg * G + g) * kNP + r) * a.KS + ks) * 2);
+    if (writer) { red[0] = sa; red[1] = su; }
+    __syncthreads();
+    for (int q = threadIdx.x; q < npairs; q += blockDim.x) {
+      const float* rq = lds + npairs + (int64_t)q * a.KS * 2;
+      float av = 0.f, uv = 0.f;
+      for (int s = 0; s < a.KS; ++s) { av += rq[2 * s]; uv += rq[2 * s + 1]; }
+      finish(q, av, uv);
+    }
   }
-  float* red = lds + ((((rg * G + g) * kNP + r) * a.KS + ks) * 2);
-  if (writer) { red[0] = sa; red[1] = su; }
   __syncthreads();
-  const int npairs = a.RGW * G * kNP;
-  for (int q = threadIdx.x; q < npairs; q += blockDim.x) {
-    const float* rq = lds + (int64_t)q * a.KS * 2;
-    float av = 0.f, uv = 0.f;
-    for (int s = 0; s < a.KS; ++s) { av += rq[2 * s]; uv += rq[2 * s + 1]; }
-    const int rgq = q / (G * kNP), gq_ = (q / kNP) % G, rq_ = q % kNP;
-    finish(((blockIdx.x * a.RGW + rgq) * G + gq_) * kNP + rq_, av, uv);
-  }
+  // digit planes of the block's h values (rows past F form whole groups and are skipped)
+  const int n = min(npairs, a.F - f0);
+  const int ngh = a.F / D::NV;
+  const int64_t g0 = (int64_t)blockIdx.y * ngh + f0 / D::NV;
+  dig_block<FMT>(threadIdx.x < npairs ? hv[threadIdx.x] : 0.f, n, ys, a.hd + g0 * D::NPL, a.hsc + g0);
 }
 
 // ------------------------------------------------------------------ down
@@ -345,7 +435,8 @@ struct DownT1 {
   int H, F, k;
   const int* idx;        // [T][k]; nullptr: dense mode (expert 0, gate 1, one slot)
   const float* gates;    // [T][k]
-  const float* h;        // [T*k][F]
+  const u32x4* hd;       // h digit planes [T*k][F/NV][NPL]
+  const float* hsc;      // h digit scales [T*k][F/NV]
   const float* y_add;    // [T][H], nullable: added to the combined result
   float* y;              // [T][H]
 };
@@ -354,15 +445,17 @@ struct DownT1 {
 // expert (t = blockIdx.y).
 template <int FMT, int L, int CPL>
 __global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
-  constexpr int G = 64 / L, W = Fmt<FMT>::WPC, NR = kNRW / G;
+  using D = Dig<FMT>;
+  constexpr int G = 64 / L, NR = kNRW / G;
   __shared__ float red[8][kNRW];
   static_assert(kNRW % G == 0, "rows per block");
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   const int g = lane / L, t = lane % L;
   const int tok = blockIdx.y, p = tok * a.k + j;
   const int e = a.idx ? a.idx[p] : 0;
-  float xv[CPL][W];
-  load_xv<FMT, L, CPL>(xv, a.h + (int64_t)p * a.F, t);
+  ActDig<FMT, CPL> ha;
+  const int ngh = a.F / D::NV;
+  load_act<FMT, L, CPL>(ha, a.hd + (int64_t)p * ngh * D::NPL, a.hsc + (int64_t)p * ngh, t);
   const int ib = blockIdx.x * kNRW + g * NR;
   const int64_t rb = row_bytes(FMT, a.F);
   const uint8_t* Dm = a.dq + (int64_t)e * a.mat_bytes;
@@ -376,7 +469,7 @@ __global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
     for (int r = 0; r < kD; ++r) load_row<FMT, L, CPL>(b[r], rowp(r), a.F, t);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      part[r] = row_dot<FMT, CPL>(b[r % kD], xv);
+      part[r] = row_dot<FMT, CPL>(b[r % kD], ha);
       if (r + kD < NR) load_row<FMT, L, CPL>(b[r % kD], rowp(r + kD), a.F, t);
     }
   }
@@ -385,7 +478,7 @@ __global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
   if ((t % (L / NR)) == 0) {
     const int i = ib + r;
     float v = s;
-    if constexpr (Fmt<FMT>::ROW) v *= a.ds[(int64_t)e * a.H + min(i, a.H - 1)] * row_post<FMT>();
+    if constexpr (Fmt<FMT>::ROW) v *= a.ds[(int64_t)e * a.H + min(i, a.H - 1)];
     red[j][g * NR + r] = v;
   }
   __syncthreads();
@@ -412,32 +505,56 @@ static int pow2_div(int n) {
   return L;
 }
 
+// Gate/up geometry: lane groups of L lanes over KS K-slices, RGW row-group
+// waves per slice, NP row pairs per lane group; the block's G*RGW*NP rows
+// form whole digit groups of h (a multiple of NV, at most 256).
+struct GuGeom {
+  int L, G, KS, RGW, NP;
+};
+
+static bool gu_geom(int fmt, int F, int H, int slots, GuGeom& q) {
+  const int nc = nchunks(fmt, H);
+  q.L = pow2_div(nc);
+  if (q.L < 8) return false;
+  q.G = 64 / q.L;
+  q.KS = nc / q.L;
+  q.RGW = q.KS >= 4 ? 1 : 4 / q.KS;
+  // row pairs per lane group: as many as keep >= 2048 waves in flight
+  q.NP = MD_GU_MAXNP;
+  while (q.NP > 2 && (int64_t)((F + q.RGW * q.G * q.NP - 1) / (q.RGW * q.G * q.NP)) * slots * q.KS * q.RGW < 2048)
+    q.NP /= 2;
+  const int NV = dig_nv(fmt);
+  while ((q.RGW * q.G * q.NP) % NV) {
+    if (q.NP < MD_GU_MAXNP) q.NP *= 2;
+    else q.RGW *= 2;
+  }
+  return q.KS * q.RGW <= 16 && q.RGW * q.G * q.NP <= 256;
+}
+
 bool t1_supported(int fmt, int H, int F) {
-  const int ncg = nchunks(fmt, H), ncd = nchunks(fmt, F);
-  const int Lg = pow2_div(ncg), Ld = pow2_div(ncd);
-  if (Lg < 8 || Ld < 8) return false;
-  if (ncg / Lg > 16) return false;          // K-slices per block
+  GuGeom q;
+  if (!gu_geom(fmt, F, H, 1, q) || !gu_geom(fmt, F, H, 64, q)) return false;
+  const int ncd = nchunks(fmt, F);
+  const int Ld = pow2_div(ncd);
+  if (Ld < 8) return false;
   const int cpl = ncd / Ld;
   return cpl == 1 || cpl == 2 || cpl == 3;
 }
 
 hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
                             int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const double* part, int S,
-                            const float* bias, const float* x, float* h, int* idx_out, float* gates_out,
-                            hipStream_t st) {
-  const int nc = nchunks(fmt, H);
-  const int L = pow2_div(nc), G = 64 / L;
-  GateUpT1 a{gq, uq, gs, us, mat_bytes, F, H, act, E, k, part, bias, S, x, h, idx_out, gates_out, nc / L, 1};
-  // row-group waves per block: fill up to 4 waves when one slice suffices
-  a.RGW = a.KS >= 4 ? 1 : 4 / a.KS;
-  // row pairs per lane group: as many as keep >= 2048 waves in flight
+                            const float* bias, const void* xd, const float* xsc, void* hd, float* hsc, int* idx_out,
+                            float* gates_out, hipStream_t st) {
   const int slots = (part ? k : 1) * T;
-  int NP = MD_GU_MAXNP;
-  while (NP > 2 && (int64_t)((F + a.RGW * G * NP - 1) / (a.RGW * G * NP)) * slots * a.KS * a.RGW < 2048) NP /= 2;
-  const int pairs_per_block = a.RGW * G * NP;
+  GuGeom q;
+  if (!gu_geom(fmt, F, H, slots, q)) return hipErrorInvalidConfiguration;
+  GateUpT1 a{gq, uq, gs, us, mat_bytes, F, H, act, E, k, part, bias, S, static_cast<const u32x4*>(xd), xsc,
+             static_cast<u32x4*>(hd), hsc, idx_out, gates_out, q.KS, q.RGW};
+  const int L = q.L, NP = q.NP;
+  const int pairs_per_block = q.RGW * q.G * NP;
   const dim3 grid((F + pairs_per_block - 1) / pairs_per_block, slots);
-  const dim3 block(64 * a.KS * a.RGW);
-  const size_t lds = a.KS > 1 ? sizeof(float) * 2 * a.KS * pairs_per_block : 0;
+  const dim3 block(64 * q.KS * q.RGW);
+  const size_t lds = sizeof(float) * (pairs_per_block + (q.KS > 1 ? 2 * q.KS * pairs_per_block : 0));
 #define MD_GU(F_, L_, N_) \
   if (fmt == F_ && L == L_ && NP == N_) { \
     hipLaunchKernelGGL((k_gateup_t1<F_, L_, N_>), grid, block, lds, st, a); return hipGetLastError(); }
@@ -451,11 +568,11 @@ hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const
 }
 
 hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t mat_bytes, int H, int F, int k, int T,
-                          const int* idx, const float* gates, const float* h, const float* y_add, float* y,
-                          hipStream_t st) {
+                          const int* idx, const float* gates, const void* hd, const float* hsc, const float* y_add,
+                          float* y, hipStream_t st) {
   const int nc = nchunks(fmt, F);
   const int L = pow2_div(nc), CPL = nc / L;
-  DownT1 a{dq, ds, mat_bytes, H, F, idx ? k : 1, idx, gates, h, y_add, y};
+  DownT1 a{dq, ds, mat_bytes, H, F, idx ? k : 1, idx, gates, static_cast<const u32x4*>(hd), hsc, y_add, y};
   const dim3 grid((H + kNRW - 1) / kNRW, T), block(64 * a.k);
 #define MD_DN(F_, L_, C_) \
   if (fmt == F_ && L == L_ && CPL == C_) { \

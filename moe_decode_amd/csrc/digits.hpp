@@ -1,0 +1,135 @@
+// digits.hpp -- activations as integer digit planes for the integer dot
+// instructions of gfx950 (v_dot8_i32_i4, v_dot4_i32_i8).
+//
+// A group is the WPC activations that one 16-byte weight chunk multiplies.
+// The group is scaled by a power of two 2^s, chosen from its largest
+// magnitude, and rounded to integers X with |X| <= 2^26 (4-bit weights) or
+// 2^29 (8-bit weights).  X is written in balanced base 16 (seven digits in
+// [-8, 7]) or balanced base 256 (four digits in [-128, 127]): adding the bias
+// B = sum_j 8*16^j (or 128*256^j) makes every nibble (byte) of Y = X + B the
+// digit plus 8 (128), so flipping its top bit gives the digit as a two's-
+// complement nibble (byte).  Plane j packs digit j of every value of the group
+// into the nibble or byte position of the weight it multiplies, so one dot
+// instruction per weight word forms  sum_i w_i * d_j(X_i)  exactly in int32,
+// and  sum_j base^j * P_j = sum_i w_i X_i.  The chunk's value is that integer
+// times 2^-s; the only rounding is that of x to X (relative 2^-27 of the
+// group's largest magnitude, or 2^-30) and of the final fp32 combine.
+#pragma once
+
+#include "common.hpp"
+
+namespace md {
+
+template <int FMT> struct Dig;
+template <> struct Dig<Q4_0> {
+  static constexpr int NV = 32, NPL = 7, SB = 26, SH = 4, PER = 8;
+  static constexpr uint32_t BIAS = 0x08888888u, FLIP = 0x88888888u;
+  // word m, nibble i <- value: low nibble of byte b is weight 4m+b, high is 16+4m+b
+  static constexpr int pos(int m, int i) { return (i & 1) ? 16 + 4 * m + (i >> 1) : 4 * m + (i >> 1); }
+};
+template <> struct Dig<I4_ROW> {
+  static constexpr int NV = 32, NPL = 7, SB = 26, SH = 4, PER = 8;
+  static constexpr uint32_t BIAS = 0x08888888u, FLIP = 0x88888888u;
+  static constexpr int pos(int m, int i) { return 8 * m + i; }
+};
+template <> struct Dig<Q8_0> {
+  static constexpr int NV = 16, NPL = 4, SB = 29, SH = 8, PER = 4;
+  static constexpr uint32_t BIAS = 0x80808080u, FLIP = 0x80808080u;
+  static constexpr int pos(int m, int i) { return 4 * m + i; }
+};
+template <> struct Dig<I8_ROW> : Dig<Q8_0> {};
+
+__host__ __device__ constexpr int dig_nv(int fmt) { return (fmt == Q8_0 || fmt == I8_ROW) ? 16 : 32; }
+__host__ __device__ constexpr int dig_npl(int fmt) { return (fmt == Q8_0 || fmt == I8_ROW) ? 4 : 7; }
+// bytes of digit planes per group, and per K activations
+__host__ __device__ constexpr int64_t dig_group_bytes(int fmt) { return 16 * dig_npl(fmt); }
+__host__ __device__ constexpr int64_t dig_bytes(int fmt, int K) { return (int64_t)(K / dig_nv(fmt)) * dig_group_bytes(fmt); }
+
+// Shift s of a group whose largest magnitude is m: m < 2^e, s = SB - e,
+// limited so that 2^-s stays a normal number for tiny groups.
+template <int FMT>
+MD_DEV int dig_shift(float m) {
+  int e = 0;
+  (void)frexpf(m, &e);
+  const int s = Dig<FMT>::SB - e;
+  return s > 120 ? 120 : s;
+}
+
+// Biased integer image of one value (its nibbles / bytes are digit + 8 / 128).
+template <int FMT>
+MD_DEV uint32_t dig_biased(float v, int s) {
+  return (uint32_t)(int)rintf(ldexpf(v, s)) + Dig<FMT>::BIAS;
+}
+
+// Word (plane j, weight word m) of a group from the biased images Y[0..NV).
+template <int FMT, typename GetY>
+MD_DEV uint32_t dig_word(int j, int m, GetY Y) {
+  using D = Dig<FMT>;
+  constexpr uint32_t mask = (1u << D::SH) - 1u;
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < D::PER; ++i) w |= ((Y(D::pos(m, i)) >> (D::SH * j)) & mask) << (D::SH * i);
+  return w ^ D::FLIP;
+}
+
+// One thread writes a whole group: planes (NPL x 4 words) and the scale 2^-s.
+template <int FMT>
+MD_DEV void dig_group(const float* v, uint32_t* planes, float* scale) {
+  using D = Dig<FMT>;
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < D::NV; ++i) m = fmaxf(m, fabsf(v[i]));
+  const int s = dig_shift<FMT>(m);
+  uint32_t Y[D::NV];
+#pragma unroll
+  for (int i = 0; i < D::NV; ++i) Y[i] = dig_biased<FMT>(v[i], s);
+#pragma unroll
+  for (int j = 0; j < D::NPL; ++j)
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) planes[4 * j + mm] = dig_word<FMT>(j, mm, [&](int p) { return Y[p]; });
+  *scale = ldexpf(1.0f, -s);
+}
+
+// Value of one chunk: w = the chunk's 4 weight words, d = its group's planes,
+// sc = 2^-s.  Returns sum_i w_i x_i (before the weights' block or row scale).
+template <int FMT>
+MD_DEV float dig_chunk(u32x4 w, const u32x4* d, float sc) {
+  using D = Dig<FMT>;
+  if constexpr (FMT == Q4_0) w ^= u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};  // n - 8
+  int acc[D::NPL];
+#pragma unroll
+  for (int j = 0; j < D::NPL; ++j) {
+    int a = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if constexpr (D::SH == 4)
+        a = __builtin_amdgcn_sdot8((int)w[m], (int)d[j][m], a, false);
+      else
+        a = __builtin_amdgcn_sdot4((int)w[m], (int)d[j][m], a, false);
+    }
+    acc[j] = a;
+  }
+  int lo, hi;
+  if constexpr (D::SH == 4) {
+    lo = acc[0] + 16 * (acc[1] + 16 * (acc[2] + 16 * acc[3]));
+    hi = acc[4] + 16 * (acc[5] + 16 * acc[6]);
+  } else {
+    lo = acc[0] + 256 * acc[1];
+    hi = acc[2] + 256 * acc[3];
+  }
+  return fmaf((float)hi, sc * 65536.0f, (float)lo * sc);
+}
+
+// Block scale of chunk c for the digit path (no 1/16: nibbles enter as values).
+template <int FMT>
+MD_DEV float dig_block_scale(const uint8_t* row, int K, int c) {
+  if constexpr (FMT == Q8_0) {
+    return h2f(*reinterpret_cast<const uint16_t*>(row + K + 2 * (c >> 1)));
+  } else if constexpr (FMT == Q4_0) {
+    return h2f(*reinterpret_cast<const uint16_t*>(row + (K / 32) * 16 + 2 * c));
+  } else {
+    return 1.0f;
+  }
+}
+
+}  // namespace md

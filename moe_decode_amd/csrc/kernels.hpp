@@ -29,6 +29,19 @@ struct DispOut {
   int* pos_of_pair;
 };
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Digit planes (digits.hpp) of the rows of an R x K fp32 matrix, in the
+// layout of weight format fmt: planes [R][K/NV][NPL] x 16 bytes, scales
+// [R][K/NV].  x == nullptr: nothing to do.
+struct DigJob {
+  const float* x;
+  int R, K, fmt;
+  u32x4* planes;
+  float* scales;
+};
+hipError_t launch_digits(const DigJob& j, hipStream_t st);
+
 struct GemvCfg {
   int L;        // lanes per row group (8..64)
   int R;        // rows per lane group
@@ -46,21 +59,35 @@ GemvCfg qgemv_config(int fmt, int N, int K, int batch);
 hipError_t launch_qgemv(int fmt, int xt, const GemvCfg& c, const uint8_t* W, const float* scales, int N, int K,
                         const void* x, int batch, float* y, float* partial, hipStream_t st);
 
+// Router logits come as S K-slices of fp64 partials, element (s, t, e) at
+// part[s*ps + t*pt + e*pe]: [t][e][s] for a few tokens (the layout the
+// one-token gate/up kernel reads), [s][t][e] for a chunk (router GEMM).
+struct RouterPlan {
+  bool gemm;
+  int S;
+  int64_t ps, pt, pe;
+};
+RouterPlan router_plan(int T, int H, int E);
 int router_splits(int H, int E);
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
-                              hipStream_t st);
-hipError_t launch_route_finalize(const double* part, int S, const float* bias, int T, int E, int k, float* logits,
-                                 int* idx, float* gates, const DispOut* d, hipStream_t st);
+                              const DigJob& j0, const DigJob& j1, hipStream_t st);
+// Also runs the digit jobs j0, j1 (small-T plan only; the GEMM plan rejects them).
+hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, const RouterPlan& p, double* part,
+                         const DigJob& j0, const DigJob& j1, hipStream_t st);
+hipError_t launch_select(const double* part, const RouterPlan& p, const float* bias, int T, int E, int k,
+                         float* logits, int* idx, float* gates, hipStream_t st);
+hipError_t launch_dispatch(const int* idx, int T, int E, int k, const DispOut& d, hipStream_t st);
 
 // one-token decode path (decode.hip)
 bool t1_supported(int fmt, int H, int F);
+// x and h enter as digit planes (planes, scales) in the weights' format.
 hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
                             int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const double* part, int S,
-                            const float* bias, const float* x, float* h, int* idx_out, float* gates_out,
-                            hipStream_t st);
+                            const float* bias, const void* xd, const float* xsc, void* hd, float* hsc, int* idx_out,
+                            float* gates_out, hipStream_t st);
 hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t mat_bytes, int H, int F, int k, int T,
-                          const int* idx, const float* gates, const float* h, const float* y_add, float* y,
-                          hipStream_t st);
+                          const int* idx, const float* gates, const void* hd, const float* hsc, const float* y_add,
+                          float* y, hipStream_t st);
 
 // prefill grouped GEMM on the matrix cores (prefill.hip)
 hipError_t launch_split_bf16(const float* x, int64_t n, unsigned short* hi, unsigned short* lo, hipStream_t st);

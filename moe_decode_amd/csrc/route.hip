@@ -1,7 +1,7 @@
-// route.hip -- top-k selection with softmax gates for many tokens, the expert
-// dispatch, and the weight layout pass (gfx950, wave64).
+// route.hip -- the chunk router GEMM, top-k selection with softmax gates for
+// many tokens, the expert dispatch, and the weight layout pass (gfx950, wave64).
 //
-// The logits are formed from k_router_part's fp64 partials (added in a fixed
+// The logits are formed from fp64 partials over K-slices (added in slice
 // order, plus the bias, rounded once to fp32).  Selection uses 64-bit keys: the order-preserving image of the fp32 logit in
 // the high word (with -0 folded onto +0) and the complemented expert index in
 // the low word, so one integer maximum picks the largest logit and, among
@@ -11,6 +11,122 @@
 #include "kernels.hpp"
 
 namespace md {
+
+// -------------------------------------------------------------- router
+
+// Chunk router: logits partials of many tokens as a register-tiled fp64 GEMM.
+// Block (ex, ty, s) covers experts 64*ex.., tokens 64*ty.. and K-slice s; a
+// thread owns 4 experts x 4 tokens (experts tx + 16i, tokens tyy + 16j).  W_r
+// and x tiles are staged as fp32 in LDS (transposed, padded) and widened
+// to fp64 at use; each product of two fp32 values is exact in fp64, and the
+// K-slice's terms are accumulated in ascending k with fp64 FMAs.
+constexpr int kRG = 64;   // experts / tokens per block tile
+constexpr int kRKC = 32;  // K per LDS stage
+
+__global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x, int T, int H,
+                                                     const float* __restrict__ Wr, int E, int Ks,
+                                                     double* __restrict__ part) {
+  __shared__ float sw[kRKC][kRG + 1];
+  __shared__ float sx[kRKC][kRG + 1];
+  const int tid = threadIdx.x, tx = tid & 15, tyy = tid >> 4;
+  const int e0 = blockIdx.x * kRG, t0 = blockIdx.y * kRG, sl = blockIdx.z;
+  const int kbeg = sl * Ks;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+
+  // the next stage's tiles are fetched into registers while this one is used
+  float4 pw[2], px[2];
+  auto fetch = [&](int kc) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int idx = tid + 256 * r, row = idx >> 3, c4 = idx & 7;
+      pw[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      px[r] = pw[r];
+      if (e0 + row < E) pw[r] = *reinterpret_cast<const float4*>(Wr + (int64_t)(e0 + row) * H + kc + 4 * c4);
+      if (t0 + row < T) px[r] = *reinterpret_cast<const float4*>(x + (int64_t)(t0 + row) * H + kc + 4 * c4);
+    }
+  };
+  fetch(kbeg);
+  for (int kc = kbeg; kc < kbeg + Ks; kc += kRKC) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int idx = tid + 256 * r, row = idx >> 3, c4 = idx & 7;
+      sw[4 * c4 + 0][row] = pw[r].x; sw[4 * c4 + 1][row] = pw[r].y;
+      sw[4 * c4 + 2][row] = pw[r].z; sw[4 * c4 + 3][row] = pw[r].w;
+      sx[4 * c4 + 0][row] = px[r].x; sx[4 * c4 + 1][row] = px[r].y;
+      sx[4 * c4 + 2][row] = px[r].z; sx[4 * c4 + 3][row] = px[r].w;
+    }
+    __syncthreads();
+    if (kc + kRKC < kbeg + Ks) fetch(kc + kRKC);
+#pragma unroll 4
+    for (int kk = 0; kk < kRKC; ++kk) {
+      double wd[4], xd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wd[i] = (double)sw[kk][tx + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xd[j] = (double)sx[kk][tyy + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(wd[i], xd[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + tyy + 16 * j;
+    if (t >= T) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + tx + 16 * i;
+      if (e < E) part[((int64_t)sl * T + t) * E + e] = acc[i][j];
+    }
+  }
+}
+
+#ifndef MD_ROUTER_GEMM_BLOCKS
+#define MD_ROUTER_GEMM_BLOCKS 256
+#endif
+
+RouterPlan router_plan(int T, int H, int E) {
+  RouterPlan p{};
+  if (T <= 8) {  // one block per (expert, K-slice); partials [t][e][s]
+    p.gemm = false;
+    p.S = router_splits(H, E);
+    p.ps = 1;
+    p.pt = (int64_t)E * p.S;
+    p.pe = p.S;
+    return p;
+  }
+  // tiles x K-slices: the fewest slices giving MD_ROUTER_GEMM_BLOCKS blocks,
+  // with at least two LDS stages per slice; partials [s][t][e]
+  const int tiles = ((E + kRG - 1) / kRG) * ((T + kRG - 1) / kRG);
+  const int units = H / kRKC;
+  int S = 1;
+  for (int d = 1; d <= units; ++d) {
+    if (units % d || H / d < 2 * kRKC) continue;
+    S = d;
+    if (tiles * d >= MD_ROUTER_GEMM_BLOCKS) break;
+  }
+  p.gemm = true;
+  p.S = S;
+  p.ps = (int64_t)T * E;
+  p.pt = E;
+  p.pe = 1;
+  return p;
+}
+
+hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, const RouterPlan& p, double* part,
+                         const DigJob& j0, const DigJob& j1, hipStream_t st) {
+  if (!p.gemm) return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, st);
+  if (j0.x || j1.x) return hipErrorInvalidValue;
+  const dim3 grid((E + kRG - 1) / kRG, (T + kRG - 1) / kRG, p.S);
+  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, st, x, T, H, Wr, E, H / p.S, part);
+  return hipGetLastError();
+}
 
 // -------------------------------------------------------------- select
 
@@ -28,85 +144,98 @@ MD_DEV uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// One workgroup (1024 threads).  Wave w handles tokens w, w+16, ...
-// Then (when d != nullptr) a stable counting sort of the T*k pairs by expert:
-// per-expert token bitmasks give each pair its rank among the pairs of its
-// expert (pairs of one expert are ordered by token, and a token selects an
-// expert at most once), exclusive scans give the offsets and the list of
-// active experts in ascending order.
-__global__ __launch_bounds__(1024) void k_route_finalize(const double* __restrict__ part, int S,
-                                                         const float* __restrict__ bias, int T, int E, int k,
-                                                         float* __restrict__ logits, int* __restrict__ idx,
-                                                         float* __restrict__ gates, DispOut d, int do_disp) {
+// One workgroup per token.  Thread e forms expert e's logit: the S partials
+// added in slice order, then the bias, rounded once to fp32.  Wave 0 then
+// takes the k winners one at a time by a 64-bit wave maximum; lane j
+// computes exp(l_j - l_0) in fp64, the sum runs over j in order, and lane j
+// writes gate j.
+__global__ __launch_bounds__(256) void k_select(const double* __restrict__ part, int S, int64_t ps, int64_t pt,
+                                                int64_t pe, const float* __restrict__ bias, int T, int E, int k,
+                                                float* __restrict__ logits, int* __restrict__ idx,
+                                                float* __restrict__ gates) {
+  __shared__ float s_l[256];
+  const int t = blockIdx.x, e = threadIdx.x, lane = threadIdx.x & 63;
+  if (e < E) {
+    const double* p = part + t * pt + e * pe;
+    double a = 0.0;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      double v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = p[(s + i) * ps];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a += v[i];
+    }
+    for (; s < S; ++s) a += p[s * ps];
+    if (bias) a += (double)bias[e];
+    const float l = (float)a;
+    if (logits) logits[(int64_t)t * E + e] = l;
+    s_l[e] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  uint64_t key[4];
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ei = lane + 64 * i;
+    key[i] = 0;
+    lv[i] = 0.f;
+    if (ei < E) {
+      lv[i] = s_l[ei];
+      key[i] = ((uint64_t)order_key(lv[i]) << 32) | (uint32_t)(~(uint32_t)ei);
+    }
+  }
+  float my_l = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int w = (int)(~(uint32_t)best);
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == w) { key[i] = 0; l = lv[i]; }
+    l = __shfl(l, w & 63, 64);
+    if (lane == j) { my_l = l; my_e = w; }
+  }
+  const double m = (double)__shfl(my_l, 0, 64);
+  const double ex = lane < k ? exp((double)my_l - m) : 0.0;
+  double z = 0.0;
+  for (int j = 0; j < k; ++j) z += __shfl(ex, j, 64);
+  if (lane < k) {
+    idx[t * k + lane] = my_e;
+    gates[t * k + lane] = (float)(ex / z);
+  }
+}
+
+hipError_t launch_select(const double* part, const RouterPlan& p, const float* bias, int T, int E, int k,
+                         float* logits, int* idx, float* gates, hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(T), dim3(256), 0, st, part, p.S, p.ps, p.pt, p.pe, bias, T, E, k,
+                     logits, idx, gates);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- dispatch
+
+// One workgroup (1024 threads): a stable counting sort of the T*k pairs by
+// expert.  Per-expert token bitmasks give each pair its rank among the pairs
+// of its expert (pairs of one expert are ordered by token, and a token
+// selects an expert at most once); exclusive scans give the offsets and the
+// list of active experts in ascending order.
+__global__ __launch_bounds__(1024) void k_dispatch(const int* __restrict__ idx, int T, int E, int k, DispOut d) {
   __shared__ uint32_t mask[256][4];
-  __shared__ int sel[128 * 8];
   __shared__ int cnt[256], poff[256], apos[256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 256 * 4; i += 1024) (&mask[0][0])[i] = 0u;
   __syncthreads();
-
-  for (int t = wave; t < T; t += 16) {
-    uint64_t key[4];
-    float lv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      key[i] = 0;
-      lv[i] = 0.f;
-      if (e < E) {
-        double a = 0.0;
-        for (int s = 0; s < S; ++s) a += part[((int64_t)t * E + e) * S + s];
-        if (bias) a += (double)bias[e];
-        const float l = (float)a;
-        if (logits) logits[(int64_t)t * E + e] = l;
-        lv[i] = l;
-        key[i] = ((uint64_t)order_key(l) << 32) | (uint32_t)(~(uint32_t)e);
-      }
-    }
-    float sl[8];
-    int se[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      uint64_t best = key[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(~(uint32_t)best);
-      se[j] = e;
-      // the owner lane retires the winner and publishes its logit
-      float l = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == e) { key[i] = 0; l = lv[i]; }
-      sl[j] = __shfl(l, e & 63, 64);
-    }
-    if (lane == 0) {
-      const double m = (double)sl[0];
-      double z = 0.0, ex[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < k) { ex[j] = exp((double)sl[j] - m); z += ex[j]; }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < k) {
-          idx[t * k + j] = se[j];
-          gates[t * k + j] = (float)(ex[j] / z);
-          sel[t * k + j] = se[j];
-        }
-      }
-    }
-    if (do_disp && lane < k) {
-      int e = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j == lane) e = se[j];
-      atomicOr(&mask[e][t >> 5], 1u << (t & 31));
-    }
+  for (int p = threadIdx.x; p < T * k; p += 1024) {
+    const int t = p / k;
+    atomicOr(&mask[idx[p]][t >> 5], 1u << (t & 31));
   }
-  if (!do_disp) return;
   __syncthreads();
-  // per-expert pair counts, active flags; exclusive scans by wave 0
   if (threadIdx.x < 256) {
     const int e = threadIdx.x;
     cnt[e] = e < E ? __popc(mask[e][0]) + __popc(mask[e][1]) + __popc(mask[e][2]) + __popc(mask[e][3]) : 0;
@@ -141,7 +270,7 @@ __global__ __launch_bounds__(1024) void k_route_finalize(const double* __restric
     d.active_off[apos[e]] = poff[e];
   }
   for (int p = threadIdx.x; p < T * k; p += 1024) {
-    const int t = p / k, e = sel[p];
+    const int t = p / k, e = idx[p];
     int rank = 0;
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(mask[e][w]);
     rank += __popc(mask[e][t >> 5] & ((1u << (t & 31)) - 1u));
@@ -151,11 +280,8 @@ __global__ __launch_bounds__(1024) void k_route_finalize(const double* __restric
   }
 }
 
-hipError_t launch_route_finalize(const double* part, int S, const float* bias, int T, int E, int k, float* logits,
-                                 int* idx, float* gates, const DispOut* d, hipStream_t st) {
-  DispOut dd = d ? *d : DispOut{nullptr, nullptr, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(k_route_finalize, dim3(1), dim3(1024), 0, st, part, S, bias, T, E, k, logits, idx, gates, dd,
-                     d ? 1 : 0);
+hipError_t launch_dispatch(const int* idx, int T, int E, int k, const DispOut& d, hipStream_t st) {
+  hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(1024), 0, st, idx, T, E, k, d);
   return hipGetLastError();
 }
 
