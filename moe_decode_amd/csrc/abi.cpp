@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 
@@ -113,6 +114,7 @@ struct MoeWs {
   size_t x_dig, x_exp, h_dig, h_exp, hs_dig, hs_exp;  // int8 digit planes (per-row formats)
   size_t xs_dig, xs_exp;  // x digits in the shared expert's order
   size_t xd, sxd, hd, shd;  // digit planes of x and h for the one-token kernels (routed, shared formats)
+  size_t fo, fctr;          // fused kernel: per-pair down outputs, counters
 };
 
 // Few tokens on shapes the one-token kernels cover: independent (token, slot)
@@ -120,6 +122,17 @@ struct MoeWs {
 bool use_pairs(const md_moe_layer* L, int T) {
   return T <= kMaxPairT && md::t1_supported(L->type, L->H, L->F) &&
          (!L->has_shared || md::t1_supported(L->shared.gate.type, L->H, L->shared.gate.rows));
+}
+
+// Few tokens on shapes the fused persistent kernel covers, when MD_FUSED=1 is
+// set in the environment at call time (the separate one-token kernels are the
+// default: they are faster on the shapes measured so far).  The workspace
+// size does not depend on the choice.
+bool use_fused(const md_moe_layer* L) {
+  const char* v = getenv("MD_FUSED");
+  if (!v || v[0] != '1') return false;
+  return md::fused_supported(L->type, L->H, L->F, L->has_shared ? L->shared.gate.type : 0,
+                             L->has_shared ? L->shared.gate.rows : 0, L->has_shared != 0);
 }
 
 MoeWs moe_ws(const md_moe_layer* L, int T) {
@@ -148,6 +161,8 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
       w.sxd = take(dig_buf_bytes(L->shared.gate.type, T, H));
       w.shd = take(dig_buf_bytes(L->shared.gate.type, T, L->shared.gate.rows));
     }
+    w.fo = take(sizeof(float) * (size_t)T * (k + 1) * H);
+    w.fctr = take(sizeof(int) * (size_t)md::fused_counter_words(T, k, H));
   } else {
     w.o = take(sizeof(float) * (size_t)T * k * H);
     w.x_hi = take(2 * (size_t)T * H);
@@ -374,7 +389,7 @@ md_status md_moe_route_topk(const float* x, int32_t T, int32_t H, const float* W
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
   const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(workspace);
-  hipError_t e = md::launch_router(x, T, H, W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
+  hipError_t e = md::launch_router(x, T, H, W_r, E, rp, part, md::DigJob{}, md::DigJob{}, md::ZeroJob{}, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   e = md::launch_select(part, rp, bias, T, E, k, logits, idx, gates, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "select launch");
@@ -492,9 +507,63 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       shd = dig_buf_at(ws + w.shd, sfmt, T, L->shared.gate.rows);
       js = dig_job(x, T, H, sfmt, sxd);
     }
+    const bool fused = use_fused(L);
+    md::ZeroJob zj{};
+    if (fused) zj = md::ZeroJob{static_cast<int*>(P(w.fctr)), md::fused_counter_words(T, k, H)};
     if (!mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
-    e = md::launch_router(x, T, H, L->W_r, E, rp, part, dig_job(x, T, H, fmt, xd), js, stream);
+    e = md::launch_router(x, T, H, L->W_r, E, rp, part, dig_job(x, T, H, fmt, xd), js, zj, stream);
     if (e != hipSuccess) return hip_fail(e, "router launch");
+    if (fused) {
+      // gate/up, down and the combine (and the shared expert) in one kernel
+      if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0) || !mark(MD_STAGE_SHARED, ev1) ||
+          !mark(MD_STAGE_SELECT, ev0) || !mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0))
+        return hip_fail(e, "event record");
+      md::FusedLaunch fl{};
+      fl.fmt = fmt;
+      fl.gq = static_cast<const uint8_t*>(L->gate_q);
+      fl.uq = static_cast<const uint8_t*>(L->up_q);
+      fl.dq = static_cast<const uint8_t*>(L->down_q);
+      fl.gs = row_type(fmt) ? L->gate_scale : nullptr;
+      fl.us = row_type(fmt) ? L->up_scale : nullptr;
+      fl.ds = row_type(fmt) ? L->down_scale : nullptr;
+      fl.gu_bytes = gu_bytes;
+      fl.dn_bytes = dn_bytes;
+      fl.F = F;
+      fl.act = L->act;
+      fl.xd = xd.planes;
+      fl.xsc = xd.scales;
+      fl.hd = hd.planes;
+      fl.hsc = hd.scales;
+      if (L->has_shared) {
+        const md_ffn& sf = L->shared;
+        fl.sfmt = sf.gate.type;
+        fl.sgq = static_cast<const uint8_t*>(sf.gate.q);
+        fl.suq = static_cast<const uint8_t*>(sf.up.q);
+        fl.sdq = static_cast<const uint8_t*>(sf.down.q);
+        fl.sgs = row_type(sf.gate.type) ? sf.gate.row_scale : nullptr;
+        fl.sus = row_type(sf.gate.type) ? sf.up.row_scale : nullptr;
+        fl.sds = row_type(sf.gate.type) ? sf.down.row_scale : nullptr;
+        fl.Fs = sf.gate.rows;
+        fl.sact = sf.act;
+        fl.sxd = sxd.planes;
+        fl.sxsc = sxd.scales;
+        fl.shd = shd.planes;
+        fl.shsc = shd.scales;
+      }
+      fl.H = H; fl.E = E; fl.k = k; fl.T = T;
+      fl.part = part; fl.S = rp.S; fl.bias = L->router_bias;
+      fl.o = static_cast<float*>(P(w.fo));
+      fl.y = y;
+      fl.idx_out = idx;
+      fl.gates_out = gates;
+      fl.ctr = static_cast<int*>(P(w.fctr));
+      e = md::launch_moe_fused(fl, stream);
+      if (e != hipSuccess) return hip_fail(e, "fused launch");
+      if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0) || !mark(MD_STAGE_DOWN, ev1) ||
+          !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
+        return hip_fail(e, "event record");
+      return ok();
+    }
     if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
     if (L->has_shared) {
       s = run_ffn(&L->shared, x, T, &sxd, sxd, shd, static_cast<float*>(P(w.h_s)), y_s, stream);
@@ -555,7 +624,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
   const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(P(w.part));
-  e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
+  e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, md::ZeroJob{}, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");
 

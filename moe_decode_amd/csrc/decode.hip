@@ -28,112 +28,17 @@
 #include "common.hpp"
 #include "digits.hpp"
 #include "kernels.hpp"
+#include "rows.hpp"
 
 namespace md {
 
-#ifndef MD_GU_WINDOW
-#define MD_GU_WINDOW 2
-#endif
-#ifndef MD_DN_WINDOW
-#define MD_DN_WINDOW 8
+#ifndef MD_GU_MAXNP
+#define MD_GU_MAXNP 8
 #endif
 #ifndef MD_DN_ROWS
 #define MD_DN_ROWS 8
 #endif
-#ifndef MD_GU_MAXNP
-#define MD_GU_MAXNP 8
-#endif
 constexpr int kNRW = MD_DN_ROWS;   // output rows per workgroup in k_down_t1
-
-// Sum over the L lanes of a group for N rows at once.  On return lane t holds
-// the full sum of row (t / (L/N)) % N.
-template <int N, int L>
-MD_DEV float butterfly(float (&v)[N], int t) {
-  static_assert(N <= L, "more rows than lanes");
-#pragma unroll
-  for (int s = 0; (N >> s) > 1; ++s) {
-    const int n = N >> s, half = n / 2, off = L >> (s + 1);
-    const bool up = (t & off) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = up ? v[i] : v[i + half];
-      const float keep = up ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, off, 64);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int off = L / (2 * N); off > 0; off >>= 1) r += __shfl_xor(r, off, 64);
-  return r;
-}
-
-template <int FMT, int CPL>
-struct RowBuf {
-  u32x4 w[CPL];
-  float s[CPL];
-};
-
-template <int FMT, int L, int CPL>
-MD_DEV void load_row(RowBuf<FMT, CPL>& b, const uint8_t* row, int K, int c0) {
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) b.w[i] = ld_stream(row + 16 * (int64_t)(c0 + L * i));
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) b.s[i] = dig_block_scale<FMT>(row, K, c0 + L * i);
-}
-
-// Activation digit planes of the CPL chunks a lane owns.
-template <int FMT, int CPL>
-struct ActDig {
-  u32x4 d[CPL][Dig<FMT>::NPL];
-  float sc[CPL];
-};
-
-template <int FMT, int L, int CPL>
-MD_DEV void load_act(ActDig<FMT, CPL>& x, const u32x4* planes, const float* scales, int c0) {
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-#pragma unroll
-    for (int j = 0; j < Dig<FMT>::NPL; ++j) x.d[i][j] = planes[(int64_t)(c0 + L * i) * Dig<FMT>::NPL + j];
-    x.sc[i] = scales[c0 + L * i];
-  }
-}
-
-template <int FMT, int CPL>
-MD_DEV float row_dot(const RowBuf<FMT, CPL>& b, const ActDig<FMT, CPL>& x) {
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const float v = dig_chunk<FMT>(b.w[i], x.d[i], x.sc[i]);
-    acc = Fmt<FMT>::ROW ? acc + v : fmaf(b.s[i], v, acc);
-  }
-  return acc;
-}
-
-// Digit planes of n values held one per thread (thread q: value q; n a
-// multiple of NV and at most blockDim.x): group g's planes go to
-// planes[g * NPL .. ] and its scale to scales[g].  ys: LDS scratch of n words.
-// Every thread of the block must call it (it synchronises).
-template <int FMT>
-MD_DEV void dig_block(float v, int n, uint32_t* ys, u32x4* planes, float* scales) {
-  using D = Dig<FMT>;
-  const int q = threadIdx.x;
-  float m = q < n ? fabsf(v) : 0.f;
-#pragma unroll
-  for (int off = D::NV / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  const int s = dig_shift<FMT>(m);
-  if (q < n) {
-    ys[q] = dig_biased<FMT>(v, s);
-    if (q % D::NV == 0) scales[q / D::NV] = ldexpf(1.0f, -s);
-  }
-  __syncthreads();
-  uint32_t* out = reinterpret_cast<uint32_t*>(planes);
-  const int nw = n / D::NV * D::NPL * 4;
-  for (int i = q; i < nw; i += blockDim.x) {
-    const int g = i / (D::NPL * 4), w = i % (D::NPL * 4);
-    out[i] = dig_word<FMT>(w / 4, w % 4, [&](int p) { return ys[g * D::NV + p]; });
-  }
-  __syncthreads();
-}
 
 // The digit planes of rows [0, R) of a row-major R x K fp32 matrix (K a
 // multiple of 256), 256 values per block iteration; grid-stride over blocks.
@@ -172,9 +77,11 @@ hipError_t launch_digits(const DigJob& j, hipStream_t st) {
 // S partials in order, then the bias, and rounds once to fp32.
 __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr, int E, int S,
-                                                     double* __restrict__ part, DigJob j0, DigJob j1) {
+                                                     double* __restrict__ part, DigJob j0, DigJob j1, ZeroJob z) {
   __shared__ double red[4][4];
   __shared__ uint32_t ys[256];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < z.n; i += blockDim.x) z.p[i] = 0;
   // the activations' digit planes for the expert kernels (independent of the routing)
   dig_rows(j0, ys);
   dig_rows(j1, ys);
@@ -235,67 +142,9 @@ int router_splits(int H, int E) {
 }
 
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
-                              const DigJob& j0, const DigJob& j1, hipStream_t st) {
-  hipLaunchKernelGGL(k_router_part, dim3(E * S), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1);
+                              const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st) {
+  hipLaunchKernelGGL(k_router_part, dim3(E * S), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1, z);
   return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ top-k
-
-MD_DEV uint32_t order_key32(float l) {
-  uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Wave-level top-k of one token's E logits (E <= 256).  All lanes return the
-// same k experts in selection order and, when asked, their gates.
-MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __restrict__ bias, int E, int k, int lane,
-                      int (&sel)[8], float (&gts)[8], bool want_gates) {
-  uint64_t key[4];
-  float lv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = 0;
-    lv[i] = 0.f;
-    if (e < E) {
-      double a = 0.0;
-      for (int s = 0; s < S; ++s) a += part[(int64_t)e * S + s];
-      if (bias) a += (double)bias[e];
-      lv[i] = (float)a;
-      key[i] = ((uint64_t)order_key32(lv[i]) << 32) | (uint32_t)(~(uint32_t)e);
-    }
-  }
-  float sl[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint64_t o = __shfl_xor(best, off, 64);
-      best = o > best ? o : best;
-    }
-    const int e = (int)(~(uint32_t)best);
-    float l = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == e) { key[i] = 0; l = lv[i]; }
-    sl[j] = __shfl(l, e & 63, 64);
-    sel[j] = e;
-  }
-  if (want_gates) {
-    const double m = (double)sl[0];
-    double ex[8], z = 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) { ex[j] = exp((double)sl[j] - m); z += ex[j]; }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k) gts[j] = (float)(ex[j] / z);
-  }
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -324,23 +173,19 @@ struct GateUpT1 {
 // in LDS.  blockIdx.y = t * slots + j: token t's slot j (each pair of a
 // several-token call is an independent one-token problem).  The block's rows
 // are whole digit groups of h, whose planes it writes for the down kernel.
+// At least 6 waves per SIMD (<= 80 VGPRs): two 12-wave workgroups per CU.
 template <int FMT, int L, int kNP>
-__global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_gateup_t1(GateUpT1 a) {
   using D = Dig<FMT>;
   constexpr int G = 64 / L;
   extern __shared__ float lds[];  // [npairs] h values, then [RGW][G][kNP][KS][2] slice sums
   __shared__ int s_sel[8];
   __shared__ uint32_t ys[256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane / L, t = lane % L;
-  const int ks = wave % a.KS, rg = wave / a.KS;
-  const int c0 = ks * L + t;  // this lane's chunk (one chunk per lane per slice)
   const int slots = a.part ? a.k : 1;
   const int tok = blockIdx.y / slots, slot = blockIdx.y % slots;
   const int npairs = a.RGW * G * kNP;
-  ActDig<FMT, 1> xa;
   const int ngx = a.H / D::NV;
-  load_act<FMT, L, 1>(xa, a.xd + (int64_t)tok * ngx * D::NPL, a.xsc + (int64_t)tok * ngx, c0);
 
   int e = 0;
   if (a.part) {
@@ -363,67 +208,12 @@ __global__ __launch_bounds__(1024) void k_gateup_t1(GateUpT1 a) {
     e = s_sel[slot];
   }
 
-  const int f0 = blockIdx.x * npairs;
-  const int fb = f0 + ((rg * G + g) * kNP);
-  const int64_t rb = row_bytes(FMT, a.H);
-  const uint8_t* Gm = a.gq + (int64_t)e * a.mat_bytes;
-  const uint8_t* Um = a.uq + (int64_t)e * a.mat_bytes;
-  float pg[kNP], pu[kNP];
-  {
-    // rolling window: kD row pairs in flight while one pair is decoded
-    constexpr int kD = kNP < MD_GU_WINDOW ? kNP : MD_GU_WINDOW;
-    RowBuf<FMT, 1> bg[kD], bu[kD];
-    auto rowp = [&](const uint8_t* M, int p) { return M + (int64_t)min(fb + p, a.F - 1) * rb; };
-#pragma unroll
-    for (int p = 0; p < kD; ++p) {
-      load_row<FMT, L, 1>(bg[p], rowp(Gm, p), a.H, c0);
-      load_row<FMT, L, 1>(bu[p], rowp(Um, p), a.H, c0);
-    }
-#pragma unroll
-    for (int p = 0; p < kNP; ++p) {
-      pg[p] = row_dot<FMT, 1>(bg[p % kD], xa);
-      pu[p] = row_dot<FMT, 1>(bu[p % kD], xa);
-      if (p + kD < kNP) {
-        load_row<FMT, L, 1>(bg[p % kD], rowp(Gm, p + kD), a.H, c0);
-        load_row<FMT, L, 1>(bu[p % kD], rowp(Um, p + kD), a.H, c0);
-      }
-    }
-  }
-  const float sa = butterfly<kNP, L>(pg, t);
-  const float su = butterfly<kNP, L>(pu, t);
-  const int r = (t / (L / kNP)) % kNP;
-  const bool writer = (t % (L / kNP)) == 0;
-  float* hv = lds;
-  auto finish = [&](int q, float av, float uv) {
-    const int f = f0 + q;
-    float sg = 1.f, sv = 1.f;
-    if constexpr (Fmt<FMT>::ROW) {
-      if (f < a.F) {
-        sg = a.gs[(int64_t)e * a.F + f];
-        sv = a.us[(int64_t)e * a.F + f];
-      }
-    }
-    hv[q] = f < a.F ? act_f(a.act, av * sg) * (uv * sv) : 0.f;
-  };
-  if (a.KS == 1) {
-    if (writer) finish((rg * G + g) * kNP + r, sa, su);
-  } else {
-    float* red = lds + npairs + ((((rg * G + g) * kNP + r) * a.KS + ks) * 2);
-    if (writer) { red[0] = sa; red[1] = su; }
-    __syncthreads();
-    for (int q = threadIdx.x; q < npairs; q += blockDim.x) {
-      const float* rq = lds + npairs + (int64_t)q * a.KS * 2;
-      float av = 0.f, uv = 0.f;
-      for (int s = 0; s < a.KS; ++s) { av += rq[2 * s]; uv += rq[2 * s + 1]; }
-      finish(q, av, uv);
-    }
-  }
-  __syncthreads();
-  // digit planes of the block's h values (rows past F form whole groups and are skipped)
-  const int n = min(npairs, a.F - f0);
   const int ngh = a.F / D::NV;
-  const int64_t g0 = (int64_t)blockIdx.y * ngh + f0 / D::NV;
-  dig_block<FMT>(threadIdx.x < npairs ? hv[threadIdx.x] : 0.f, n, ys, a.hd + g0 * D::NPL, a.hsc + g0);
+  GuTile u{a.gq + (int64_t)e * a.mat_bytes, a.uq + (int64_t)e * a.mat_bytes,
+           Fmt<FMT>::ROW ? a.gs + (int64_t)e * a.F : nullptr, Fmt<FMT>::ROW ? a.us + (int64_t)e * a.F : nullptr,
+           a.F, a.H, a.act, a.KS, a.RGW, a.xd + (int64_t)tok * ngx * D::NPL, a.xsc + (int64_t)tok * ngx,
+           a.hd + (int64_t)blockIdx.y * ngh * D::NPL, a.hsc + (int64_t)blockIdx.y * ngh};
+  gu_tile<FMT, L, kNP>(u, blockIdx.x * npairs, lds, ys);
 }
 
 // ------------------------------------------------------------------ down
@@ -446,41 +236,13 @@ struct DownT1 {
 template <int FMT, int L, int CPL>
 __global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
   using D = Dig<FMT>;
-  constexpr int G = 64 / L, NR = kNRW / G;
   __shared__ float red[8][kNRW];
-  static_assert(kNRW % G == 0, "rows per block");
-  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
-  const int g = lane / L, t = lane % L;
+  const int j = threadIdx.x >> 6;
   const int tok = blockIdx.y, p = tok * a.k + j;
   const int e = a.idx ? a.idx[p] : 0;
-  ActDig<FMT, CPL> ha;
   const int ngh = a.F / D::NV;
-  load_act<FMT, L, CPL>(ha, a.hd + (int64_t)p * ngh * D::NPL, a.hsc + (int64_t)p * ngh, t);
-  const int ib = blockIdx.x * kNRW + g * NR;
-  const int64_t rb = row_bytes(FMT, a.F);
-  const uint8_t* Dm = a.dq + (int64_t)e * a.mat_bytes;
-  float part[NR];
-  {
-    // rolling window: kD rows in flight while one row is decoded
-    constexpr int kD = NR < MD_DN_WINDOW ? NR : MD_DN_WINDOW;
-    RowBuf<FMT, CPL> b[kD];
-    auto rowp = [&](int r) { return Dm + (int64_t)min(ib + r, a.H - 1) * rb; };
-#pragma unroll
-    for (int r = 0; r < kD; ++r) load_row<FMT, L, CPL>(b[r], rowp(r), a.F, t);
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      part[r] = row_dot<FMT, CPL>(b[r % kD], ha);
-      if (r + kD < NR) load_row<FMT, L, CPL>(b[r % kD], rowp(r + kD), a.F, t);
-    }
-  }
-  const float s = butterfly<NR, L>(part, t);
-  const int r = (t / (L / NR)) % NR;
-  if ((t % (L / NR)) == 0) {
-    const int i = ib + r;
-    float v = s;
-    if constexpr (Fmt<FMT>::ROW) v *= a.ds[(int64_t)e * a.H + min(i, a.H - 1)];
-    red[j][g * NR + r] = v;
-  }
+  dn_rows<FMT, L, CPL, kNRW>(a.dq + (int64_t)e * a.mat_bytes, Fmt<FMT>::ROW ? a.ds + (int64_t)e * a.H : nullptr, a.H, a.F,
+                             a.hd + (int64_t)p * ngh * D::NPL, a.hsc + (int64_t)p * ngh, blockIdx.x * kNRW, red[j]);
   __syncthreads();
   if (threadIdx.x < kNRW) {
     const int i = blockIdx.x * kNRW + threadIdx.x;

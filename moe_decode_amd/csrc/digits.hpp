@@ -90,34 +90,57 @@ MD_DEV void dig_group(const float* v, uint32_t* planes, float* scale) {
   *scale = ldexpf(1.0f, -s);
 }
 
+// Running plane sums of one lane: the integer dot instructions accumulate
+// into a[] without being cleared between chunks, and a chunk's value is the
+// difference of the combined sums before and after it (lo, hi hold the last
+// combination).  All of it is exact two's-complement arithmetic: a sum that
+// wraps still gives the right difference, since each chunk's own combination
+// fits easily in 32 bits.
+template <int FMT>
+struct DigAcc {
+  int a[Dig<FMT>::NPL];
+  int lo, hi;
+  MD_DEV DigAcc() : lo(0), hi(0) {
+#pragma unroll
+    for (int j = 0; j < Dig<FMT>::NPL; ++j) a[j] = 0;
+  }
+};
+
 // Value of one chunk: w = the chunk's 4 weight words, d = its group's planes,
 // sc = 2^-s.  Returns sum_i w_i x_i (before the weights' block or row scale).
 template <int FMT>
-MD_DEV float dig_chunk(u32x4 w, const u32x4* d, float sc) {
+MD_DEV float dig_chunk(u32x4 w, const u32x4* d, float sc, DigAcc<FMT>& r) {
   using D = Dig<FMT>;
   if constexpr (FMT == Q4_0) w ^= u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};  // n - 8
-  int acc[D::NPL];
 #pragma unroll
   for (int j = 0; j < D::NPL; ++j) {
-    int a = 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       if constexpr (D::SH == 4)
-        a = __builtin_amdgcn_sdot8((int)w[m], (int)d[j][m], a, false);
+        r.a[j] = __builtin_amdgcn_sdot8((int)w[m], (int)d[j][m], r.a[j], false);
       else
-        a = __builtin_amdgcn_sdot4((int)w[m], (int)d[j][m], a, false);
+        r.a[j] = __builtin_amdgcn_sdot4((int)w[m], (int)d[j][m], r.a[j], false);
     }
-    acc[j] = a;
   }
-  int lo, hi;
+  uint32_t lo, hi;  // unsigned: wrap-around is defined
   if constexpr (D::SH == 4) {
-    lo = acc[0] + 16 * (acc[1] + 16 * (acc[2] + 16 * acc[3]));
-    hi = acc[4] + 16 * (acc[5] + 16 * acc[6]);
+    lo = (uint32_t)r.a[0] + 16u * ((uint32_t)r.a[1] + 16u * ((uint32_t)r.a[2] + 16u * (uint32_t)r.a[3]));
+    hi = (uint32_t)r.a[4] + 16u * ((uint32_t)r.a[5] + 16u * (uint32_t)r.a[6]);
   } else {
-    lo = acc[0] + 256 * acc[1];
-    hi = acc[2] + 256 * acc[3];
+    lo = (uint32_t)r.a[0] + 256u * (uint32_t)r.a[1];
+    hi = (uint32_t)r.a[2] + 256u * (uint32_t)r.a[3];
   }
-  return fmaf((float)hi, sc * 65536.0f, (float)lo * sc);
+  const int dlo = (int)(lo - (uint32_t)r.lo), dhi = (int)(hi - (uint32_t)r.hi);
+  r.lo = (int)lo;
+  r.hi = (int)hi;
+  return fmaf((float)dhi, sc * 65536.0f, (float)dlo * sc);
+}
+
+// The same with the plane sums cleared for the chunk (no state carried).
+template <int FMT>
+MD_DEV float dig_chunk(u32x4 w, const u32x4* d, float sc) {
+  DigAcc<FMT> r;
+  return dig_chunk<FMT>(w, d, sc, r);
 }
 
 // Block scale of chunk c for the digit path (no 1/16: nibbles enter as values).

@@ -42,6 +42,12 @@ struct DigJob {
 };
 hipError_t launch_digits(const DigJob& j, hipStream_t st);
 
+// n ints at p set to zero by the router kernel (counters of the fused kernel).
+struct ZeroJob {
+  int* p;
+  int n;
+};
+
 struct GemvCfg {
   int L;        // lanes per row group (8..64)
   int R;        // rows per lane group
@@ -70,10 +76,11 @@ struct RouterPlan {
 RouterPlan router_plan(int T, int H, int E);
 int router_splits(int H, int E);
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
-                              const DigJob& j0, const DigJob& j1, hipStream_t st);
-// Also runs the digit jobs j0, j1 (small-T plan only; the GEMM plan rejects them).
+                              const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st);
+// Also runs the digit jobs j0, j1 and the zero job (small-T plan only; the
+// GEMM plan rejects them).
 hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, const RouterPlan& p, double* part,
-                         const DigJob& j0, const DigJob& j1, hipStream_t st);
+                         const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st);
 hipError_t launch_select(const double* part, const RouterPlan& p, const float* bias, int T, int E, int k,
                          float* logits, int* idx, float* gates, hipStream_t st);
 hipError_t launch_dispatch(const int* idx, int T, int E, int k, const DispOut& d, hipStream_t st);
@@ -88,6 +95,39 @@ hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const
 hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t mat_bytes, int H, int F, int k, int T,
                           const int* idx, const float* gates, const void* hd, const float* hsc, const float* y_add,
                           float* y, hipStream_t st);
+
+// the few-token layer after the router as one persistent kernel (fused.hip)
+struct FusedLaunch {
+  int fmt;                                  // routed experts
+  const uint8_t *gq, *uq, *dq;
+  const float *gs, *us, *ds;                // row scales (per-row formats) or nullptr
+  int64_t gu_bytes, dn_bytes;
+  int F, act;
+  const void* xd;                           // x digit planes / scales (routed format)
+  const float* xsc;
+  void* hd;                                 // h digit planes / scales, [T*k] pairs
+  float* hsc;
+  int sfmt;                                 // shared expert (sgq == nullptr: none)
+  const uint8_t *sgq, *suq, *sdq;
+  const float *sgs, *sus, *sds;
+  int Fs, sact;
+  const void* sxd;
+  const float* sxsc;
+  void* shd;                                // [T] pairs
+  float* shsc;
+  int H, E, k, T;
+  const double* part;                       // router partials [T][E][S]
+  int S;
+  const float* bias;
+  float* o;                                 // [T*k + T][H] scratch
+  float* y;
+  int* idx_out;
+  float* gates_out;
+  int* ctr;                                 // fused_counter_words ints, zero at launch
+};
+bool fused_supported(int fmt, int H, int F, int sfmt, int Fs, bool has_shared);
+int fused_counter_words(int T, int k, int H);
+hipError_t launch_moe_fused(const FusedLaunch& L, hipStream_t st);
 
 // prefill grouped GEMM on the matrix cores (prefill.hip)
 hipError_t launch_split_bf16(const float* x, int64_t n, unsigned short* hi, unsigned short* lo, hipStream_t st);

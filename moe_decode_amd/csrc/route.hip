@@ -9,6 +9,7 @@
 // "Experimental lanes".
 #include "common.hpp"
 #include "kernels.hpp"
+#include "rows.hpp"
 
 namespace md {
 
@@ -120,29 +121,15 @@ RouterPlan router_plan(int T, int H, int E) {
 }
 
 hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, const RouterPlan& p, double* part,
-                         const DigJob& j0, const DigJob& j1, hipStream_t st) {
-  if (!p.gemm) return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, st);
-  if (j0.x || j1.x) return hipErrorInvalidValue;
+                         const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st) {
+  if (!p.gemm) return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, z, st);
+  if (j0.x || j1.x || z.n) return hipErrorInvalidValue;
   const dim3 grid((E + kRG - 1) / kRG, (T + kRG - 1) / kRG, p.S);
   hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, st, x, T, H, Wr, E, H / p.S, part);
   return hipGetLastError();
 }
 
 // -------------------------------------------------------------- select
-
-MD_DEV uint32_t order_key(float l) {
-  uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-MD_DEV uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
 
 // One workgroup per token.  Thread e forms expert e's logit: the S partials
 // added in slice order, then the bias, rounded once to fp32.  Wave 0 then
@@ -183,7 +170,7 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ part,
     lv[i] = 0.f;
     if (ei < E) {
       lv[i] = s_l[ei];
-      key[i] = ((uint64_t)order_key(lv[i]) << 32) | (uint32_t)(~(uint32_t)ei);
+      key[i] = ((uint64_t)order_key32(lv[i]) << 32) | (uint32_t)(~(uint32_t)ei);
     }
   }
   float my_l = 0.f;
@@ -198,7 +185,7 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ part,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lane + 64 * i == w) { key[i] = 0; l = lv[i]; }
-    l = __shfl(l, w & 63, 64);
+    l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), w & 63));
     if (lane == j) { my_l = l; my_e = w; }
   }
   const double m = (double)__shfl(my_l, 0, 64);

@@ -1,0 +1,372 @@
+// rows.hpp -- wave-level building blocks of the one-token kernels (gfx950,
+// wave64): lane-group reductions, 16-byte row streaming against activation
+// digit planes held in registers, digit planes of a workgroup's values, and
+// the single-wave router top-k.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "digits.hpp"
+
+namespace md {
+
+#ifndef MD_GU_WINDOW
+#define MD_GU_WINDOW 2
+#endif
+#ifndef MD_DN_WINDOW
+#define MD_DN_WINDOW 8
+#endif
+#ifndef MD_GU_RUN
+#define MD_GU_RUN 0
+#endif
+
+// Sum over the L lanes of a group for N rows at once.  On return lane t holds
+// the full sum of row (t / (L/N)) % N.
+template <int N, int L>
+MD_DEV float butterfly(float (&v)[N], int t) {
+  static_assert(N <= L, "more rows than lanes");
+#pragma unroll
+  for (int s = 0; (N >> s) > 1; ++s) {
+    const int n = N >> s, half = n / 2, off = L >> (s + 1);
+    // m = all ones on the upper lane of each pair: it sends v[i] and keeps
+    // v[i + half]; the lower lane the other way round.  Bit-field inserts
+    // keep both candidates in registers (a select between array elements
+    // would be turned into a computed index and a chain of compares).
+    const uint32_t m = (t & off) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + half]);
+      const float send = __uint_as_float((a & m) | (b & ~m));
+      const float keep = __uint_as_float((b & m) | (a & ~m));
+      v[i] = keep + __shfl_xor(send, off, 64);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int off = L / (2 * N); off > 0; off >>= 1) r += __shfl_xor(r, off, 64);
+  return r;
+}
+
+template <int FMT, int CPL>
+struct RowBuf {
+  u32x4 w[CPL];
+  float s[CPL];
+};
+
+template <int FMT, int L, int CPL>
+MD_DEV void load_row(RowBuf<FMT, CPL>& b, const uint8_t* row, int K, int c0) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) b.w[i] = ld_stream(row + 16 * (int64_t)(c0 + L * i));
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) b.s[i] = dig_block_scale<FMT>(row, K, c0 + L * i);
+}
+
+// Activation digit planes of the CPL chunks a lane owns.
+template <int FMT, int CPL>
+struct ActDig {
+  u32x4 d[CPL][Dig<FMT>::NPL];
+  float sc[CPL];
+};
+
+// kCoh: the planes were written by another workgroup of the same launch
+// (agent-scope atomic loads, which see the writer's agent-scope stores).
+template <int FMT, int L, int CPL, bool kCoh = false>
+MD_DEV void load_act(ActDig<FMT, CPL>& x, const u32x4* planes, const float* scales, int c0) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+#pragma unroll
+    for (int j = 0; j < Dig<FMT>::NPL; ++j) {
+      const u32x4* p = planes + (int64_t)(c0 + L * i) * Dig<FMT>::NPL + j;
+      if constexpr (kCoh) {
+        const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+        const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        x.d[i][j] = u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+      } else {
+        x.d[i][j] = *p;
+      }
+    }
+    if constexpr (kCoh)
+      x.sc[i] = __hip_atomic_load(scales + c0 + L * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      x.sc[i] = scales[c0 + L * i];
+  }
+}
+
+// kRun: carry the plane sums in r across calls (fewer instructions, more
+// live registers); otherwise each chunk starts from zero.
+template <int FMT, int CPL, bool kRun = true>
+MD_DEV float row_dot(const RowBuf<FMT, CPL>& b, const ActDig<FMT, CPL>& x, DigAcc<FMT>& r) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const float v = kRun ? dig_chunk<FMT>(b.w[i], x.d[i], x.sc[i], r) : dig_chunk<FMT>(b.w[i], x.d[i], x.sc[i]);
+    acc = Fmt<FMT>::ROW ? acc + v : fmaf(b.s[i], v, acc);
+  }
+  return acc;
+}
+
+// Store that another workgroup of the same launch reads (agent scope).
+template <bool kCoh, typename V>
+MD_DEV void put(V* p, V v) {
+  if constexpr (kCoh)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// Digit planes of n values held one per thread (thread q: value q; n a
+// multiple of NV and at most blockDim.x): group g's planes go to
+// planes[g * NPL .. ] and its scale to scales[g].  ys: LDS scratch of n words.
+// Every thread of the block must call it (it synchronises).
+template <int FMT, bool kCoh = false>
+MD_DEV void dig_block(float v, int n, uint32_t* ys, u32x4* planes, float* scales) {
+  using D = Dig<FMT>;
+  const int q = threadIdx.x;
+  float m = q < n ? fabsf(v) : 0.f;
+#pragma unroll
+  for (int off = D::NV / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const int s = dig_shift<FMT>(m);
+  if (q < n) {
+    ys[q] = dig_biased<FMT>(v, s);
+    if (q % D::NV == 0) put<kCoh>(scales + q / D::NV, ldexpf(1.0f, -s));
+  }
+  __syncthreads();
+  uint32_t* out = reinterpret_cast<uint32_t*>(planes);
+  const int nw = n / D::NV * D::NPL * 4;
+  for (int i = q; i < nw; i += blockDim.x) {
+    const int g = i / (D::NPL * 4), w = i % (D::NPL * 4);
+    put<kCoh>(out + i, dig_word<FMT>(w / 4, w % 4, [&](int p) { return ys[g * D::NV + p]; }));
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ top-k
+
+
+// Maximum of a 64-bit value over the wave, returned to every lane (uniform).
+// Lane moves by DPP only: within quads, then mirrored half-rows and rows (each
+// row of 16 lanes then holds its maximum), then the row broadcasts carry it
+// to lane 63, which is read back.
+MD_DEV uint64_t wave_max_u64(uint64_t v) {
+  auto step = [&](auto ctrl, auto row_mask) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, decltype(ctrl)::value,
+                                                                decltype(row_mask)::value, 0xF, false);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, decltype(ctrl)::value,
+                                                                decltype(row_mask)::value, 0xF, false);
+    const uint64_t p = ((uint64_t)phi << 32) | plo;
+    v = p > v ? p : v;
+  };
+  step(std::integral_constant<int, 0xB1>{}, std::integral_constant<int, 0xF>{});   // quad_perm [1,0,3,2]
+  step(std::integral_constant<int, 0x4E>{}, std::integral_constant<int, 0xF>{});   // quad_perm [2,3,0,1]
+  step(std::integral_constant<int, 0x141>{}, std::integral_constant<int, 0xF>{});  // row_half_mirror
+  step(std::integral_constant<int, 0x140>{}, std::integral_constant<int, 0xF>{});  // row_mirror
+  step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast:15 into rows 1, 3
+  step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});  // row_bcast:31 into rows 2, 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+MD_DEV uint32_t order_key32(float l) {
+  uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wave-level top-k of one token's E logits (E <= 256), formed from the S
+// router partials of each expert (added in slice order, plus the bias,
+// rounded once to fp32).  Keys: order-preserving image of the logit in the
+// high word, complemented expert index in the low word, so the largest key is
+// the largest logit and, among exact ties, the lower index.  All lanes return
+// the same k experts in selection order and, when asked, their gates: lane j
+// forms exp(l_j - l_0) in fp64, the sum runs over j in order, gate j = its
+// term / sum, rounded to fp32.
+MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __restrict__ bias, int E, int k, int lane,
+                      int (&sel)[8], float (&gts)[8], bool want_gates) {
+  uint64_t key[4];
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = 0;
+    lv[i] = 0.f;
+    if (e < E) {
+      double a = 0.0;
+      for (int s = 0; s < S; ++s) a += part[(int64_t)e * S + s];
+      if (bias) a += (double)bias[e];
+      lv[i] = (float)a;
+      key[i] = ((uint64_t)order_key32(lv[i]) << 32) | (uint32_t)(~(uint32_t)e);
+    }
+  }
+  float my_l = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    sel[j] = 0;
+    if (j >= k) continue;
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(~(uint32_t)best);
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == e) { key[i] = 0; l = lv[i]; }
+    l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e & 63));
+    if (lane == j) my_l = l;
+    sel[j] = e;
+  }
+  if (want_gates) {
+    const double m = (double)__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(my_l)));
+    const double ex = lane < k ? exp((double)my_l - m) : 0.0;
+    double z = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const uint64_t u = (uint64_t)__double_as_longlong(ex);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, j);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), j);
+      z += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    }
+    const float g = (float)(ex / z);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gts[j] = j < k ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), j)) : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------ tiles
+
+// Gate/up rows of one (token, slot) pair for one workgroup: KS*RGW waves;
+// wave (rg, ks) streams kNP row pairs per lane group over K-slice ks, rows
+// [f0, f0 + RGW*G*kNP).  h = act(gate) * up goes through LDS (lds: the h
+// values, then 2*KS per row of slice sums) and leaves as digit planes of the
+// down matrix's format (the same format).  Waves past KS*RGW only take part
+// in the barriers; every thread of the workgroup must call it.  kCoh: the h
+// planes are read by other workgroups of the same launch.
+struct GuTile {
+  const uint8_t* Gm;      // the expert's gate matrix (device layout)
+  const uint8_t* Um;      // its up matrix
+  const float* gs;        // row scales of gate / up (per-row formats) or nullptr
+  const float* us;
+  int F, H, act, KS, RGW;
+  const u32x4* xd;        // x digit planes of the token (group 0)
+  const float* xsc;
+  u32x4* hd;              // h digit planes of the pair (group 0)
+  float* hsc;
+};
+
+template <int FMT, int L, int kNP, bool kCoh = false>
+MD_DEV void gu_tile(const GuTile& a, int f0, float* lds, uint32_t* ys) {
+  using D = Dig<FMT>;
+  constexpr int G = 64 / L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane / L, t = lane % L;
+  const int ks = wave % a.KS, rg = wave / a.KS;
+  const int npairs = a.RGW * G * kNP;
+  float* hv = lds;
+  float* red = lds + npairs;
+  auto finish = [&](int q, float av, float uv) {
+    const int f = f0 + q;
+    float sg = 1.f, sv = 1.f;
+    if (f < a.F && a.gs) {
+      sg = a.gs[f];
+      sv = a.us[f];
+    }
+    hv[q] = f < a.F ? act_f(a.act, av * sg) * (uv * sv) : 0.f;
+  };
+  if (rg < a.RGW) {
+    const int c0 = ks * L + t;  // this lane's chunk (one chunk per lane per slice)
+    ActDig<FMT, 1> xa;
+    load_act<FMT, L, 1>(xa, a.xd, a.xsc, c0);
+    const int fb = f0 + (rg * G + g) * kNP;
+    const int64_t rb = row_bytes(FMT, a.H);
+    float pg[kNP], pu[kNP];
+    {
+      // rolling window: kD row pairs in flight while one pair is decoded
+      constexpr int kD = kNP < MD_GU_WINDOW ? kNP : MD_GU_WINDOW;
+      RowBuf<FMT, 1> bg[kD], bu[kD];
+      DigAcc<FMT> ra;  // one running state serves the gate and up rows alike
+      auto rowp = [&](const uint8_t* M, int p) { return M + (int64_t)min(fb + p, a.F - 1) * rb; };
+#pragma unroll
+      for (int p = 0; p < kD; ++p) {
+        load_row<FMT, L, 1>(bg[p], rowp(a.Gm, p), a.H, c0);
+        load_row<FMT, L, 1>(bu[p], rowp(a.Um, p), a.H, c0);
+      }
+#pragma unroll
+      for (int p = 0; p < kNP; ++p) {
+        pg[p] = row_dot<FMT, 1, MD_GU_RUN>(bg[p % kD], xa, ra);
+        pu[p] = row_dot<FMT, 1, MD_GU_RUN>(bu[p % kD], xa, ra);
+        if (p + kD < kNP) {
+          load_row<FMT, L, 1>(bg[p % kD], rowp(a.Gm, p + kD), a.H, c0);
+          load_row<FMT, L, 1>(bu[p % kD], rowp(a.Um, p + kD), a.H, c0);
+        }
+      }
+    }
+    const float sa = butterfly<kNP, L>(pg, t);
+    const float su = butterfly<kNP, L>(pu, t);
+    const int r = (t / (L / kNP)) % kNP;
+    if ((t % (L / kNP)) == 0) {
+      const int q = (rg * G + g) * kNP + r;
+      if (a.KS == 1) {
+        finish(q, sa, su);
+      } else {
+        red[(q * a.KS + ks) * 2] = sa;
+        red[(q * a.KS + ks) * 2 + 1] = su;
+      }
+    }
+  }
+  if (a.KS > 1) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < npairs; q += blockDim.x) {
+      const float* rq = red + q * a.KS * 2;
+      float av = 0.f, uv = 0.f;
+      for (int s = 0; s < a.KS; ++s) { av += rq[2 * s]; uv += rq[2 * s + 1]; }
+      finish(q, av, uv);
+    }
+  }
+  __syncthreads();
+  // digit planes of the tile's h values (rows past F form whole groups and are skipped)
+  const int n = min(npairs, a.F - f0);
+  dig_block<FMT, kCoh>(threadIdx.x < npairs ? hv[threadIdx.x] : 0.f, n, ys, a.hd + (int64_t)(f0 / D::NV) * D::NPL,
+                       a.hsc + f0 / D::NV);
+}
+
+// One wave, NRW output rows [i0, i0 + NRW) of a row-major H x F down matrix
+// Dm (lane groups of L lanes, NR = NRW / (64 / L) rows each), against h digit
+// planes (hd, hsc: the pair's group 0).  Writer lanes store row i0 + j's value
+// (times its row scale when ds != nullptr) to out[j]; rows past H are not
+// written.  kCoh: h was written, and out is read, by other workgroups of the
+// same launch.
+template <int FMT, int L, int CPL, int NRW, bool kCoh = false>
+MD_DEV void dn_rows(const uint8_t* Dm, const float* ds, int H, int F, const u32x4* hd, const float* hsc, int i0,
+                    float* out) {
+  constexpr int G = 64 / L, NR = NRW / G;
+  static_assert(NRW % G == 0 && NR <= L, "rows per wave");
+  const int lane = threadIdx.x & 63;
+  const int g = lane / L, t = lane % L;
+  ActDig<FMT, CPL> ha;
+  load_act<FMT, L, CPL, kCoh>(ha, hd, hsc, t);
+  const int ib = i0 + g * NR;
+  const int64_t rb = row_bytes(FMT, F);
+  float part[NR];
+  {
+    // rolling window: kD rows in flight while one row is decoded
+    constexpr int kD = NR < MD_DN_WINDOW ? NR : MD_DN_WINDOW;
+    RowBuf<FMT, CPL> b[kD];
+    DigAcc<FMT> ra;
+    auto rowp = [&](int r) { return Dm + (int64_t)min(ib + r, H - 1) * rb; };
+#pragma unroll
+    for (int r = 0; r < kD; ++r) load_row<FMT, L, CPL>(b[r], rowp(r), F, t);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      part[r] = row_dot<FMT, CPL>(b[r % kD], ha, ra);
+      if (r + kD < NR) load_row<FMT, L, CPL>(b[r % kD], rowp(r + kD), F, t);
+    }
+  }
+  const float s = butterfly<NR, L>(part, t);
+  const int r = (t / (L / NR)) % NR;
+  const int i = ib + r;
+  if ((t % (L / NR)) == 0 && i < H) put<kCoh>(out + g * NR + r, ds ? s * ds[i] : s);
+}
+
+}  // namespace md

@@ -165,3 +165,22 @@ def test_single_expert_gate_one_is_its_ffn():
         yf = md.ffn_forward(ffn, _t(x[t:t + 1]))
         torch.cuda.synchronize()
         assert torch.equal(yf[0], y[t])
+
+
+@pytest.mark.parametrize("key,T", [("c0", 1), ("c3", 1), ("c3", 8), ("c4_i4", 1), ("c4_i4", 4), ("c4_i8", 1)])
+def test_moe_fused_kernel_matches_oracle(orc_mt, key, T, monkeypatch):
+    """The few-token layer through the fused persistent kernel (switched on
+    with MD_FUSED=1) against the oracle, and against the separate kernels'
+    routing."""
+    sp = W.spec(key)
+    x = W.moe_x(sp, T)
+    say(f"[moe fused] {key} T={T}")
+    y, idx, gates = _moe_gpu(key, x)
+    monkeypatch.setenv("MD_FUSED", "1")
+    yf, idf, gf = _moe_gpu(key, x)
+    y_ref, i_ref, g_ref, S = oracle_moe(orc_mt, sp, x)
+    assert np.array_equal(idx, i_ref) and np.array_equal(idf, i_ref)
+    assert np.array_equal(gates, gf)
+    assert np.max(np.abs(gates - g_ref)) <= 1e-6
+    assert_within(y, y_ref, S, f"{key} T={T} separate")
+    assert_within(yf, y_ref, S, f"{key} T={T} fused")
