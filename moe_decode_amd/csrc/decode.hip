@@ -174,7 +174,7 @@ struct GateUpT1 {
 // several-token call is an independent one-token problem).  The block's rows
 // are whole digit groups of h, whose planes it writes for the down kernel.
 // At least 6 waves per SIMD (<= 80 VGPRs): two 12-wave workgroups per CU.
-template <int FMT, int L, int kNP>
+template <int FMT, int L, int kNP, bool kLoop>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_gateup_t1(GateUpT1 a) {
   using D = Dig<FMT>;
   constexpr int G = 64 / L;
@@ -213,7 +213,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
            Fmt<FMT>::ROW ? a.gs + (int64_t)e * a.F : nullptr, Fmt<FMT>::ROW ? a.us + (int64_t)e * a.F : nullptr,
            a.F, a.H, a.act, a.KS, a.RGW, a.xd + (int64_t)tok * ngx * D::NPL, a.xsc + (int64_t)tok * ngx,
            a.hd + (int64_t)blockIdx.y * ngh * D::NPL, a.hsc + (int64_t)blockIdx.y * ngh};
-  gu_tile<FMT, L, kNP>(u, blockIdx.x * npairs, lds, ys);
+  if constexpr (kLoop) {
+    // more row tiles than resident workgroups: each loops over its tiles of
+    // this slot, so the top-k runs once per workgroup
+    const int ntiles = (a.F + npairs - 1) / npairs;
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) gu_tile<FMT, L, kNP>(u, tile * npairs, lds, ys);
+  } else {
+    gu_tile<FMT, L, kNP>(u, blockIdx.x * npairs, lds, ys);
+  }
 }
 
 // ------------------------------------------------------------------ down
@@ -260,6 +267,18 @@ __global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
 }
 
 // ------------------------------------------------------------------ launch
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 static int pow2_div(int n) {
   int L = 64;
@@ -314,12 +333,23 @@ hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const
              static_cast<u32x4*>(hd), hsc, idx_out, gates_out, q.KS, q.RGW};
   const int L = q.L, NP = q.NP;
   const int pairs_per_block = q.RGW * q.G * NP;
-  const dim3 grid((F + pairs_per_block - 1) / pairs_per_block, slots);
+  // row tiles per slot; the grid holds at most what is resident at once, and
+  // each workgroup loops over its tiles (the top-k runs once per workgroup)
+  const int ntiles = (F + pairs_per_block - 1) / pairs_per_block;
   const dim3 block(64 * q.KS * q.RGW);
   const size_t lds = sizeof(float) * (pairs_per_block + (q.KS > 1 ? 2 * q.KS * pairs_per_block : 0));
 #define MD_GU(F_, L_, N_) \
   if (fmt == F_ && L == L_ && NP == N_) { \
-    hipLaunchKernelGGL((k_gateup_t1<F_, L_, N_>), grid, block, lds, st, a); return hipGetLastError(); }
+    static int occ = 0; \
+    if (!occ && (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gateup_t1<F_, L_, N_, true>, block.x, lds) != \
+                 hipSuccess || occ < 1)) occ = 1; \
+    const int per_slot = (int)(((int64_t)device_cus() * occ + slots - 1) / slots); \
+    if (ntiles <= per_slot) { \
+      hipLaunchKernelGGL((k_gateup_t1<F_, L_, N_, false>), dim3(ntiles, slots), block, lds, st, a); \
+    } else { \
+      hipLaunchKernelGGL((k_gateup_t1<F_, L_, N_, true>), dim3(per_slot < 1 ? 1 : per_slot, slots), block, lds, st, a); \
+    } \
+    return hipGetLastError(); }
 #define MD_GUL(F_) MD_GU(F_, 64, 8) MD_GU(F_, 32, 8) MD_GU(F_, 16, 8) MD_GU(F_, 8, 8) \
                    MD_GU(F_, 64, 4) MD_GU(F_, 32, 4) MD_GU(F_, 16, 4) MD_GU(F_, 8, 4) \
                    MD_GU(F_, 64, 2) MD_GU(F_, 32, 2) MD_GU(F_, 16, 2) MD_GU(F_, 8, 2)

@@ -251,18 +251,6 @@ static bool fused_geom(int fmt, int H, int F, FGeom& g) {
   return g.CPLD >= 1 && g.CPLD <= 3;
 }
 
-static int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <class R, class SH>
 static hipError_t launch_cfg(const FusedArgs& a, hipStream_t st) {
   static int per_cu = 0;

@@ -58,6 +58,7 @@ struct GemvCfg {
 };
 
 // ---- launchers (return hipGetLastError() of the launch) -------------------
+int device_cus();  // compute units of the current device (cached)
 hipError_t launch_prepare_layout(int fmt, int rows, int cols, int count, const void* src, void* dst,
                                  hipStream_t st);
 
