@@ -107,7 +107,9 @@ def run_mode(layer, sp, T, steps, warmup, stage="gateup"):
 
 
 def cpu_baseline(sp, budget_s=20.0):
-    """The oracle, as is, on a bounded sample of the same decode workload."""
+    """The oracle, as is, on a bounded sample of the same decode workload:
+    single-token forwards over the seeded token pool (cycled) until about
+    budget_s seconds of oracle time have been spent."""
     import numpy as np
     import oracle
     from synth import workloads as W
@@ -117,27 +119,101 @@ def cpu_baseline(sp, budget_s=20.0):
     rng = np.random.default_rng([sp.index, 777, 1, sp.variant])
     xs = rng.standard_normal((POOL, 1, sp.H)).astype(np.float32)
     Wr, b = W.moe_router(sp)
+    shared = W.moe_shared(sp)
     done, spent = 0, 0.0
     cache = {}
-    for i in range(POOL):
-        idx, _, _, _ = orc.route_topk(xs[i], Wr, b, sp.k)
+    i = 0
+    while spent < budget_s:
+        x = xs[i % POOL]
+        i += 1
+        idx, _, _, _ = orc.route_topk(x, Wr, b, sp.k)
         experts = {}
         for e in np.unique(idx):
             e = int(e)
             if e not in cache:
+                if len(cache) >= 24:
+                    cache.clear()
                 cache[e] = W.moe_expert(sp, e)
             experts[e] = cache[e]
         t = time.perf_counter()
-        orc.moe_forward(sp.H, sp.F, sp.E, sp.k, sp.act, Wr, b, experts, W.moe_shared(sp), xs[i])
+        orc.moe_forward(sp.H, sp.F, sp.E, sp.k, sp.act, Wr, b, experts, shared, x)
         spent += time.perf_counter() - t
         done += 1
-        if len(cache) > 24:
-            cache.clear()
-        if spent >= budget_s:
-            break
     return {"value": done / spent, "unit": "tokens/s", "cores": orc.threads, "kind": "oracle",
-            "sample": f"{done} single-token decode forwards of the same layer (fp64 oracle, OpenMP over rows), "
-                      f"{spent:.1f} s of oracle time"}
+            "sample": f"{done} single-token decode forwards of this layer over a pool of {POOL} seeded tokens "
+                      f"(fp64 oracle, OpenMP over output rows), {spent:.1f} s of oracle time; expert generation "
+                      f"outside the timed part"}
+
+
+def traffic_record(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed PMC
+    summary, if the kernel sources still hash to the ones it was taken with
+    (else None)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
+    h = re.search(r"^source_sha256:\s*([0-9a-f]+)\s*$", text, re.M)
+    if not m or not h or h.group(1) != kernel_source_hash():
+        return None
+    return float(m.group(1))
+
+
+def kernel_source_hash():
+    import hashlib
+    d = os.path.join(ROOT, "moe_decode_amd", "csrc")
+    hs = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            hs.update(name.encode())
+            hs.update(open(os.path.join(d, name), "rb").read())
+    return hs.hexdigest()
+
+
+def run_dense(key, name, batch, steps, warmup):
+    """One dense quantized GEMV of a dense workload.  A call takes a few
+    microseconds of GPU time, less than the Python call path, so `steps`
+    calls are captured in a HIP graph and the graph's replay is timed with
+    HIP events (GPU time per call, without the host)."""
+    import torch
+    import moe_decode_amd as md
+    from synth import workloads as W
+    from synth.device import device_dense, x_tensor
+    sp = W.spec(key)
+    Wd = device_dense(sp, name)
+    x = x_tensor(W.dense_x(sp, Wd.cols, batch))
+    y = torch.empty(batch, Wd.rows, dtype=torch.float32, device="cuda")
+    need = md.qgemv_workspace_size(Wd, batch)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        md.qgemv(Wd, x, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            for _ in range(steps):
+                md.qgemv(Wd, x, y=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s_)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    reps = 5
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (reps * steps)
+    nbytes = Wd.nbytes
+    return {"matrix": f"{name} {Wd.rows}x{Wd.cols} {sp.fmt}", "batch": batch, "ms_per_call": ms,
+            "timing": "HIP graph of the calls, replayed", "weight_bytes": nbytes,
+            "weight_GBps": nbytes / (ms / 1e3) / 1e9}
 
 
 def copy_calibration(nbytes=1 << 30):
@@ -206,6 +282,12 @@ def main():
             log(f"[bench] {sp.key} T={Tm}: {m['ms_per_step'] * 1e3:.1f} us/step")
         del layer
         torch.cuda.empty_cache()
+        for key, name, batch in (("c1", "gate", 1), ("c1", "down", 1), ("c1", "q", 1), ("c1", "k", 1),
+                                 ("c2", "w_10240x2560", 1), ("c2", "w_10240x2560", 8),
+                                 ("c2", "w_2560x10240", 1), ("c2", "w_2560x10240", 8)):
+            m = run_dense(key, name, batch, max(20, args.steps), 10)
+            modes[f"{key}_{name}_b{batch}"] = m
+            log(f"[bench] {key} {name} batch {batch}: {m['ms_per_call'] * 1e3:.1f} us ({m['weight_GBps']:.0f} GB/s)")
         for key, Ts in (("c4_i8", (1, 4, 128)), ("c3", (1, 128))):
             s2 = W.spec(key)
             l2 = device_moe(s2)
@@ -222,6 +304,9 @@ def main():
         log(f"[bench] oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
 
     achieved = r["stage_bytes_avg"] / (r["stage_ms_avg"] / 1e3) / 1e9
+    kernel = "k_gateup_t1" if T <= 8 else ("k_moe_mfma_i8" if sp.fmt.endswith("_row") else "k_moe_mfma")
+    workload_tag = f"{sp.key}_T{T}"
+    traffic = traffic_record(kernel, workload_tag)
     out = {
         "metric": METRIC,
         "value": r["tokens_per_s"],
@@ -233,25 +318,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i32+f32",
         "data": "synthetic",
         "config": {
             "workload": f"{sp.key}: MoE layer {'decode' if T == 1 else 'forward'}, {T} token(s)/step, {sp.E} experts "
                         f"top-{sp.k}, hidden {sp.H}, expert FFN {sp.F}, {sp.fmt} weights (GeGLU), whole expert set "
                         f"resident in HBM",
             "tokens_per_step": T,
+            "arithmetic": "integer dot products of weight codes with activation digit planes, exact int32 sums, "
+                          "fp32 combine and accumulation" if T <= 8 else "matrix-core products, fp32 accumulation",
             "weight_bytes_per_step": r["weight_bytes_per_step"],
             "weight_GBps": r["weight_GBps"],
             "weight_frac_of_8TBps": r["weight_GBps"] / HBM_PEAK_GBS,
         },
         "roofline": {
-            "kernel": "k_gateup (selected experts' gate+up GEMV with fused GeGLU)",
+            "kernel": kernel + " (the selected experts' gate and up projections with the fused activation)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": r["stage_bytes_avg"],
             "avg_launch_ms": r["stage_ms_avg"],
         },

@@ -147,6 +147,13 @@ def prepare_layout(type_, rows, cols, count, src, dst, stream=None):
     _check(lib().md_prepare_layout(TYPES.get(type_, type_), rows, cols, count, _ptr(src), _ptr(dst), _stream(stream)))
 
 
+def qgemv_workspace_size(W, batch):
+    d = W.desc()
+    need = ctypes.c_size_t(0)
+    _check(lib().md_qgemv_workspace_size(ctypes.byref(d), batch, ctypes.byref(need)))
+    return need.value
+
+
 def qgemv(W, x, y=None, workspace=None, stream=None):
     """y[b] = W x[b]; x (batch x cols) fp32 or bf16 tensor on the GPU."""
     import torch

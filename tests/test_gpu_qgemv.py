@@ -150,3 +150,34 @@ def test_dense_swiglu_ffn_chunk(orc_mt, T):
     y = md.ffn_forward(ffn, torch.from_numpy(x).cuda())
     torch.cuda.synchronize()
     assert_within(y.cpu().numpy(), y_ref, S, f"c1 SwiGLU FFN T={T}")
+
+
+def test_qgemv_graph_replays_match_eager():
+    """qgemv calls captured in a HIP graph (the plain kernel and the split-K
+    kernel with its reduce), replayed several times with eager work and
+    synchronisations in between: every replay equals the eager result."""
+    import moe_decode_amd as md
+    import torch
+    from synth.device import x_tensor
+    sp = W.spec("c1")
+    mats = [dense_matrix("c1", "gate"), dense_matrix("c1", "k")]
+    xs = [x_tensor(W.dense_x(sp, m.cols, 1, salt=3)) for m in mats]
+    wss = [torch.empty(max(md.qgemv_workspace_size(m, 1), 1), dtype=torch.uint8, device="cuda") for m in mats]
+    eager = [md.qgemv(m, x, workspace=w).clone() for m, x, w in zip(mats, xs, wss)]
+    ys = [torch.zeros_like(e) for e in eager]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for m, x, y, w in zip(mats, xs, ys, wss):
+                md.qgemv(m, x, y=y, workspace=w)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        for y in ys:
+            y.fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y, e), f"replay {rep}"
