@@ -417,13 +417,18 @@ MD_DEV i32x4 decode_a8(const uint8_t* p) {
   }
 }
 
-template <int FMT, int GU>
+// RT: 16-row MFMA tiles per wave; each digit-plane fragment read from LDS
+// feeds RT products (the block covers 64*RT rows: for gate/up 32*RT gate rows
+// and the same up rows).
+template <int FMT, int GU, int RT>
 __global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
   using TL = Tile<FMT>;
   constexpr int KB = TL::B8 ? 16 : 8;  // weight bytes per lane per 64-wide step
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kRows * TL::WSTR];
+  constexpr int BR = 64 * RT;          // weight rows per block
+  constexpr int WCH = BR * TL::WB / 16, WPT = WCH / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BR * TL::WSTR];
   __shared__ __attribute__((aligned(16))) int8_t s_d[2][4 * kTok * kLST];
-  __shared__ float s_up[32][kTok];
+  __shared__ float s_up[BR / 2][kTok];
   __shared__ int s_e[kTok];
 
   struct { int e, p0, p1; } er;
@@ -443,11 +448,11 @@ __global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
   const int q = lane >> 4, li = lane & 15;
   const int64_t rb = row_bytes(FMT, a.K);
   const int nkt = a.K / kKT;
-  const int r0 = GU ? blockIdx.x * 32 : blockIdx.x * kRows;
+  const int r0 = GU ? blockIdx.x * (BR / 2) : blockIdx.x * BR;
   auto row_ptr = [&](int r) -> const uint8_t* {
     if (GU) {
-      const int f = min(r0 + (r & 31), a.M - 1);
-      return (r < 32 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes + (int64_t)f * rb;
+      const int f = min(r0 + (r % (BR / 2)), a.M - 1);
+      return (r < BR / 2 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes + (int64_t)f * rb;
     }
     return a.wq + (int64_t)er.e * a.mat_bytes + (int64_t)min(r0 + r, a.M - 1) * rb;
   };
@@ -460,11 +465,11 @@ __global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
   const int8_t* dsrc = jj < nt ? a.digits + (int64_t)act_row(jj) * 4 * a.K : nullptr;
   if (tid < kTok) s_e[tid] = tid < nt ? a.expo[act_row(tid)] : 0;
 
-  u32x4 rw[2][TL::WPT];
+  u32x4 rw[2][WPT];
   uint4 rd[2][4];
   auto gload = [&](int kt, int set) {
 #pragma unroll
-    for (int i = 0; i < TL::WPT; ++i) {
+    for (int i = 0; i < WPT; ++i) {
       const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
       rw[set][i] = ld_stream(row_ptr(r) + (int64_t)kt * TL::WB + 16 * piece);
     }
@@ -475,7 +480,7 @@ __global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
   };
   auto lstore = [&](int buf, int set) {
 #pragma unroll
-    for (int i = 0; i < TL::WPT; ++i) {
+    for (int i = 0; i < WPT; ++i) {
       const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
       *reinterpret_cast<u32x4*>(&s_w[buf][r * TL::WSTR + 16 * piece]) = rw[set][i];
     }
@@ -483,18 +488,24 @@ __global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
     for (int l = 0; l < 4; ++l)
       *reinterpret_cast<uint4*>(&s_d[buf][(l * kTok + jj) * kLST + 16 * pp]) = rd[set][l];
   };
-  i32x4 acc[4];
+  i32x4 acc[RT][4];
 #pragma unroll
-  for (int l = 0; l < 4; ++l) acc[l] = i32x4{0, 0, 0, 0};
-  const int wr = wave * 16;
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int l = 0; l < 4; ++l) acc[rt][l] = i32x4{0, 0, 0, 0};
+  const int wr = wave * 16 * RT;
   auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < kKT / 64; ++s) {
-      const i32x4 av = decode_a8<FMT>(&s_w[buf][(wr + li) * TL::WSTR + KB * (4 * s + q)]);
+      i32x4 av[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        av[rt] = decode_a8<FMT>(&s_w[buf][(wr + 16 * rt + li) * TL::WSTR + KB * (4 * s + q)]);
 #pragma unroll
       for (int l = 0; l < 4; ++l) {
         const i32x4 bv = *reinterpret_cast<const i32x4*>(&s_d[buf][(l * kTok + li) * kLST + 64 * s + 16 * q]);
-        acc[l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[l], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[rt], bv, acc[rt][l], 0, 0, 0);
       }
     }
   };
@@ -514,29 +525,37 @@ __global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
     __syncthreads();
   }
 
-  // epilogue: lane holds rows wr + 4q + v of token column li
+  // epilogue: lane holds rows wr + 16 rt + 4q + v of token column li
   const int j = li;
   const float ex = ldexpf(1.0f, s_e[j] - 30);
-  float val[4];
+  float val[RT][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    val[v] = (fmaf((float)acc[3][v], 16777216.0f, (float)acc[2][v] * 65536.0f) +
-              fmaf((float)acc[1][v], 256.0f, (float)acc[0][v])) * ex;
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      val[rt][v] = (fmaf((float)acc[rt][3][v], 16777216.0f, (float)acc[rt][2][v] * 65536.0f) +
+                    fmaf((float)acc[rt][1][v], 256.0f, (float)acc[rt][0][v])) * ex;
   if constexpr (GU) {
+    // waves 0, 1: gate rows; waves 2, 3: the same rows of up
     if (wave >= 2) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s_up[wr - 32 + 4 * q + v][j] = val[v];
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s_up[wr - BR / 2 + 16 * rt + 4 * q + v][j] = val[rt][v];
     }
     __syncthreads();
     if (wave < 2 && j < nt) {
       const int pos = t0 + j;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = wr + 4 * q + v, f = r0 + rr;
-        if (f < a.M) {
-          const float av = val[v] * a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
-          const float uv = s_up[rr][j] * a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
-          a.out[(int64_t)pos * a.M + f] = act_f(a.act, av) * uv;
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int rr = wr + 16 * rt + 4 * q + v, f = r0 + rr;
+          if (f < a.M) {
+            const float av = val[rt][v] * a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
+            const float uv = s_up[rr][j] * a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
+            a.out[(int64_t)pos * a.M + f] = act_f(a.act, av) * uv;
+          }
         }
       }
     }
@@ -544,9 +563,13 @@ __global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
     if (j < nt) {
       const int pos = t0 + j;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int i = r0 + wr + 4 * q + v;
-        if (i < a.M) a.out[(int64_t)pos * a.M + i] = val[v] * a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = r0 + wr + 16 * rt + 4 * q + v;
+          if (i < a.M)
+            a.out[(int64_t)pos * a.M + i] = val[rt][v] * a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
+        }
       }
     }
   }
@@ -557,15 +580,18 @@ hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uin
                               int max_active, const int8_t* digits, const int* expo, bool act_by_token, float* out,
                               hipStream_t st) {
   MfmaI8Args a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, digits, expo, act_by_token ? 1 : 0, out};
-  const int rows_per_block = gateup ? 32 : kRows;
+  // int4 weights: two row tiles per wave (LDS reads of the activation digits
+  // per weight byte halve); int8: one (its weight tiles are twice as large)
+  const int RT = fmt == I4_ROW ? 2 : 1;
+  const int rows_per_block = (gateup ? 32 : 64) * RT;
   const int tiles = (d.T + kTok - 1) / kTok;
   const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.n_active ? max_active : 1, tiles);
-#define MD_MF8(F_) \
-  if (fmt == F_) { \
-    if (gateup) hipLaunchKernelGGL((k_moe_mfma_i8<F_, 1>), grid, dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((k_moe_mfma_i8<F_, 0>), grid, dim3(256), 0, st, a); \
+#define MD_MF8(F_, RT_) \
+  if (fmt == F_ && RT == RT_) { \
+    if (gateup) hipLaunchKernelGGL((k_moe_mfma_i8<F_, 1, RT_>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((k_moe_mfma_i8<F_, 0, RT_>), grid, dim3(256), 0, st, a); \
     return hipGetLastError(); }
-  MD_MF8(I8_ROW) MD_MF8(I4_ROW)
+  MD_MF8(I8_ROW, 1) MD_MF8(I4_ROW, 2)
 #undef MD_MF8
   return hipErrorInvalidValue;
 }
