@@ -162,7 +162,9 @@ md_status md_ffn_forward(const md_ffn *f /*host*/, const float *x, int32_t T, fl
  * x, y: device T x H fp32.  idx_out (int32 T x k) and gates_out (fp32 T x k)
  * receive the routing when non-NULL.  Only the selected experts' weight bytes
  * are read; an expert selected by several tokens is read once per call.
- * For T <= 8 the layer runs as router, gate/up and down kernels; with
+ * For T <= 8 the layer runs as router, gate/up and down kernels (a shared
+ * expert runs inside the routed launches where its shapes are covered, else
+ * as its own two launches first); with
  * MD_FUSED=1 in the environment (read at each call) the gate/up, down and
  * combine of the shapes it covers run as one persistent kernel instead (same
  * results up to fp32 summation order; the workspace size is the same). */
@@ -176,9 +178,11 @@ md_status md_moe_layer_forward(const md_moe_layer *L /*host*/, const float *x, i
  * `stage` and `stop` just after them (HIP events created by the caller), so
  * the elapsed time between the two events is that stage's time on the
  * stream.  A stage the call does not run (the shared expert of a layer
- * without one) records both events back to back; so do the stages that the
- * fused persistent kernel covers besides MD_STAGE_GATEUP, which then times
- * that whole kernel. */
+ * without one) records both events back to back; so do the stages that a
+ * merged launch covers besides MD_STAGE_GATEUP, which then times the whole
+ * merged work: the fused persistent kernel, or (few tokens, a layer with a
+ * shared expert on the shapes it covers) the routed+shared gate/up and down
+ * launches. */
 typedef enum md_stage {
     MD_STAGE_SHARED = 0,      /* dense shared-expert FFN                      */
     MD_STAGE_ROUTER = 1,      /* router logits                                */

@@ -564,6 +564,42 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
         return hip_fail(e, "event record");
       return ok();
     }
+    if (L->has_shared && md::rs_supported(fmt, H, F, L->shared.gate.type, L->shared.gate.rows, k, T)) {
+      // the shared expert inside the routed launches
+      if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0) || !mark(MD_STAGE_SHARED, ev1) ||
+          !mark(MD_STAGE_SELECT, ev0) || !mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0))
+        return hip_fail(e, "event record");
+      const md_ffn& sf = L->shared;
+      md::RsLaunch rl{};
+      rl.fmt = fmt;
+      rl.gq = static_cast<const uint8_t*>(L->gate_q);
+      rl.uq = static_cast<const uint8_t*>(L->up_q);
+      rl.dq = static_cast<const uint8_t*>(L->down_q);
+      rl.gs = L->gate_scale;
+      rl.us = L->up_scale;
+      rl.ds = L->down_scale;
+      rl.gu_bytes = gu_bytes;
+      rl.dn_bytes = dn_bytes;
+      rl.F = F; rl.act = L->act; rl.H = H; rl.E = E; rl.k = k; rl.T = T;
+      rl.part = part; rl.S = rp.S; rl.bias = L->router_bias;
+      rl.xd = xd.planes; rl.xsc = xd.scales; rl.hd = hd.planes; rl.hsc = hd.scales;
+      rl.sfmt = sf.gate.type;
+      rl.sgq = static_cast<const uint8_t*>(sf.gate.q);
+      rl.suq = static_cast<const uint8_t*>(sf.up.q);
+      rl.sdq = static_cast<const uint8_t*>(sf.down.q);
+      rl.sgs = row_type(sf.gate.type) ? sf.gate.row_scale : nullptr;
+      rl.sus = row_type(sf.gate.type) ? sf.up.row_scale : nullptr;
+      rl.sds = row_type(sf.gate.type) ? sf.down.row_scale : nullptr;
+      rl.Fs = sf.gate.rows; rl.sact = sf.act;
+      rl.sxd = sxd.planes; rl.sxsc = sxd.scales; rl.shd = shd.planes; rl.shsc = shd.scales;
+      rl.idx = idx; rl.gates = gates; rl.y = y;
+      e = md::launch_moe_rs(rl, stream);
+      if (e != hipSuccess) return hip_fail(e, "routed+shared launch");
+      if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0) || !mark(MD_STAGE_DOWN, ev1) ||
+          !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
+        return hip_fail(e, "event record");
+      return ok();
+    }
     if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
     if (L->has_shared) {
       s = run_ffn(&L->shared, x, T, &sxd, sxd, shd, static_cast<float*>(P(w.h_s)), y_s, stream);

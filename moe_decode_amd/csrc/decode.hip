@@ -266,6 +266,116 @@ __global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
   }
 }
 
+// ------------------------------------------------------------------ routed + shared
+
+// A layer with a shared expert: the shared expert's gate/up tiles run in the
+// routed gate/up launch (its own format and geometry, same workgroup size),
+// and its down rows in the routed down launch as one more wave per workgroup,
+// added after the gated routed rows -- the same order and arithmetic as the
+// separate launches, in two launches fewer.
+struct SharedGU {
+  const uint8_t* gq;
+  const uint8_t* uq;
+  const float* gs;       // row scales (per-row formats) or nullptr
+  const float* us;
+  int F, act, KS, RGW, ntiles;
+  const u32x4* xd;       // x digit planes in the shared expert's format [T][H/NV][NPL]
+  const float* xsc;
+  u32x4* hd;             // its h digit planes [T][F/NV][NPL]
+  float* hsc;
+};
+
+// Blocks [0, T*k*rtiles): routed pair bid / rtiles, row tile bid % rtiles;
+// then T*ntiles shared blocks (token, row tile).
+template <int FMT, int L, int kNP, int SFMT, int SL, int SNP>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_gateup_rs(GateUpT1 a,
+                                                                                             SharedGU sh,
+                                                                                             int rtiles, int T) {
+  extern __shared__ float lds[];
+  __shared__ int s_sel[8];
+  __shared__ uint32_t ys[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nrb = T * a.k * rtiles;
+  const int bid = blockIdx.x;
+  if (bid < nrb) {
+    using D = Dig<FMT>;
+    constexpr int G = 64 / L;
+    const int pair = bid / rtiles, tile = bid % rtiles, tok = pair / a.k, slot = pair % a.k;
+    if (wave == 0) {
+      int sel[8];
+      float gts[8];
+      const bool first = tile == 0 && slot == 0;
+      wave_topk(a.part + (int64_t)tok * a.E * a.S, a.S, a.bias, a.E, a.k, lane, sel, gts, first);
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j < a.k) {
+            s_sel[j] = sel[j];
+            if (first) { a.idx_out[tok * a.k + j] = sel[j]; a.gates_out[tok * a.k + j] = gts[j]; }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int e = s_sel[slot];
+    const int ngx = a.H / D::NV, ngh = a.F / D::NV;
+    const GuTile u{a.gq + (int64_t)e * a.mat_bytes, a.uq + (int64_t)e * a.mat_bytes,
+                   Fmt<FMT>::ROW ? a.gs + (int64_t)e * a.F : nullptr, Fmt<FMT>::ROW ? a.us + (int64_t)e * a.F : nullptr,
+                   a.F, a.H, a.act, a.KS, a.RGW, a.xd + (int64_t)tok * ngx * D::NPL, a.xsc + (int64_t)tok * ngx,
+                   a.hd + (int64_t)pair * ngh * D::NPL, a.hsc + (int64_t)pair * ngh};
+    gu_tile<FMT, L, kNP>(u, tile * (a.RGW * G * kNP), lds, ys);
+  } else {
+    using D = Dig<SFMT>;
+    constexpr int G = 64 / SL;
+    const int r = bid - nrb, tok = r / sh.ntiles, tile = r % sh.ntiles;
+    const int ngx = a.H / D::NV, ngh = sh.F / D::NV;
+    const GuTile u{sh.gq, sh.uq, sh.gs, sh.us, sh.F, a.H, sh.act, sh.KS, sh.RGW,
+                   sh.xd + (int64_t)tok * ngx * D::NPL, sh.xsc + (int64_t)tok * ngx,
+                   sh.hd + (int64_t)tok * ngh * D::NPL, sh.hsc + (int64_t)tok * ngh};
+    gu_tile<SFMT, SL, SNP>(u, tile * (sh.RGW * G * SNP), lds, ys);
+  }
+}
+
+struct SharedDN {
+  const uint8_t* dq;
+  const float* ds;       // row scales (per-row formats) or nullptr
+  int F;
+  const u32x4* hd;       // h digit planes [T][F/NV][NPL]
+  const float* hsc;
+};
+
+// Block = k + 1 waves: wave j < k streams kNRW rows of token t's slot j
+// expert, wave k the same rows of the shared expert (t = blockIdx.y).
+template <int FMT, int L, int CPL, int SFMT, int SL, int SCPL>
+__global__ __launch_bounds__(576) void k_down_rs(DownT1 a, SharedDN sh) {
+  __shared__ float red[9][kNRW];
+  const int j = threadIdx.x >> 6;
+  const int tok = blockIdx.y;
+  if (j < a.k) {
+    using D = Dig<FMT>;
+    const int p = tok * a.k + j, e = a.idx[p];
+    const int ngh = a.F / D::NV;
+    dn_rows<FMT, L, CPL, kNRW>(a.dq + (int64_t)e * a.mat_bytes, Fmt<FMT>::ROW ? a.ds + (int64_t)e * a.H : nullptr,
+                               a.H, a.F, a.hd + (int64_t)p * ngh * D::NPL, a.hsc + (int64_t)p * ngh,
+                               blockIdx.x * kNRW, red[j]);
+  } else {
+    using D = Dig<SFMT>;
+    const int ngh = sh.F / D::NV;
+    dn_rows<SFMT, SL, SCPL, kNRW>(sh.dq, sh.ds, a.H, sh.F, sh.hd + (int64_t)tok * ngh * D::NPL,
+                                  sh.hsc + (int64_t)tok * ngh, blockIdx.x * kNRW, red[a.k]);
+  }
+  __syncthreads();
+  if (threadIdx.x < kNRW) {
+    const int i = blockIdx.x * kNRW + threadIdx.x;
+    if (i < a.H) {
+      float v = 0.f;
+      for (int q = 0; q < a.k; ++q) v = fmaf(a.gates[tok * a.k + q], red[q][threadIdx.x], v);
+      v += red[a.k][threadIdx.x];
+      a.y[(int64_t)tok * a.H + i] = v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launch
 
 int device_cus() {
@@ -376,6 +486,57 @@ hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t m
 #undef MD_DNL
 #undef MD_DN
   return hipErrorInvalidConfiguration;
+}
+
+// ---- routed + shared
+
+// The instantiated shape family: Q4_0 experts (hidden 2048: 64-lane row
+// groups, 8 row pairs; FFN 768: 8-lane groups, 3 chunks per lane) with a Q8_0
+// shared expert (64-lane groups, 8 row pairs; FFN 2048: 64 lanes, 2 chunks).
+struct RsGeom {
+  GuGeom r, s;
+  int Ld, CPLd, Lsd, CPLsd;
+};
+static bool rs_geom(int fmt, int H, int F, int sfmt, int Fs, int k, int T, RsGeom& g) {
+  if (k + 1 > 9) return false;
+  if (!gu_geom(fmt, F, H, T * k, g.r) || !gu_geom(sfmt, Fs, H, T, g.s)) return false;
+  if (g.r.KS * g.r.RGW != g.s.KS * g.s.RGW) return false;   // one workgroup size
+  const int ncd = nchunks(fmt, F), ncs = nchunks(sfmt, Fs);
+  g.Ld = pow2_div(ncd);
+  g.Lsd = pow2_div(ncs);
+  g.CPLd = ncd / g.Ld;
+  g.CPLsd = ncs / g.Lsd;
+  return fmt == Q4_0 && sfmt == Q8_0 && g.r.L == 64 && g.r.NP == 8 && g.s.L == 64 && g.s.NP == 8 && g.Ld == 8 &&
+         g.CPLd == 3 && g.Lsd == 64 && g.CPLsd == 2;
+}
+
+bool rs_supported(int fmt, int H, int F, int sfmt, int Fs, int k, int T) {
+  RsGeom g;
+  return rs_geom(fmt, H, F, sfmt, Fs, k, T, g);
+}
+
+hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st) {
+  RsGeom g;
+  if (!rs_geom(L.fmt, L.H, L.F, L.sfmt, L.Fs, L.k, L.T, g)) return hipErrorInvalidConfiguration;
+  const int rpb = g.r.RGW * g.r.G * g.r.NP, spb = g.s.RGW * g.s.G * g.s.NP;
+  const int rtiles = (L.F + rpb - 1) / rpb, stiles = (L.Fs + spb - 1) / spb;
+  GateUpT1 a{L.gq, L.uq, L.gs, L.us, L.gu_bytes, L.F, L.H, L.act, L.E, L.k, L.part, L.bias, L.S,
+             static_cast<const u32x4*>(L.xd), L.xsc, static_cast<u32x4*>(L.hd), L.hsc, L.idx, L.gates, g.r.KS, g.r.RGW};
+  SharedGU sh{L.sgq, L.suq, L.sgs, L.sus, L.Fs, L.sact, g.s.KS, g.s.RGW, stiles,
+              static_cast<const u32x4*>(L.sxd), L.sxsc, static_cast<u32x4*>(L.shd), L.shsc};
+  const int mx = rpb > spb ? rpb : spb;
+  const int ks = g.r.KS > g.s.KS ? g.r.KS : g.s.KS;
+  const size_t lds = sizeof(float) * (mx + (ks > 1 ? 2 * ks * mx : 0));
+  const int nblk = L.T * L.k * rtiles + L.T * stiles;
+  hipLaunchKernelGGL((k_gateup_rs<Q4_0, 64, 8, Q8_0, 64, 8>), dim3(nblk), dim3(64 * g.r.KS * g.r.RGW), lds, st, a, sh,
+                     rtiles, L.T);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DownT1 d{L.dq, L.ds, L.dn_bytes, L.H, L.F, L.k, L.idx, L.gates, static_cast<const u32x4*>(L.hd), L.hsc, nullptr, L.y};
+  SharedDN sd{L.sdq, L.sds, L.Fs, static_cast<const u32x4*>(L.shd), L.shsc};
+  hipLaunchKernelGGL((k_down_rs<Q4_0, 8, 3, Q8_0, 64, 2>), dim3((L.H + kNRW - 1) / kNRW, L.T), dim3(64 * (L.k + 1)), 0,
+                     st, d, sd);
+  return hipGetLastError();
 }
 
 }  // namespace md

@@ -97,6 +97,36 @@ hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t m
                           const int* idx, const float* gates, const void* hd, const float* hsc, const float* y_add,
                           float* y, hipStream_t st);
 
+// few tokens, layer with a shared expert: routed and shared gate/up in one
+// launch, routed and shared down (with the combine) in another (decode.hip)
+struct RsLaunch {
+  int fmt;
+  const uint8_t *gq, *uq, *dq;
+  const float *gs, *us, *ds;                // row scales (per-row formats) or nullptr
+  int64_t gu_bytes, dn_bytes;
+  int F, act, H, E, k, T;
+  const double* part;                       // router partials [T][E][S]
+  int S;
+  const float* bias;
+  const void* xd;                           // x digit planes / scales (routed format)
+  const float* xsc;
+  void* hd;                                 // h digit planes / scales [T*k]
+  float* hsc;
+  int sfmt;
+  const uint8_t *sgq, *suq, *sdq;
+  const float *sgs, *sus, *sds;
+  int Fs, sact;
+  const void* sxd;
+  const float* sxsc;
+  void* shd;                                // [T]
+  float* shsc;
+  int* idx;
+  float* gates;
+  float* y;
+};
+bool rs_supported(int fmt, int H, int F, int sfmt, int Fs, int k, int T);
+hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st);
+
 // the few-token layer after the router as one persistent kernel (fused.hip)
 struct FusedLaunch {
   int fmt;                                  // routed experts

@@ -420,8 +420,11 @@ MD_DEV i32x4 decode_a8(const uint8_t* p) {
 // RT: 16-row MFMA tiles per wave; each digit-plane fragment read from LDS
 // feeds RT products (the block covers 64*RT rows: for gate/up 32*RT gate rows
 // and the same up rows).
+#ifndef MD_I8_WAVES
+#define MD_I8_WAVES 2
+#endif
 template <int FMT, int GU, int RT>
-__global__ __launch_bounds__(256) void k_moe_mfma_i8(MfmaI8Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES))) void k_moe_mfma_i8(MfmaI8Args a) {
   using TL = Tile<FMT>;
   constexpr int KB = TL::B8 ? 16 : 8;  // weight bytes per lane per 64-wide step
   constexpr int BR = 64 * RT;          // weight rows per block
