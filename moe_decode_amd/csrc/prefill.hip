@@ -131,14 +131,21 @@ MD_DEV bf16x8 load_b(const u16* tile, int j, int s, int q) {
   }
 }
 
-template <int FMT, int GU>
-__global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
+#ifndef MD_BF_WAVES
+#define MD_BF_WAVES 2
+#endif
+// RT: 16-row MFMA tiles per wave; each activation fragment read from LDS
+// feeds RT products (64*RT rows per block; gate/up: 32*RT gate + 32*RT up).
+template <int FMT, int GU, int RT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES))) void k_moe_mfma(MfmaArgs a) {
   using TL = Tile<FMT>;
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kRows * TL::WSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][kRows * 8];
+  constexpr int BR = 64 * RT;
+  constexpr int WCH = BR * TL::WB / 16, WPT = WCH / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BR * TL::WSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][BR * 8];
   __shared__ __attribute__((aligned(16))) u16 s_hi[2][kTok * kAST];
   __shared__ __attribute__((aligned(16))) u16 s_lo[2][kTok * kAST];
-  __shared__ float s_up[32][kTok];
+  __shared__ float s_up[BR / 2][kTok];
 
   struct { int e, p0, p1; } er;
   if (a.d.n_active == nullptr) {  // dense FFN: one expert, positions = tokens
@@ -154,13 +161,13 @@ __global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
   const int q = lane >> 4, li = lane & 15;
   const int64_t rb = row_bytes(FMT, a.K);
   const int nkt = a.K / kKT;
-  // block rows: gate/up stage -> 32 gate + 32 up rows of f0..f0+31
-  const int r0 = GU ? blockIdx.x * 32 : blockIdx.x * kRows;
+  // block rows: gate/up stage -> BR/2 gate + BR/2 up rows of f0..
+  const int r0 = GU ? blockIdx.x * (BR / 2) : blockIdx.x * BR;
 
-  auto row_ptr = [&](int r) -> const uint8_t* {  // r: block row 0..63
+  auto row_ptr = [&](int r) -> const uint8_t* {  // r: block row 0..BR-1
     if (GU) {
-      const int f = min(r0 + (r & 31), a.M - 1);
-      const uint8_t* base = (r < 32 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes;
+      const int f = min(r0 + (r % (BR / 2)), a.M - 1);
+      const uint8_t* base = (r < BR / 2 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes;
       return base + (int64_t)f * rb;
     }
     return a.wq + (int64_t)er.e * a.mat_bytes + (int64_t)min(r0 + r, a.M - 1) * rb;
@@ -181,17 +188,17 @@ __global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
       alo = a.a_lo + (int64_t)row * a.K;
     }
     // two register sets: tile kt+1 waits in one while tile kt+2 is in flight
-    u32x4 rw[2][TL::WPT];
+    u32x4 rw[2][WPT];
     u32x4 rs[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     uint4 rh[2][2], rl[2][2];
     auto gload = [&](int kt, int set) {
 #pragma unroll
-      for (int i = 0; i < TL::WPT; ++i) {
+      for (int i = 0; i < WPT; ++i) {
         const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
         rw[set][i] = ld_stream(row_ptr(r) + (int64_t)kt * TL::WB + 16 * piece);
       }
       if constexpr (TL::BLK) {
-        if (tid < kRows) {
+        if (tid < BR) {
           const int scoff = FMT == Q8_0 ? a.K : (a.K / 32) * 16;
           rs[set] = *reinterpret_cast<const u32x4*>(row_ptr(tid) + scoff + 16 * kt);
         }
@@ -209,12 +216,12 @@ __global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
     };
     auto lstore = [&](int buf, int set) {
 #pragma unroll
-      for (int i = 0; i < TL::WPT; ++i) {
+      for (int i = 0; i < WPT; ++i) {
         const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
         *reinterpret_cast<u32x4*>(&s_w[buf][r * TL::WSTR + 16 * piece]) = rw[set][i];
       }
       if constexpr (TL::BLK) {
-        if (tid < kRows) *reinterpret_cast<u32x4*>(&s_sc[buf][tid * 8]) = rs[set];
+        if (tid < BR) *reinterpret_cast<u32x4*>(&s_sc[buf][tid * 8]) = rs[set];
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -223,28 +230,34 @@ __global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
       }
     };
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int wr = wave * 16;  // this wave's first block row
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wr = wave * 16 * RT;  // this wave's first block row
     auto compute = [&](int buf) {
 #pragma unroll
       for (int s = 0; s < kKT / 32; ++s) {
-        const uint8_t* wp = &s_w[buf][(wr + li) * TL::WSTR + (TL::B8 ? 32 * s + 8 * q : 16 * s + 4 * q)];
-        const bf16x8 av = decode_a<FMT>(wp);
         const bf16x8 bh = load_b<FMT>(s_hi[buf], li, s, q);
         const bf16x8 bl = load_b<FMT>(s_lo[buf], li, s, q);
-        if constexpr (TL::BLK) {
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float d = h2f(s_sc[buf][(wr + 4 * q + v) * 8 + s]);
-            if constexpr (FMT == Q4_0) d *= 0.0625f;
-            acc[v] = fmaf(d, z[v], acc[v]);
+        for (int rt = 0; rt < RT; ++rt) {
+          const uint8_t* wp =
+              &s_w[buf][(wr + 16 * rt + li) * TL::WSTR + (TL::B8 ? 32 * s + 8 * q : 16 * s + 4 * q)];
+          const bf16x8 av = decode_a<FMT>(wp);
+          if constexpr (TL::BLK) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float d = h2f(s_sc[buf][(wr + 16 * rt + 4 * q + v) * 8 + s]);
+              if constexpr (FMT == Q4_0) d *= 0.0625f;
+              acc[rt][v] = fmaf(d, z[v], acc[rt][v]);
+            }
+          } else {
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rt], 0, 0, 0);
+            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rt], 0, 0, 0);
           }
-        } else {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc, 0, 0, 0);
         }
       }
     };
@@ -266,31 +279,36 @@ __global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
       __syncthreads();
     }
 
-    // epilogue: lane holds rows wr + 4q + v (v < 4) of token column li
+    // epilogue: lane holds rows wr + 16 rt + 4q + v (v < 4) of token column li
     const int j = li;
     if constexpr (GU) {
       if (wave >= 2) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s_up[wr - 32 + 4 * q + v][j] = acc[v];
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s_up[wr - BR / 2 + 16 * rt + 4 * q + v][j] = acc[rt][v];
       }
       __syncthreads();
       if (wave < 2 && j < nt) {
         const int pos = t0 + j;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rr = wr + 4 * q + v, f = r0 + rr;
-          if (f < a.M) {
-            float av = acc[v], uv = s_up[rr][j];
-            if constexpr (Fmt<FMT>::ROW) {
-              av *= a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
-              uv *= a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int rr = wr + 16 * rt + 4 * q + v, f = r0 + rr;
+            if (f < a.M) {
+              float av = acc[rt][v], uv = s_up[rr][j];
+              if constexpr (Fmt<FMT>::ROW) {
+                av *= a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
+                uv *= a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
+              }
+              const float hv = act_f(a.act, av) * uv;
+              const int64_t o = (int64_t)pos * a.M + f;
+              a.out[o] = hv;
+              const __bf16 hh = (__bf16)hv;
+              a.out_hi[o] = __builtin_bit_cast(u16, hh);
+              a.out_lo[o] = __builtin_bit_cast(u16, (__bf16)(hv - (float)hh));
             }
-            const float hv = act_f(a.act, av) * uv;
-            const int64_t o = (int64_t)pos * a.M + f;
-            a.out[o] = hv;
-            const __bf16 hh = (__bf16)hv;
-            a.out_hi[o] = __builtin_bit_cast(u16, hh);
-            a.out_lo[o] = __builtin_bit_cast(u16, (__bf16)(hv - (float)hh));
           }
         }
       }
@@ -298,12 +316,15 @@ __global__ __launch_bounds__(256) void k_moe_mfma(MfmaArgs a) {
       if (j < nt) {
         const int pos = t0 + j;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = r0 + wr + 4 * q + v;
-          if (i < a.M) {
-            float ov = acc[v];
-            if constexpr (Fmt<FMT>::ROW) ov *= a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
-            a.out[(int64_t)pos * a.M + i] = ov;
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int i = r0 + wr + 16 * rt + 4 * q + v;
+            if (i < a.M) {
+              float ov = acc[rt][v];
+              if constexpr (Fmt<FMT>::ROW) ov *= a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
+              a.out[(int64_t)pos * a.M + i] = ov;
+            }
           }
         }
       }
@@ -318,16 +339,19 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
                            const u16* a_hi, const u16* a_lo, bool act_by_token, float* out, u16* out_hi,
                            u16* out_lo, hipStream_t st) {
   MfmaArgs a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, a_hi, a_lo, act_by_token ? 1 : 0, out, out_hi, out_lo};
-  const int rows_per_block = gateup ? 32 : kRows;
+  // 4-bit codes: two row tiles per wave (activation fragment reads per weight
+  // byte halve); 8-bit codes: one (twice the weight bytes per tile)
+  const int RT = (fmt == Q4_0 || fmt == I4_ROW) ? 2 : 1;
+  const int rows_per_block = (gateup ? 32 : 64) * RT;
   // token tiles: an expert holds at most T tokens (one per token)
   const int tiles = (d.T + kTok - 1) / kTok;
   const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.n_active ? max_active : 1, tiles);
-#define MD_MF(F_) \
-  if (fmt == F_) { \
-    if (gateup) hipLaunchKernelGGL((k_moe_mfma<F_, 1>), grid, dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((k_moe_mfma<F_, 0>), grid, dim3(256), 0, st, a); \
+#define MD_MF(F_, RT_) \
+  if (fmt == F_ && RT == RT_) { \
+    if (gateup) hipLaunchKernelGGL((k_moe_mfma<F_, 1, RT_>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((k_moe_mfma<F_, 0, RT_>), grid, dim3(256), 0, st, a); \
     return hipGetLastError(); }
-  MD_MF(Q8_0) MD_MF(Q4_0) MD_MF(I8_ROW) MD_MF(I4_ROW)
+  MD_MF(Q8_0, 1) MD_MF(Q4_0, 2) MD_MF(I8_ROW, 1) MD_MF(I4_ROW, 2)
 #undef MD_MF
   return hipErrorInvalidValue;
 }
