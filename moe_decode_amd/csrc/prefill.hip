@@ -424,6 +424,7 @@ struct MfmaI8Args {
   const int* expo;       // [rows]
   int act_by_token;
   float* out;            // h [pos][F] or o [pos][H]
+  int R;                 // row blocks per workgroup
 };
 
 template <int FMT>
@@ -446,6 +447,12 @@ MD_DEV i32x4 decode_a8(const uint8_t* p) {
 // and the same up rows).
 #ifndef MD_I8_WAVES
 #define MD_I8_WAVES 2
+#endif
+#ifndef MD_I8_R_LONG
+#define MD_I8_R_LONG 1
+#endif
+#ifndef MD_I8_R_SHORT
+#define MD_I8_R_SHORT 4
 #endif
 template <int FMT, int GU, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES))) void k_moe_mfma_i8(MfmaI8Args a) {
@@ -475,8 +482,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
   const int q = lane >> 4, li = lane & 15;
   const int64_t rb = row_bytes(FMT, a.K);
   const int nkt = a.K / kKT;
-  const int r0 = GU ? blockIdx.x * (BR / 2) : blockIdx.x * BR;
-  auto row_ptr = [&](int r) -> const uint8_t* {
+  // this block's row blocks: rb_first .. rb_first + nrb - 1, streamed as one
+  // sequence of nrb * nkt weight tiles (the loads run on across row blocks)
+  constexpr int RPB = GU ? BR / 2 : BR;  // matrix rows per row block
+  const int nrb_all = (a.M + RPB - 1) / RPB;
+  const int rb_first = blockIdx.x * a.R;
+  const int nrb = min(a.R, nrb_all - rb_first);
+  const int NT = nrb * nkt;
+  auto row_ptr = [&](int rbi, int r) -> const uint8_t* {
+    const int r0 = (rb_first + rbi) * RPB;
     if (GU) {
       const int f = min(r0 + (r % (BR / 2)), a.M - 1);
       return (r < BR / 2 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes + (int64_t)f * rb;
@@ -494,11 +508,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
 
   u32x4 rw[2][WPT];
   uint4 rd[2][4];
-  auto gload = [&](int kt, int set) {
+  auto gload = [&](int ti, int set) {
+    const int rbi = ti / nkt, kt = ti - rbi * nkt;
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
-      rw[set][i] = ld_stream(row_ptr(r) + (int64_t)kt * TL::WB + 16 * piece);
+      rw[set][i] = ld_stream(row_ptr(rbi, r) + (int64_t)kt * TL::WB + 16 * piece);
     }
 #pragma unroll
     for (int l = 0; l < 4; ++l)
@@ -536,69 +551,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
       }
     }
   };
-  gload(0, 0);
-  if (nkt > 1) gload(1, 1);
-  lstore(0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    if (kt + 2 < nkt) gload(kt + 2, 0);
-    compute(0);
-    if (kt + 1 < nkt) lstore(1, 1);
-    __syncthreads();
-    if (kt + 1 >= nkt) break;
-    if (kt + 3 < nkt) gload(kt + 3, 1);
-    compute(1);
-    if (kt + 2 < nkt) lstore(0, 0);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds rows wr + 16 rt + 4q + v of token column li
-  const int j = li;
-  const float ex = ldexpf(1.0f, s_e[j] - 30);
-  float val[RT][4];
+  // epilogue of row block rbi: lane holds rows wr + 16 rt + 4q + v of token column li
+  auto finish = [&](int rbi) {
+    const int r0 = (rb_first + rbi) * RPB;
+    const int j = li;
+    const float ex = ldexpf(1.0f, s_e[j] - 30);
+    float val[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      val[rt][v] = (fmaf((float)acc[rt][3][v], 16777216.0f, (float)acc[rt][2][v] * 65536.0f) +
-                    fmaf((float)acc[rt][1][v], 256.0f, (float)acc[rt][0][v])) * ex;
-  if constexpr (GU) {
-    // waves 0, 1: gate rows; waves 2, 3: the same rows of up
-    if (wave >= 2) {
+      for (int v = 0; v < 4; ++v)
+        val[rt][v] = (fmaf((float)acc[rt][3][v], 16777216.0f, (float)acc[rt][2][v] * 65536.0f) +
+                      fmaf((float)acc[rt][1][v], 256.0f, (float)acc[rt][0][v])) * ex;
+    if constexpr (GU) {
+      // waves 0, 1: gate rows; waves 2, 3: the same rows of up
+      if (wave >= 2) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s_up[wr - BR / 2 + 16 * rt + 4 * q + v][j] = val[rt][v];
-    }
-    __syncthreads();
-    if (wave < 2 && j < nt) {
-      const int pos = t0 + j;
+          for (int v = 0; v < 4; ++v) s_up[wr - BR / 2 + 16 * rt + 4 * q + v][j] = val[rt][v];
+      }
+      __syncthreads();
+      if (wave < 2 && j < nt) {
+        const int pos = t0 + j;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int rr = wr + 16 * rt + 4 * q + v, f = r0 + rr;
-          if (f < a.M) {
-            const float av = val[rt][v] * a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
-            const float uv = s_up[rr][j] * a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
-            a.out[(int64_t)pos * a.M + f] = act_f(a.act, av) * uv;
+          for (int v = 0; v < 4; ++v) {
+            const int rr = wr + 16 * rt + 4 * q + v, f = r0 + rr;
+            if (f < a.M) {
+              const float av = val[rt][v] * a.ws[(int64_t)er.e * a.M + f] * row_post<FMT>();
+              const float uv = s_up[rr][j] * a.ws2[(int64_t)er.e * a.M + f] * row_post<FMT>();
+              a.out[(int64_t)pos * a.M + f] = act_f(a.act, av) * uv;
+            }
+          }
+        }
+      }
+    } else {
+      if (j < nt) {
+        const int pos = t0 + j;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int i = r0 + wr + 16 * rt + 4 * q + v;
+            if (i < a.M)
+              a.out[(int64_t)pos * a.M + i] = val[rt][v] * a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
           }
         }
       }
     }
-  } else {
-    if (j < nt) {
-      const int pos = t0 + j;
+  };
+  gload(0, 0);
+  if (NT > 1) gload(1, 1);
+  lstore(0, 0);
+  __syncthreads();
+  auto end_of_row_block = [&](int ti) {
+    if ((ti + 1) % nkt == 0) {
+      finish(ti / nkt);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = r0 + wr + 16 * rt + 4 * q + v;
-          if (i < a.M)
-            a.out[(int64_t)pos * a.M + i] = val[rt][v] * a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
-        }
-      }
+        for (int l = 0; l < 4; ++l) acc[rt][l] = i32x4{0, 0, 0, 0};
     }
+  };
+  for (int ti = 0; ti < NT; ti += 2) {
+    if (ti + 2 < NT) gload(ti + 2, 0);
+    compute(0);
+    end_of_row_block(ti);
+    if (ti + 1 < NT) lstore(1, 1);
+    __syncthreads();
+    if (ti + 1 >= NT) break;
+    if (ti + 3 < NT) gload(ti + 3, 1);
+    compute(1);
+    end_of_row_block(ti + 1);
+    if (ti + 2 < NT) lstore(0, 0);
+    __syncthreads();
   }
 }
 
@@ -606,13 +634,18 @@ hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uin
                               const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d,
                               int max_active, const int8_t* digits, const int* expo, bool act_by_token, float* out,
                               hipStream_t st) {
-  MfmaI8Args a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, digits, expo, act_by_token ? 1 : 0, out};
+  MfmaI8Args a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, digits, expo, act_by_token ? 1 : 0, out, 1};
   // int4 weights: two row tiles per wave (LDS reads of the activation digits
   // per weight byte halve); int8: one (its weight tiles are twice as large)
   const int RT = fmt == I4_ROW ? 2 : 1;
   const int rows_per_block = (gateup ? 32 : 64) * RT;
   const int tiles = (d.T + kTok - 1) / kTok;
-  const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.n_active ? max_active : 1, tiles);
+  // row blocks per workgroup: short rows (few K tiles) stream several row
+  // blocks back to back so the load pipeline's fill is paid once
+  const int nkt = K / kKT;
+  a.R = nkt >= 16 ? MD_I8_R_LONG : MD_I8_R_SHORT;
+  const int nrb = (M + rows_per_block - 1) / rows_per_block;
+  const dim3 grid((nrb + a.R - 1) / a.R, d.n_active ? max_active : 1, tiles);
 #define MD_MF8(F_, RT_) \
   if (fmt == F_ && RT == RT_) { \
     if (gateup) hipLaunchKernelGGL((k_moe_mfma_i8<F_, 1, RT_>), grid, dim3(256), 0, st, a); \
