@@ -60,6 +60,9 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIBPATH):
             raise ImportError(f"{LIBPATH} is missing: build it with `python -m moe_decode_amd.build`")
+        # torch first: its HIP runtime is then the one the library binds to
+        # (two runtimes in one process would each see the device as busy)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIBPATH)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         psz = ctypes.POINTER(ctypes.c_size_t)

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ W,
   const int row0 = ((blockIdx.x * kWaves + wave) * G + g) * R;
   if (row0 >= N) return;
   const int nc = nchunks(FMT, K);
-  const int cs = nc / S, c0 = blockIdx.y * cs;
+  const int c0 = (int)((int64_t)blockIdx.y * nc / S), c1 = (int)((int64_t)(blockIdx.y + 1) * nc / S);
   const int64_t rb = row_bytes(FMT, K);
   const uint8_t* rowp[R];
 #pragma unroll
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kBlock) void k_qgemv(const uint8_t* __restrict__ W,
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
-  rows_dot<FMT, XT, L, R, B>(rowp, K, c0, c0 + cs, t, xp, acc);
+  rows_dot<FMT, XT, L, R, B>(rowp, K, c0, c1, t, xp, acc);
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -116,13 +116,18 @@ GemvCfg qgemv_config(int fmt, int N, int K, int batch) {
   const int nc = nchunks(fmt, K);
   c.L = pow2_divisor_le64(nc);
   c.B = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
-  c.R = c.B <= 2 ? 4 : 2;
   const int G = 64 / c.L;
+  // rows per lane group: as many as keep >= 2048 waves (more independent
+  // loads in flight per lane), then split K (uneven ranges allowed) until
+  // the grid has that many waves; every K-slice keeps >= 2 chunks per lane
+  const int rmax = c.B <= 2 ? 4 : 2;
+  c.R = rmax;
+  auto blocks = [&](int R) { return (N + kWaves * G * R - 1) / (kWaves * G * R); };
+  while (c.R > 1 && (int64_t)blocks(c.R) * kWaves < 2048) c.R /= 2;
   c.rows_per_block = kWaves * G * c.R;
-  const int bx = (N + c.rows_per_block - 1) / c.rows_per_block;
-  // split K until the grid has enough waves to keep HBM busy
+  const int bx = blocks(c.R);
   c.S = 1;
-  while (bx * kWaves * c.S < 2048 && nc % (2 * c.S * c.L) == 0 && c.S < 16) c.S *= 2;
+  while ((int64_t)bx * kWaves * c.S < 2048 && nc / (2 * c.S) >= 2 * c.L && c.S < 16) c.S *= 2;
   c.grid = dim3(bx, c.S);
   return c;
 }
@@ -134,7 +139,8 @@ static hipError_t qgemv_fx(const GemvCfg& c, const uint8_t* W, const float* s, i
   if (c.L == L_ && c.R == R_ && c.B == B_) { \
     hipLaunchKernelGGL((k_qgemv<FMT, XT, L_, R_, B_>), c.grid, dim3(kBlock), 0, st, W, s, N, K, x, nb, out, c.S); \
     return hipGetLastError(); }
-#define MD_QL(L_) MD_Q(L_, 4, 1) MD_Q(L_, 4, 2) MD_Q(L_, 2, 4) MD_Q(L_, 2, 8)
+#define MD_QL(L_) MD_Q(L_, 4, 1) MD_Q(L_, 2, 1) MD_Q(L_, 1, 1) MD_Q(L_, 4, 2) MD_Q(L_, 2, 2) MD_Q(L_, 1, 2) \
+                  MD_Q(L_, 2, 4) MD_Q(L_, 1, 4) MD_Q(L_, 2, 8) MD_Q(L_, 1, 8)
   MD_QL(64) MD_QL(32) MD_QL(16) MD_QL(8)
 #undef MD_QL
 #undef MD_Q
