@@ -339,12 +339,32 @@ md_status md_prepare_layout(int32_t type, int32_t rows, int32_t cols, int32_t co
   return e == hipSuccess ? ok() : hip_fail(e, "prepare_layout launch");
 }
 
+// Batches of 4 or more on block formats run on the matrix cores (the VALU
+// engine re-reads every token's activations for every weight chunk).
+static bool gemv_on_mfma(const md_qmatrix* W, int batch) {
+  return batch >= 4 && (W->type == MD_Q8_0 || W->type == MD_Q4_0) && md::mfma_supported(W->cols);
+}
+
+// Matrix-core GEMV workspace: [ks][batch][rows] partials (ks > 1), then the
+// bf16 hi / lo halves of fp32 activations.
+static size_t gemv_mfma_bytes(const md_qmatrix* W, int batch, size_t* part, size_t* pair) {
+  const int ks = md::mfma_gemv_splits(W->type, W->rows, W->cols);
+  *part = ks > 1 ? align256(sizeof(float) * (size_t)ks * batch * W->rows) : 0;
+  *pair = align256(2 * (size_t)batch * W->cols);
+  return *part + 2 * *pair;
+}
+
 md_status md_qgemv_workspace_size(const md_qmatrix* W, int32_t batch, size_t* bytes) {
   md_status s = check_qmatrix("W", W);
   if (s != MD_OK) return s;
   if (!bytes) return fail(MD_ERR_INVALID_ARG, "null bytes");
   if (batch <= 0) return fail(MD_ERR_SHAPE, "batch %d", batch);
   if (batch > kMaxBatch) return fail(MD_ERR_UNSUPPORTED, "batch %d > %d", batch, kMaxBatch);
+  if (gemv_on_mfma(W, batch)) {
+    size_t part, pair;
+    *bytes = gemv_mfma_bytes(W, batch, &part, &pair);
+    return ok();
+  }
   md::GemvCfg c = md::qgemv_config(W->type, W->rows, W->cols, batch);
   *bytes = c.S > 1 ? align256(sizeof(float) * (size_t)c.S * batch * W->rows) : 0;
   return ok();
@@ -359,6 +379,32 @@ md_status md_qgemv(const md_qmatrix* W, const void* x, int32_t xtype, int32_t ba
   if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
   if (!aligned16(x) || !aligned16(y)) return fail(MD_ERR_ALIGNMENT, "x and y must be 16-byte aligned");
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
+  if (gemv_on_mfma(W, batch)) {
+    size_t part, pair;
+    gemv_mfma_bytes(W, batch, &part, &pair);
+    char* ws = static_cast<char*>(workspace);
+    const int ks = md::mfma_gemv_splits(W->type, W->rows, W->cols);
+    const u16* hi = static_cast<const u16*>(x);
+    const u16* lo = nullptr;  // bf16 activations have no low half
+    hipError_t e = hipSuccess;
+    if (xtype == MD_X_F32) {
+      u16* h = reinterpret_cast<u16*>(ws + part);
+      u16* l = reinterpret_cast<u16*>(ws + part + pair);
+      e = md::launch_split_bf16(static_cast<const float*>(x), (int64_t)batch * W->cols, h, l, stream);
+      if (e != hipSuccess) return hip_fail(e, "split launch");
+      hi = h;
+      lo = l;
+    }
+    float* out = ks > 1 ? reinterpret_cast<float*>(ws) : y;
+    e = md::launch_mfma_gemv(W->type, static_cast<const uint8_t*>(W->q), W->row_scale, W->rows, W->cols, batch, hi,
+                             lo, ks, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "matrix-core gemv launch");
+    if (ks > 1) {
+      e = md::launch_splitk_reduce(out, ks, (int64_t)batch * W->rows, y, stream);
+      if (e != hipSuccess) return hip_fail(e, "split-K reduce launch");
+    }
+    return ok();
+  }
   md::GemvCfg c = md::qgemv_config(W->type, W->rows, W->cols, batch);
   hipError_t e = md::launch_qgemv(W->type, xtype, c, static_cast<const uint8_t*>(W->q), W->row_scale, W->rows, W->cols,
                                   x, batch, y, static_cast<float*>(workspace), stream);

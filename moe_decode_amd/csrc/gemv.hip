@@ -105,6 +105,11 @@ __global__ __launch_bounds__(kBlock) void k_splitk_reduce(const float* __restric
   y[i] = a;
 }
 
+hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* y, hipStream_t st) {
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, part, S, n, y);
+  return hipGetLastError();
+}
+
 static int pow2_divisor_le64(int n) {
   int L = 64;
   while (L > 1 && n % L) L >>= 1;

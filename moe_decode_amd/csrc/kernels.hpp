@@ -168,6 +168,13 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
                            const unsigned short* a_hi, const unsigned short* a_lo, bool act_by_token, float* out,
                            unsigned short* out_hi, unsigned short* out_lo, hipStream_t st);
 
+// dense GEMV of T <= 16 tokens on the matrix cores (block formats), K split
+// in ks ranges: partials [ks][T][M] in out (reduce with launch_splitk_reduce)
+int mfma_gemv_splits(int fmt, int M, int K);
+hipError_t launch_mfma_gemv(int fmt, const uint8_t* wq, const float* ws, int M, int K, int T, const uint16_t* a_hi,
+                            const uint16_t* a_lo, int ks, float* out, hipStream_t st);
+hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* y, hipStream_t st);
+
 hipError_t launch_limbs(const float* a, int R, int K, bool perm4, int8_t* digits, int* expo, hipStream_t st);
 hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
                               const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d,

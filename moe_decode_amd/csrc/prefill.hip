@@ -77,11 +77,12 @@ struct MfmaArgs {
   int act;
   Disp d;
   const u16* a_hi;       // activation pairs, rows of K
-  const u16* a_lo;
+  const u16* a_lo;       // nullptr: activations exactly bf16 (no low half)
   int act_by_token;      // activation row = token of the position (x) or the position (h)
   float* out;            // h [pos][F] or o [pos][H]
   u16* out_hi;           // h as a bf16 pair for the next stage (gate/up stage)
   u16* out_lo;
+  int ks;                // dense mode: K splits (blockIdx.z); partial sums go to out + z*T*M
 };
 
 template <int FMT>
@@ -160,7 +161,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, li = lane & 15;
   const int64_t rb = row_bytes(FMT, a.K);
-  const int nkt = a.K / kKT;
+  int kt_begin = 0, kt_end = a.K / kKT;
+  int ksplit = 0;
+  if (a.d.n_active == nullptr && a.ks > 1) {  // dense mode, K split over blockIdx.z
+    ksplit = (int)blockIdx.z;
+    const int n = kt_end;
+    kt_begin = (int)((int64_t)ksplit * n / a.ks);
+    kt_end = (int)((int64_t)(ksplit + 1) * n / a.ks);
+  }
+  const int nkt = kt_end - kt_begin;
   // block rows: gate/up stage -> BR/2 gate + BR/2 up rows of f0..
   const int r0 = GU ? blockIdx.x * (BR / 2) : blockIdx.x * BR;
 
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
   auto pos_token = [&](int pos) { return a.d.n_active == nullptr ? pos : a.d.pairs[pos] / a.d.k; };
 
   {
-    const int t0 = er.p0 + (int)blockIdx.z * kTok;  // this block's 16-token tile
+    const int t0 = er.p0 + (ksplit ? 0 : (int)blockIdx.z) * kTok;  // this block's 16-token tile
     if (t0 >= er.p1) return;
     const int nt = min(kTok, er.p1 - t0);
     // this thread's activation rows for staging: token slot jj = tid / 16, piece pp = tid % 16
@@ -185,13 +194,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
     if (jj < nt) {
       const int row = a.act_by_token ? pos_token(t0 + jj) : t0 + jj;
       ahi = a.a_hi + (int64_t)row * a.K;
-      alo = a.a_lo + (int64_t)row * a.K;
+      alo = a.a_lo ? a.a_lo + (int64_t)row * a.K : nullptr;
     }
+    const bool has_lo = a.a_lo != nullptr;
     // two register sets: tile kt+1 waits in one while tile kt+2 is in flight
     u32x4 rw[2][WPT];
     u32x4 rs[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     uint4 rh[2][2], rl[2][2];
-    auto gload = [&](int kt, int set) {
+    auto gload = [&](int ktl, int set) {
+      const int kt = kt_begin + ktl;
 #pragma unroll
       for (int i = 0; i < WPT; ++i) {
         const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
@@ -207,7 +218,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       for (int i = 0; i < 2; ++i) {
         if (ahi) {
           rh[set][i] = *reinterpret_cast<const uint4*>(ahi + kt * kKT + 16 * pp + 8 * i);
-          rl[set][i] = *reinterpret_cast<const uint4*>(alo + kt * kKT + 16 * pp + 8 * i);
+          rl[set][i] = alo ? *reinterpret_cast<const uint4*>(alo + kt * kKT + 16 * pp + 8 * i)
+                           : make_uint4(0u, 0u, 0u, 0u);
         } else {
           rh[set][i] = make_uint4(0u, 0u, 0u, 0u);
           rl[set][i] = make_uint4(0u, 0u, 0u, 0u);
@@ -238,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
 #pragma unroll
       for (int s = 0; s < kKT / 32; ++s) {
         const bf16x8 bh = load_b<FMT>(s_hi[buf], li, s, q);
-        const bf16x8 bl = load_b<FMT>(s_lo[buf], li, s, q);
+        const bf16x8 bl = has_lo ? load_b<FMT>(s_lo[buf], li, s, q) : bf16x8{};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const uint8_t* wp =
@@ -247,7 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
           if constexpr (TL::BLK) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
-            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
+            if (has_lo) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               float d = h2f(s_sc[buf][(wr + 16 * rt + 4 * q + v) * 8 + s]);
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
             }
           } else {
             acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rt], 0, 0, 0);
-            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rt], 0, 0, 0);
+            if (has_lo) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rt], 0, 0, 0);
           }
         }
       }
@@ -323,7 +335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
             if (i < a.M) {
               float ov = acc[rt][v];
               if constexpr (Fmt<FMT>::ROW) ov *= a.ws[(int64_t)er.e * a.M + i] * row_post<FMT>();
-              a.out[(int64_t)pos * a.M + i] = ov;
+              a.out[((int64_t)ksplit * a.d.T + pos) * a.M + i] = ov;
             }
           }
         }
@@ -334,11 +346,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
 
 bool mfma_supported(int K) { return K % kKT == 0; }
 
+// Dense GEMV of a small batch (T <= 16 tokens) on the matrix cores: rows in
+// blocks of 64*RT, K split in ks ranges of whole tiles (partials [ks][T][M]).
+int mfma_gemv_splits(int fmt, int M, int K) {
+  const int RT = (fmt == Q4_0 || fmt == I4_ROW) ? 2 : 1;
+  const int rb = (M + 64 * RT - 1) / (64 * RT), nkt = K / kKT;
+  int ks = 1;
+  while (rb * ks < 512 && nkt / (2 * ks) >= 2) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_mfma_gemv(int fmt, const uint8_t* wq, const float* ws, int M, int K, int T, const u16* a_hi,
+                            const u16* a_lo, int ks, float* out, hipStream_t st) {
+  if (T < 1 || T > kTok || ks < 1) return hipErrorInvalidValue;
+  const Disp d{nullptr, nullptr, nullptr, nullptr, 1, T};
+  MfmaArgs a{wq, nullptr, ws, nullptr, 0, M, K, 0, d, a_hi, a_lo, 0, out, nullptr, nullptr, ks};
+  const int RT = (fmt == Q4_0 || fmt == I4_ROW) ? 2 : 1;
+  const dim3 grid((M + 64 * RT - 1) / (64 * RT), 1, ks);
+  if (fmt == Q8_0) hipLaunchKernelGGL((k_moe_mfma<Q8_0, 0, 1>), grid, dim3(256), 0, st, a);
+  else if (fmt == Q4_0) hipLaunchKernelGGL((k_moe_mfma<Q4_0, 0, 2>), grid, dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
                            const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d, int max_active,
                            const u16* a_hi, const u16* a_lo, bool act_by_token, float* out, u16* out_hi,
                            u16* out_lo, hipStream_t st) {
-  MfmaArgs a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, a_hi, a_lo, act_by_token ? 1 : 0, out, out_hi, out_lo};
+  MfmaArgs a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, a_hi, a_lo, act_by_token ? 1 : 0, out, out_hi, out_lo, 1};
   // 4-bit codes: two row tiles per wave (activation fragment reads per weight
   // byte halve); 8-bit codes: one (twice the weight bytes per tile)
   const int RT = (fmt == Q4_0 || fmt == I4_ROW) ? 2 : 1;
