@@ -25,6 +25,8 @@
 // kernel writes those of h (each workgroup covers whole digit groups).  Row loads run in a
 // rolling window (several rows in flight while one is decoded).  Partial sums of the rows a lane group visited are reduced with
 // one transposed butterfly (N-1 exchanges for N rows instead of N log L).
+#include <type_traits>
+
 #include "common.hpp"
 #include "digits.hpp"
 #include "kernels.hpp"
@@ -41,18 +43,24 @@ namespace md {
 constexpr int kNRW = MD_DN_ROWS;   // output rows per workgroup in k_down_t1
 
 // The digit planes of rows [0, R) of a row-major R x K fp32 matrix (K a
-// multiple of 256), 256 values per block iteration; grid-stride over blocks.
+// multiple of 256), spread over the grid: each workgroup takes as few whole
+// groups as cover them all (at most 256 values per pass), grid-stride.
 MD_DEV void dig_rows(const DigJob& j, uint32_t* ys) {
   if (!j.x) return;
-  const int64_t n = (int64_t)j.R * j.K;
-  for (int64_t base = (int64_t)blockIdx.x * 256; base < n; base += (int64_t)gridDim.x * 256) {
-    const float v = j.x[base + threadIdx.x];
-    const int64_t g0 = base / dig_nv(j.fmt);
+  const int nv = dig_nv(j.fmt);
+  const int64_t G = (int64_t)j.R * j.K / nv;
+  int64_t per = (G + gridDim.x - 1) / gridDim.x;
+  if (per > 256 / nv) per = 256 / nv;
+  if (per < 1) per = 1;
+  for (int64_t g0 = (int64_t)blockIdx.x * per; g0 < G; g0 += (int64_t)gridDim.x * per) {
+    const int cnt = (int)(G - g0 < per ? G - g0 : per);
+    const int n = cnt * nv;
+    const float v = (int)threadIdx.x < n ? j.x[g0 * nv + threadIdx.x] : 0.f;
     switch (j.fmt) {
-      case Q8_0: dig_block<Q8_0>(v, 256, ys, j.planes + g0 * Dig<Q8_0>::NPL, j.scales + g0); break;
-      case Q4_0: dig_block<Q4_0>(v, 256, ys, j.planes + g0 * Dig<Q4_0>::NPL, j.scales + g0); break;
-      case I8_ROW: dig_block<I8_ROW>(v, 256, ys, j.planes + g0 * Dig<I8_ROW>::NPL, j.scales + g0); break;
-      default: dig_block<I4_ROW>(v, 256, ys, j.planes + g0 * Dig<I4_ROW>::NPL, j.scales + g0); break;
+      case Q8_0: dig_block<Q8_0>(v, n, ys, j.planes + g0 * Dig<Q8_0>::NPL, j.scales + g0); break;
+      case Q4_0: dig_block<Q4_0>(v, n, ys, j.planes + g0 * Dig<Q4_0>::NPL, j.scales + g0); break;
+      case I8_ROW: dig_block<I8_ROW>(v, n, ys, j.planes + g0 * Dig<I8_ROW>::NPL, j.scales + g0); break;
+      default: dig_block<I4_ROW>(v, n, ys, j.planes + g0 * Dig<I4_ROW>::NPL, j.scales + g0); break;
     }
   }
 }
@@ -75,49 +83,89 @@ hipError_t launch_digits(const DigJob& j, hipStream_t st) {
 // each lane accumulates in fp64 for up to 4 tokens at a time, and the wave
 // sums are added in a fixed order into part[t][e][s].  The consumer adds the
 // S partials in order, then the bias, and rounds once to fp32.
+// fp64 sum over the wave by DPP lane moves (quads, mirrored half-rows and
+// rows, then the row broadcasts carry the total to lane 63); fixed order.
+MD_DEV double wave_sum_f64_dpp(double v) {
+  auto step = [&](auto ctrl, auto row_mask) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(0, lo, decltype(ctrl)::value, decltype(row_mask)::value,
+                                                                0xF, false);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(0, hi, decltype(ctrl)::value, decltype(row_mask)::value,
+                                                                0xF, false);
+    v += __longlong_as_double((long long)(((uint64_t)phi << 32) | plo));
+  };
+  step(std::integral_constant<int, 0xB1>{}, std::integral_constant<int, 0xF>{});   // quad_perm [1,0,3,2]
+  step(std::integral_constant<int, 0x4E>{}, std::integral_constant<int, 0xF>{});   // quad_perm [2,3,0,1]
+  step(std::integral_constant<int, 0x141>{}, std::integral_constant<int, 0xF>{});  // row_half_mirror
+  step(std::integral_constant<int, 0x140>{}, std::integral_constant<int, 0xF>{});  // row_mirror
+  step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast:15 into rows 1, 3
+  step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});  // row_bcast:31 into rows 2, 3
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Block (e, s): expert e, K-slice s of S; the four waves split the slice,
+// each lane accumulates in fp64 for up to 4 tokens at a time, and the wave
+// sums are added in a fixed order into part[t][e][s].  The consumer adds the
+// S partials in order, then the bias, and rounds once to fp32.  A lane's
+// W_r values (at most kRV float4) are loaded once, before any product, and
+// each token's activations likewise.  The digit jobs and the zero job run
+// after the partials are written.
+constexpr int kRV = 8;
 __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr, int E, int S,
                                                      double* __restrict__ part, DigJob j0, DigJob j1, ZeroJob z) {
   __shared__ double red[4][4];
   __shared__ uint32_t ys[256];
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < z.n; i += blockDim.x) z.p[i] = 0;
-  // the activations' digit planes for the expert kernels (independent of the routing)
-  dig_rows(j0, ys);
-  dig_rows(j1, ys);
   const int e = blockIdx.x / S, sl = blockIdx.x % S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ks = H / S / 4;             // elements per wave, a multiple of 64
   const int k0 = sl * (H / S) + wave * ks;
   const float* w = Wr + (int64_t)e * H + k0;
-  const bool vec = (ks % 256) == 0;
+  const int nv = ks / 256;              // float4 per lane when ks is a multiple of 256
+  const bool vec = (ks % 256) == 0 && nv <= kRV;
+  float4 wv[kRV];
+  if (vec) {
+#pragma unroll
+    for (int u = 0; u < kRV; ++u)
+      if (u < nv) wv[u] = reinterpret_cast<const float4*>(w)[lane + 64 * u];
+  }
   for (int t0 = 0; t0 < T; t0 += 4) {
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     if (vec) {
-      for (int j = lane; j < ks / 4; j += 64) {
-        const float4 wv = reinterpret_cast<const float4*>(w)[j];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (t0 + b < T) {
-            const float4 xv = reinterpret_cast<const float4*>(x + (int64_t)(t0 + b) * H + k0)[j];
-            acc[b] = fma((double)wv.x, (double)xv.x, acc[b]);
-            acc[b] = fma((double)wv.y, (double)xv.y, acc[b]);
-            acc[b] = fma((double)wv.z, (double)xv.z, acc[b]);
-            acc[b] = fma((double)wv.w, (double)xv.w, acc[b]);
+      for (int b = 0; b < 4; ++b) {
+        if (t0 + b < T) {
+          const float4* xp = reinterpret_cast<const float4*>(x + (int64_t)(t0 + b) * H + k0);
+          float4 xv[kRV];
+#pragma unroll
+          for (int u = 0; u < kRV; ++u)
+            if (u < nv) xv[u] = xp[lane + 64 * u];
+#pragma unroll
+          for (int u = 0; u < kRV; ++u) {
+            if (u < nv) {
+              acc[b] = fma((double)wv[u].x, (double)xv[u].x, acc[b]);
+              acc[b] = fma((double)wv[u].y, (double)xv[u].y, acc[b]);
+              acc[b] = fma((double)wv[u].z, (double)xv[u].z, acc[b]);
+              acc[b] = fma((double)wv[u].w, (double)xv[u].w, acc[b]);
+            }
           }
         }
       }
     } else {
       for (int j = lane; j < ks; j += 64) {
-        const double wv = (double)w[j];
+        const double wd = (double)w[j];
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          if (t0 + b < T) acc[b] = fma(wv, (double)x[(int64_t)(t0 + b) * H + k0 + j], acc[b]);
+          if (t0 + b < T) acc[b] = fma(wd, (double)x[(int64_t)(t0 + b) * H + k0 + j], acc[b]);
       }
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const double v = wave_sum_f64(acc[b]);
+      const double v = wave_sum_f64_dpp(acc[b]);
       if (lane == 0) red[wave][b] = v;
     }
     __syncthreads();
@@ -127,6 +175,11 @@ __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x
     }
     __syncthreads();
   }
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < z.n; i += blockDim.x) z.p[i] = 0;
+  // the activations' digit planes for the expert kernels (independent of the routing)
+  dig_rows(j0, ys);
+  dig_rows(j1, ys);
 }
 
 #ifndef MD_ROUTER_BLOCKS
