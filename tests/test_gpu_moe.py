@@ -184,3 +184,23 @@ def test_moe_fused_kernel_matches_oracle(orc_mt, key, T, monkeypatch):
     assert np.max(np.abs(gates - g_ref)) <= 1e-6
     assert_within(y, y_ref, S, f"{key} T={T} separate")
     assert_within(yf, y_ref, S, f"{key} T={T} fused")
+
+
+@pytest.mark.parametrize("key", ["c4_i4", "c4_i8", "c3"])
+def test_moe_decode_activation_outliers(orc_mt, key):
+    """Activations with a few channels 200x larger than the rest (as trained
+    models have): the one-token kernels scale their integer digit planes per
+    weight chunk's group of activations, so a group holding an outlier
+    resolves its other values relative to it; outputs stay within the bound."""
+    sp = W.spec(key)
+    x = W.moe_x(sp, 2).copy()
+    rng = np.random.default_rng([sp.index, 4242])
+    ch = rng.choice(sp.H, size=max(4, sp.H // 200), replace=False)
+    x[:, ch] *= 200.0
+    say(f"[moe outliers] {key}: {len(ch)} channels x200")
+    y, idx, gates = _moe_gpu(key, x)
+    y_ref, i_ref, g_ref, S = oracle_moe(orc_mt, sp, x)
+    assert np.array_equal(idx, i_ref)
+    assert np.max(np.abs(gates - g_ref)) <= 1e-6
+    ratio = assert_within(y, y_ref, S, f"{key} outliers")
+    say(f"[moe outliers] {key} max err/S {ratio:.2e}")
