@@ -133,7 +133,7 @@ hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, c
 
 // One workgroup per token.  Thread e forms expert e's logit: the S partials
 // added in slice order, then the bias, rounded once to fp32.  Wave 0 then
-// takes the k winners one at a time by a 64-bit wave maximum; lane j
+// takes the k winners one at a time (topk_rounds); lane j
 // computes exp(l_j - l_0) in fp64, the sum runs over j in order, and lane j
 // writes gate j.
 __global__ __launch_bounds__(256) void k_select(const double* __restrict__ part, int S, int64_t ps, int64_t pt,
@@ -161,33 +161,16 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ part,
   }
   __syncthreads();
   if (threadIdx.x >= 64) return;
-  uint64_t key[4];
-  float lv[4];
+  uint32_t key[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ei = lane + 64 * i;
-    key[i] = 0;
-    lv[i] = 0.f;
-    if (ei < E) {
-      lv[i] = s_l[ei];
-      key[i] = ((uint64_t)order_key32(lv[i]) << 32) | (uint32_t)(~(uint32_t)ei);
-    }
-  }
+  for (int i = 0; i < 4; ++i) key[i] = lane + 64 * i < E ? order_key32(s_l[lane + 64 * i]) : 0u;
   float my_l = 0.f;
+  int sel[8];
+  topk_rounds(key, k, lane, sel, my_l);
   int my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int w = (int)(~(uint32_t)best);
-    float l = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == w) { key[i] = 0; l = lv[i]; }
-    l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), w & 63));
-    if (lane == j) { my_l = l; my_e = w; }
-  }
+  for (int j = 0; j < 8; ++j)
+    if (lane == j) my_e = sel[j];
   const double m = (double)__shfl(my_l, 0, 64);
   const double ex = lane < k ? exp((double)my_l - m) : 0.0;
   double z = 0.0;

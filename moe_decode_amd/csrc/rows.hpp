@@ -145,18 +145,14 @@ MD_DEV void dig_block(float v, int n, uint32_t* ys, u32x4* planes, float* scales
 // ------------------------------------------------------------------ top-k
 
 
-// Maximum of a 64-bit value over the wave, returned to every lane (uniform).
-// Lane moves by DPP only: within quads, then mirrored half-rows and rows (each
-// row of 16 lanes then holds its maximum), then the row broadcasts carry it
-// to lane 63, which is read back.
-MD_DEV uint64_t wave_max_u64(uint64_t v) {
+// Maximum of a 32-bit unsigned value over the wave, returned to every lane
+// (uniform).  Lane moves by DPP only: within quads, then mirrored half-rows and
+// rows (each row of 16 lanes then holds its maximum), then the row broadcasts
+// carry it to lane 63, which is read back.
+MD_DEV uint32_t wave_max_u32(uint32_t v) {
   auto step = [&](auto ctrl, auto row_mask) {
-    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-    const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, decltype(ctrl)::value,
-                                                                decltype(row_mask)::value, 0xF, false);
-    const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, decltype(ctrl)::value,
-                                                                decltype(row_mask)::value, 0xF, false);
-    const uint64_t p = ((uint64_t)phi << 32) | plo;
+    const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, decltype(ctrl)::value,
+                                                              decltype(row_mask)::value, 0xF, false);
     v = p > v ? p : v;
   };
   step(std::integral_constant<int, 0xB1>{}, std::integral_constant<int, 0xF>{});   // quad_perm [1,0,3,2]
@@ -165,9 +161,7 @@ MD_DEV uint64_t wave_max_u64(uint64_t v) {
   step(std::integral_constant<int, 0x140>{}, std::integral_constant<int, 0xF>{});  // row_mirror
   step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});  // row_bcast:15 into rows 1, 3
   step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});  // row_bcast:31 into rows 2, 3
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 MD_DEV uint32_t order_key32(float l) {
@@ -175,49 +169,72 @@ MD_DEV uint32_t order_key32(float l) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-level top-k of one token's E logits (E <= 256), formed from the S
-// router partials of each expert (added in slice order, plus the bias,
-// rounded once to fp32).  Keys: order-preserving image of the logit in the
-// high word, complemented expert index in the low word, so the largest key is
-// the largest logit and, among exact ties, the lower index.  All lanes return
-// the same k experts in selection order and, when asked, their gates: lane j
-// forms exp(l_j - l_0) in fp64, the sum runs over j in order, gate j = its
-// term / sum, rounded to fp32.
-MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __restrict__ bias, int E, int k, int lane,
-                      int (&sel)[8], float (&gts)[8], bool want_gates) {
-  uint64_t key[4];
-  float lv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = 0;
-    lv[i] = 0.f;
-    if (e < E) {
-      double a = 0.0;
-      for (int s = 0; s < S; ++s) a += part[(int64_t)e * S + s];
-      if (bias) a += (double)bias[e];
-      lv[i] = (float)a;
-      key[i] = ((uint64_t)order_key32(lv[i]) << 32) | (uint32_t)(~(uint32_t)e);
-    }
-  }
-  float my_l = 0.f;
+// The logit of an order key (-0 comes back as +0).
+MD_DEV float key_logit(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); }
+
+// Selection rounds over 32-bit order keys held as lane l: experts l, l + 64,
+// l + 128, l + 192 (0 marks a taken or absent expert: every finite logit maps
+// above it).  Each round takes the wave maximum of the keys; among the experts
+// that hold it (an exact tie) the lowest index wins: the first of the four
+// slots with a match, and within it the lowest lane.  sel[j] (every lane) is
+// the j-th winner; lane j's my_l is its logit.
+MD_DEV void topk_rounds(uint32_t (&key)[4], int k, int lane, int (&sel)[8], float& my_l) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     sel[j] = 0;
     if (j >= k) continue;
-    uint64_t best = key[0];
+    const uint32_t best = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+    int e = 0;
+    bool found = false;
 #pragma unroll
-    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(~(uint32_t)best);
-    float l = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t hit = __ballot(key[i] == best);
+      if (!found && hit != 0) {
+        e = 64 * i + (int)__builtin_ctzll(hit);
+        found = true;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == e) { key[i] = 0; l = lv[i]; }
-    l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), e & 63));
-    if (lane == j) my_l = l;
+      if (lane + 64 * i == e) key[i] = 0u;
+    if (lane == j) my_l = key_logit(best);
     sel[j] = e;
   }
+}
+
+// Wave-level top-k of one token's E logits (E <= 256), formed from the S
+// router partials of each expert (added in slice order, plus the bias,
+// rounded once to fp32), by topk_rounds over order-preserving 32-bit images
+// of the logits.  All lanes return the same k experts in selection order
+// and, when asked, their gates: lane j forms exp(l_j - l_0) in fp64, the sum
+// runs over j in order, gate j = its term / sum, rounded to fp32.
+MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __restrict__ bias, int E, int k, int lane,
+                      int (&sel)[8], float (&gts)[8], bool want_gates) {
+  // every load is issued before the first use (indices clamped, results of
+  // lanes past E dropped), so the logits cost one memory round trip per slice
+  double a[4];
+  float b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = part[(int64_t)min(lane + 64 * i, E - 1) * S];
+  if (bias) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = bias[min(lane + 64 * i, E - 1)];
+  }
+  for (int s = 1; s < S; ++s) {
+    double p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = part[(int64_t)min(lane + 64 * i, E - 1) * S + s];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] += p[i];
+  }
+  uint32_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (bias) a[i] += (double)b[i];
+    key[i] = lane + 64 * i < E ? order_key32((float)a[i]) : 0u;
+  }
+  float my_l = 0.f;
+  topk_rounds(key, k, lane, sel, my_l);
   if (want_gates) {
     const double m = (double)__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(my_l)));
     const double ex = lane < k ? exp((double)my_l - m) : 0.0;

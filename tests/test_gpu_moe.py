@@ -204,3 +204,58 @@ def test_moe_decode_activation_outliers(orc_mt, key):
     assert np.max(np.abs(gates - g_ref)) <= 1e-6
     ratio = assert_within(y, y_ref, S, f"{key} outliers")
     say(f"[moe outliers] {key} max err/S {ratio:.2e}")
+
+
+def _tie_logits(E):
+    """Four logit vectors with exact ties placed across the four experts each
+    lane of the selecting wave holds (e, e + 64, e + 128, e + 192)."""
+    hi = E - 1
+    boundary = np.linspace(-1, 1, E).astype(np.float32)
+    boundary[[10, E - 28]] = 5.0
+    boundary[[70, 71, 72, E // 2 + 4, E // 2 + 5, E // 2 + 6, hi, 40]] = 3.0   # 8 values for 6 slots
+    equal = np.full(E, 0.5, dtype=np.float32)
+    zeros = np.full(E, -1.0, dtype=np.float32)
+    zeros[[3, 65, E // 2 + 2, hi - 1]] = -0.0
+    zeros[[4, 66, E // 2 + 3, hi]] = 0.0
+    e = np.arange(E)
+    inner = np.where(e >= E - 70, 0.25 * (e % 5), -1.0).astype(np.float32)   # ties straddle e = 64j
+    return [boundary, equal, zeros, inner]
+
+
+@pytest.mark.parametrize("key", ["c4_i4", "c3"])
+def test_layer_ties_through_decode(orc_mt, key):
+    """Exact logit ties through the layer's own decode path (the selection
+    inside the gate/up kernel), against the oracle: 4 tokens, each with one
+    tie pattern.  c4: the logits come from one router column per token;
+    c3: a zero router and the pattern in the bias (one pattern per call)."""
+    import moe_decode_amd as md
+    import torch
+    sp = W.spec(key)
+    base = moe_layer(key)
+    cases = _tie_logits(sp.E)
+    x = W.moe_x(sp, 4).copy()
+    calls = []
+    if sp.bias_std is None:
+        Wr = np.zeros((sp.E, sp.H), dtype=np.float32)
+        for t in range(4):
+            Wr[:, t] = cases[t]
+        x[:, :4] = np.eye(4, dtype=np.float32)
+        calls.append((Wr, None, x))
+    else:
+        for c in cases:
+            calls.append((np.zeros((sp.E, sp.H), dtype=np.float32), c, x[:1]))
+    for Wr, b, xt in calls:
+        T = xt.shape[0]
+        layer = md.MoELayer(sp.H, sp.F, sp.E, sp.k, sp.act, base.gate, base.up, base.down, _t(Wr),
+                            None if b is None else _t(b), base.shared)
+        idx = torch.empty(T, sp.k, dtype=torch.int32, device="cuda")
+        gates = torch.empty(T, sp.k, dtype=torch.float32, device="cuda")
+        y = md.moe_layer_forward(layer, _t(xt), idx=idx, gates=gates)
+        torch.cuda.synchronize()
+        i_ref, g_ref, _, _ = orc_mt.route_topk(xt, Wr, b, sp.k)
+        say(f"[moe ties] {key} T={T}: {i_ref.tolist()}")
+        assert np.array_equal(idx.cpu().numpy(), i_ref), (idx.cpu().numpy(), i_ref)
+        assert np.max(np.abs(gates.cpu().numpy() - g_ref)) <= 1e-6
+        experts = {int(e): W.moe_expert(sp, int(e)) for e in np.unique(i_ref)}
+        y_ref, _, _, S = orc_mt.moe_forward(sp.H, sp.F, sp.E, sp.k, sp.act, Wr, b, experts, W.moe_shared(sp), xt)
+        assert_within(y.cpu().numpy(), y_ref, S, f"{key} ties")
