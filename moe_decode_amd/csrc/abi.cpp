@@ -109,7 +109,7 @@ md::DigJob dig_job(const float* x, int R, int K, int fmt, const DigBuf& b) {
 
 // ---- MoE workspace layout ------------------------------------------------
 struct MoeWs {
-  size_t part, logits, idx, gates, n_active, active_e, active_off, pairs, pos, h, o, h_s, y_s, total;
+  size_t part, logits, idx, gates, n_active, active_e, active_off, pairs, pos, items, h, o, h_s, y_s, total;
   size_t x_hi, x_lo, h_hi, h_lo, hs_hi, hs_lo;  // bf16 pairs of the prefill path (block formats)
   size_t x_dig, x_exp, h_dig, h_exp, hs_dig, hs_exp;  // int8 digit planes (per-row formats)
   size_t xs_dig, xs_exp;  // x digits in the shared expert's order
@@ -164,6 +164,7 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
     w.fo = take(sizeof(float) * (size_t)T * (k + 1) * H);
     w.fctr = take(sizeof(int) * (size_t)md::fused_counter_words(T, k, H));
   } else {
+    w.items = take(sizeof(int4) * (size_t)md::max_tiles(T, k, max_active(T, E, k)));
     w.o = take(sizeof(float) * (size_t)T * k * H);
     w.x_hi = take(2 * (size_t)T * H);
     w.x_lo = take(2 * (size_t)T * H);
@@ -712,16 +713,18 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
 
   // a chunk of tokens: group the (token, slot) pairs by expert, then one
   // grouped GEMM per stage on the matrix cores, each expert read once
+  const int n_items = md::max_tiles(T, k, max_active(T, E, k));
   md::DispOut dout{static_cast<int*>(P(w.n_active)), static_cast<int*>(P(w.active_e)),
-                   static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos))};
+                   static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos)),
+                   static_cast<int4*>(P(w.items)), n_items};
   e = md::launch_select(part, rp, L->router_bias, T, E, k, logits, idx, gates, stream);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   e = md::launch_dispatch(idx, T, E, k, dout, stream);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
   if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
 
-  md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T};
-  const int A = max_active(T, E, k);
+  md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T, dout.items};
+  const int A = n_items;
   float* o = static_cast<float*>(P(w.o));
   if (row_type(fmt)) {
     int8_t* h_dig = static_cast<int8_t*>(P(w.h_dig));

@@ -43,16 +43,16 @@ namespace md {
 constexpr int kNRW = MD_DN_ROWS;   // output rows per workgroup in k_down_t1
 
 // The digit planes of rows [0, R) of a row-major R x K fp32 matrix (K a
-// multiple of 256), spread over the grid: each workgroup takes as few whole
-// groups as cover them all (at most 256 values per pass), grid-stride.
-MD_DEV void dig_rows(const DigJob& j, uint32_t* ys) {
+// multiple of 256), spread over nb workgroups (this one is b): each takes as
+// few whole groups as cover them all (at most 256 values per pass).
+MD_DEV void dig_rows(const DigJob& j, uint32_t* ys, int b, int nb) {
   if (!j.x) return;
   const int nv = dig_nv(j.fmt);
   const int64_t G = (int64_t)j.R * j.K / nv;
-  int64_t per = (G + gridDim.x - 1) / gridDim.x;
+  int64_t per = (G + nb - 1) / nb;
   if (per > 256 / nv) per = 256 / nv;
   if (per < 1) per = 1;
-  for (int64_t g0 = (int64_t)blockIdx.x * per; g0 < G; g0 += (int64_t)gridDim.x * per) {
+  for (int64_t g0 = (int64_t)b * per; g0 < G; g0 += (int64_t)nb * per) {
     const int cnt = (int)(G - g0 < per ? G - g0 : per);
     const int n = cnt * nv;
     const float v = (int)threadIdx.x < n ? j.x[g0 * nv + threadIdx.x] : 0.f;
@@ -65,9 +65,17 @@ MD_DEV void dig_rows(const DigJob& j, uint32_t* ys) {
   }
 }
 
+// Workgroups that one pass of dig_rows needs for a job (0 without a job).
+static int dig_blocks(const DigJob& j) {
+  if (!j.x) return 0;
+  const int nv = dig_nv(j.fmt);
+  const int64_t G = (int64_t)j.R * j.K / nv;
+  return (int)((G + 256 / nv - 1) / (256 / nv));
+}
+
 __global__ __launch_bounds__(256) void k_digits(DigJob j) {
   __shared__ uint32_t ys[256];
-  dig_rows(j, ys);
+  dig_rows(j, ys, blockIdx.x, gridDim.x);
 }
 
 hipError_t launch_digits(const DigJob& j, hipStream_t st) {
@@ -112,14 +120,24 @@ MD_DEV double wave_sum_f64_dpp(double v) {
 // sums are added in a fixed order into part[t][e][s].  The consumer adds the
 // S partials in order, then the bias, and rounds once to fp32.  A lane's
 // W_r values (at most kRV float4) are loaded once, before any product, and
-// each token's activations likewise.  The digit jobs and the zero job run
-// after the partials are written.
+// each token's activations likewise.  Workgroups past E*S run the digit jobs
+// and the zero job beside the router work.
 constexpr int kRV = 8;
 __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr, int E, int S,
                                                      double* __restrict__ part, DigJob j0, DigJob j1, ZeroJob z) {
   __shared__ double red[4][4];
   __shared__ uint32_t ys[256];
+  const int nr = E * S;
+  if ((int)blockIdx.x >= nr) {
+    // the activations' digit planes for the expert kernels (independent of the routing)
+    const int b = blockIdx.x - nr, nb = gridDim.x - nr;
+    if (b == 0)
+      for (int i = threadIdx.x; i < z.n; i += blockDim.x) z.p[i] = 0;
+    dig_rows(j0, ys, b, nb);
+    dig_rows(j1, ys, b, nb);
+    return;
+  }
   const int e = blockIdx.x / S, sl = blockIdx.x % S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ks = H / S / 4;             // elements per wave, a multiple of 64
@@ -165,8 +183,10 @@ __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const double v = wave_sum_f64_dpp(acc[b]);
-      if (lane == 0) red[wave][b] = v;
+      if (t0 + b < T) {
+        const double v = wave_sum_f64_dpp(acc[b]);
+        if (lane == 0) red[wave][b] = v;
+      }
     }
     __syncthreads();
     if (threadIdx.x < 4 && t0 + (int)threadIdx.x < T) {
@@ -175,11 +195,6 @@ __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x
     }
     __syncthreads();
   }
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < z.n; i += blockDim.x) z.p[i] = 0;
-  // the activations' digit planes for the expert kernels (independent of the routing)
-  dig_rows(j0, ys);
-  dig_rows(j1, ys);
 }
 
 #ifndef MD_ROUTER_BLOCKS
@@ -196,7 +211,9 @@ int router_splits(int H, int E) {
 
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
                               const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st) {
-  hipLaunchKernelGGL(k_router_part, dim3(E * S), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1, z);
+  int nd = dig_blocks(j0) > dig_blocks(j1) ? dig_blocks(j0) : dig_blocks(j1);
+  if (nd < 1 && z.n > 0) nd = 1;
+  hipLaunchKernelGGL(k_router_part, dim3(E * S + nd), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1, z);
   return hipGetLastError();
 }
 

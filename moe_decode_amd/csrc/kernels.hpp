@@ -19,6 +19,10 @@ struct Disp {
   const int* pairs;        // [T*k]  pair id at each position
   int k;                   // slots per token (1 for a dense FFN)
   int T;                   // tokens (dense FFN)
+  // [max_tiles(...)] work items of the grouped GEMMs, one per 16-position
+  // tile of an active expert: {expert, first position, end of the expert's
+  // positions, 0}, experts ascending, tiles ascending; expert -1 past the end
+  const int4* items;
 };
 
 struct DispOut {
@@ -27,7 +31,15 @@ struct DispOut {
   int* active_off;
   int* pairs;
   int* pos_of_pair;
+  int4* items;
+  int n_items_max;
 };
+
+constexpr int kTokTile = 16;  // positions per matrix-core tile of the grouped GEMMs
+
+// Bound on the work items: sum over active experts of ceil(n_e / 16) is at
+// most T*k / 16 + (active experts).
+inline int max_tiles(int T, int k, int n_active_max) { return n_active_max + (T * k + kTokTile - 1) / kTokTile; }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -164,7 +176,7 @@ hipError_t launch_moe_fused(const FusedLaunch& L, hipStream_t st);
 hipError_t launch_split_bf16(const float* x, int64_t n, unsigned short* hi, unsigned short* lo, hipStream_t st);
 bool mfma_supported(int K);
 hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
-                           const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d, int max_active,
+                           const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d, int n_items,
                            const unsigned short* a_hi, const unsigned short* a_lo, bool act_by_token, float* out,
                            unsigned short* out_hi, unsigned short* out_lo, hipStream_t st);
 
@@ -178,7 +190,7 @@ hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* y, h
 hipError_t launch_limbs(const float* a, int R, int K, bool perm4, int8_t* digits, int* expo, hipStream_t st);
 hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
                               const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d,
-                              int max_active, const int8_t* digits, const int* expo, bool act_by_token, float* out,
+                              int n_items, const int8_t* digits, const int* expo, bool act_by_token, float* out,
                               hipStream_t st);
 
 GemvCfg gateup_config(int fmt, int F, int H, int max_active, int T);

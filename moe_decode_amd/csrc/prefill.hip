@@ -8,9 +8,10 @@
 //
 // A block owns 64 weight rows of one active expert (gate/up stage: gate rows
 // f0..f0+31 and up rows f0..f0+31, so the activation fuses in the epilogue;
-// down stage: 64 output rows) and one tile of 16 of the expert's tokens
-// (blockIdx.z); an expert with more tokens has its rows streamed once per
-// tile, the repeats served mostly from the on-chip caches.  K runs in tiles of
+// down stage: 64 output rows) and one tile of 16 of the expert's tokens (the
+// work item blockIdx.y of the routing hand-off); an expert with more tokens
+// has its rows streamed once per tile, the repeats (adjacent work items)
+// served mostly from the on-chip caches.  K runs in tiles of
 // 256 weights: the next two tiles' weights, scales and activations are loaded
 // with coalesced 16-byte loads into registers while the current tile,
 // double-buffered in LDS, feeds the matrix cores.
@@ -33,7 +34,7 @@ typedef unsigned short u16;
 
 constexpr int kRows = 64;         // weight rows per block
 constexpr int kKT = 256;          // K tile (8 MFMA steps of 32)
-constexpr int kTok = 16;          // tokens per MFMA tile
+constexpr int kTok = kTokTile;    // tokens per MFMA tile
 constexpr int kAST = kKT + 8;     // LDS row stride of an activation tile (16-byte pad: the 16
                                   // token rows of one operand read land in distinct banks)
 
@@ -152,11 +153,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
   if (a.d.n_active == nullptr) {  // dense FFN: one expert, positions = tokens
     if (blockIdx.y != 0) return;
     er.e = 0; er.p0 = 0; er.p1 = a.d.T;
-  } else {
-    if ((int)blockIdx.y >= *a.d.n_active) return;
-    er.e = a.d.active_e[blockIdx.y];
-    er.p0 = a.d.active_off[blockIdx.y];
-    er.p1 = a.d.active_off[blockIdx.y + 1];
+  } else {  // work item blockIdx.y: one 16-position tile of an active expert
+    const int4 it = a.d.items[blockIdx.y];
+    if (it.x < 0) return;
+    er.e = it.x; er.p0 = it.y; er.p1 = it.z;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, li = lane & 15;
@@ -370,7 +370,7 @@ hipError_t launch_mfma_gemv(int fmt, const uint8_t* wq, const float* ws, int M, 
 }
 
 hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
-                           const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d, int max_active,
+                           const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d, int n_items,
                            const u16* a_hi, const u16* a_lo, bool act_by_token, float* out, u16* out_hi,
                            u16* out_lo, hipStream_t st) {
   MfmaArgs a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, a_hi, a_lo, act_by_token ? 1 : 0, out, out_hi, out_lo, 1};
@@ -379,8 +379,8 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
   const int RT = (fmt == Q4_0 || fmt == I4_ROW) ? 2 : 1;
   const int rows_per_block = (gateup ? 32 : 64) * RT;
   // token tiles: an expert holds at most T tokens (one per token)
-  const int tiles = (d.T + kTok - 1) / kTok;
-  const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.n_active ? max_active : 1, tiles);
+  const int tiles = d.items ? 1 : (d.T + kTok - 1) / kTok;
+  const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.items ? n_items : 1, tiles);
 #define MD_MF(F_, RT_) \
   if (fmt == F_ && RT == RT_) { \
     if (gateup) hipLaunchKernelGGL((k_moe_mfma<F_, 1, RT_>), grid, dim3(256), 0, st, a); \
@@ -504,11 +504,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
   if (a.d.n_active == nullptr) {
     if (blockIdx.y != 0) return;
     er.e = 0; er.p0 = 0; er.p1 = a.d.T;
-  } else {
-    if ((int)blockIdx.y >= *a.d.n_active) return;
-    er.e = a.d.active_e[blockIdx.y];
-    er.p0 = a.d.active_off[blockIdx.y];
-    er.p1 = a.d.active_off[blockIdx.y + 1];
+  } else {  // work item blockIdx.y: one 16-position tile of an active expert
+    const int4 it = a.d.items[blockIdx.y];
+    if (it.x < 0) return;
+    er.e = it.x; er.p0 = it.y; er.p1 = it.z;
   }
   const int t0 = er.p0 + (int)blockIdx.z * kTok;
   if (t0 >= er.p1) return;
@@ -667,20 +666,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
 
 hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
                               const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d,
-                              int max_active, const int8_t* digits, const int* expo, bool act_by_token, float* out,
+                              int n_items, const int8_t* digits, const int* expo, bool act_by_token, float* out,
                               hipStream_t st) {
   MfmaI8Args a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, digits, expo, act_by_token ? 1 : 0, out, 1};
   // int4 weights: two row tiles per wave (LDS reads of the activation digits
   // per weight byte halve); int8: one (its weight tiles are twice as large)
   const int RT = fmt == I4_ROW ? 2 : 1;
   const int rows_per_block = (gateup ? 32 : 64) * RT;
-  const int tiles = (d.T + kTok - 1) / kTok;
+  const int tiles = d.items ? 1 : (d.T + kTok - 1) / kTok;
   // row blocks per workgroup: short rows (few K tiles) stream several row
   // blocks back to back so the load pipeline's fill is paid once
   const int nkt = K / kKT;
   a.R = nkt >= 16 ? MD_I8_R_LONG : MD_I8_R_SHORT;
   const int nrb = (M + rows_per_block - 1) / rows_per_block;
-  const dim3 grid((nrb + a.R - 1) / a.R, d.n_active ? max_active : 1, tiles);
+  const dim3 grid((nrb + a.R - 1) / a.R, d.items ? n_items : 1, tiles);
 #define MD_MF8(F_, RT_) \
   if (fmt == F_ && RT == RT_) { \
     if (gateup) hipLaunchKernelGGL((k_moe_mfma_i8<F_, 1, RT_>), grid, dim3(256), 0, st, a); \

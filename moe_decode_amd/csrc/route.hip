@@ -194,10 +194,12 @@ hipError_t launch_select(const double* part, const RouterPlan& p, const float* b
 // expert.  Per-expert token bitmasks give each pair its rank among the pairs
 // of its expert (pairs of one expert are ordered by token, and a token
 // selects an expert at most once); exclusive scans give the offsets and the
-// list of active experts in ascending order.
+// list of active experts in ascending order, and the work items of the
+// grouped GEMMs (16-position tiles of each active expert).
 __global__ __launch_bounds__(1024) void k_dispatch(const int* __restrict__ idx, int T, int E, int k, DispOut d) {
   __shared__ uint32_t mask[256][4];
-  __shared__ int cnt[256], poff[256], apos[256];
+  __shared__ int cnt[256], poff[256], apos[256], ioff[256];
+  __shared__ int s_items;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 256 * 4; i += 1024) (&mask[0][0])[i] = 0u;
   __syncthreads();
@@ -212,25 +214,29 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int* __restrict__ idx, 
   }
   __syncthreads();
   if (wave == 0) {
-    int run_p = 0, run_a = 0;
+    int run_p = 0, run_a = 0, run_i = 0;
     for (int base = 0; base < 256; base += 64) {
       const int e = base + lane;
       const int c = cnt[e];
       const int a = c > 0 ? 1 : 0;
-      int ic = c, ia = a;  // inclusive scans across the wave
+      const int n = (c + kTokTile - 1) / kTokTile;
+      int ic = c, ia = a, in = n;  // inclusive scans across the wave
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const int pc = __shfl_up(ic, off, 64), pa = __shfl_up(ia, off, 64);
-        if (lane >= off) { ic += pc; ia += pa; }
+        const int pc = __shfl_up(ic, off, 64), pa = __shfl_up(ia, off, 64), pn = __shfl_up(in, off, 64);
+        if (lane >= off) { ic += pc; ia += pa; in += pn; }
       }
       poff[e] = run_p + ic - c;
       apos[e] = run_a + ia - a;
+      ioff[e] = run_i + in - n;
       run_p += __shfl(ic, 63, 64);
       run_a += __shfl(ia, 63, 64);
+      run_i += __shfl(in, 63, 64);
     }
     if (lane == 0) {
       *d.n_active = run_a;
       d.active_off[run_a] = T * k;
+      s_items = run_i;
     }
   }
   __syncthreads();
@@ -238,7 +244,10 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int* __restrict__ idx, 
     const int e = threadIdx.x;
     d.active_e[apos[e]] = e;
     d.active_off[apos[e]] = poff[e];
+    for (int i = 0; i * kTokTile < cnt[e]; ++i)
+      d.items[ioff[e] + i] = make_int4(e, poff[e] + i * kTokTile, poff[e] + cnt[e], 0);
   }
+  for (int i = s_items + (int)threadIdx.x; i < d.n_items_max; i += 1024) d.items[i] = make_int4(-1, 0, 0, 0);
   for (int p = threadIdx.x; p < T * k; p += 1024) {
     const int t = p / k, e = idx[p];
     int rank = 0;
