@@ -145,12 +145,57 @@ MD_DEV float dot_chunk(u32x4 w, const float* xv) {
   return a0 + a1;
 }
 
-// Sum over the L consecutive lanes of a lane group (L a power of two <= 64).
+// ---- lane exchanges without LDS traffic (gfx950)
+//
+// xor_lanes<OFF>(x): the value of lane (lane ^ OFF).  Quads and the 8-lane
+// halves of a row by DPP, across rows by the permlane swaps.
+template <int CTRL>
+MD_DEV float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int OFF>
+MD_DEV float xor_lanes(float x) {
+  if constexpr (OFF == 1) return dpp_f<0xB1>(x);        // quad_perm [1,0,3,2]
+  else if constexpr (OFF == 2) return dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  else if constexpr (OFF == 4)                          // swizzle, bit mode: and 0x1F, xor 4
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+  else if constexpr (OFF == 8) return dpp_f<0x128>(x);  // row_ror:8 (xor 8 within a row of 16)
+  else if constexpr (OFF == 16) {                       // rows 0<->1, 2<->3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(((threadIdx.x & 16) ? r[0] : r[1]));
+  } else {                                              // halves of the wave
+    static_assert(OFF == 32, "lane offset");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(((threadIdx.x & 32) ? r[0] : r[1]));
+  }
+}
+
+// Reduction over groups of 2*OFF lanes, one step: every lane combines its
+// value with one other lane's so that, after the steps OFF, OFF/2, ..., 1,
+// each lane holds the group's total.  Step 4 pairs lane i with i ^ 7 within
+// 8 lanes (the row half-mirror), which covers the same lanes together with
+// the steps 2 and 1 that follow it.
+template <int OFF, typename Op>
+MD_DEV float allreduce_step(float x, Op op) {
+  if constexpr (OFF == 4) return op(x, dpp_f<0x141>(x));  // row_half_mirror
+  else return op(x, xor_lanes<OFF>(x));
+}
+
+template <int OFF, typename Op>
+MD_DEV float allreduce_from(float x, Op op) {
+  if constexpr (OFF >= 1) return allreduce_from<OFF / 2>(allreduce_step<OFF>(x, op), op);
+  else return x;
+}
+
+// Sum / maximum over the L consecutive lanes of a lane group (L a power of
+// two <= 64), returned to every lane of the group.
 template <int L>
 MD_DEV float group_sum(float v) {
-#pragma unroll
-  for (int off = L / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  return allreduce_from<L / 2>(v, [](float x, float y) { return x + y; });
+}
+template <int L>
+MD_DEV float group_max(float v) {
+  return allreduce_from<L / 2>(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 MD_DEV double wave_sum_f64(double v) {

@@ -21,31 +21,49 @@ namespace md {
 #define MD_GU_RUN 0
 #endif
 
+// One level of the transposed butterfly: lanes with (t & OFF) == 0 return
+// a + a(partner), the others b + b(partner), partner = lane ^ OFF (the same
+// sums, bit for bit, in either formulation).
+template <int OFF>
+MD_DEV float butterfly_level(float a, float b, int t) {
+  if constexpr (OFF == 32) {
+    // r[0] = [a of lanes 0-31, b of lanes 0-31], r[1] = [a of 32-63, b of 32-63]
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (OFF == 16) {
+    // r[0] = [a row 0, b row 0, a row 2, b row 2], r[1] = [a row 1, b row 1, a row 3, b row 3]
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    // m = all ones on the upper lane of each pair: it sends a and keeps b;
+    // the lower lane the other way round.  Bit-field selects keep both
+    // candidates in registers (a select between array elements would be
+    // turned into a computed index and a chain of compares).
+    const uint32_t m = (t & OFF) ? 0xFFFFFFFFu : 0u;
+    const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    const float send = __uint_as_float((ua & m) | (ub & ~m));
+    const float keep = __uint_as_float((ub & m) | (ua & ~m));
+    return keep + xor_lanes<OFF>(send);
+  }
+}
+
+template <int N, int L, int S>
+MD_DEV void butterfly_levels(float (&v)[N], int t) {
+  if constexpr ((N >> S) > 1) {
+    constexpr int half = (N >> S) / 2, off = L >> (S + 1);
+#pragma unroll
+    for (int i = 0; i < half; ++i) v[i] = butterfly_level<off>(v[i], v[i + half], t);
+    butterfly_levels<N, L, S + 1>(v, t);
+  }
+}
+
 // Sum over the L lanes of a group for N rows at once.  On return lane t holds
 // the full sum of row (t / (L/N)) % N.
 template <int N, int L>
 MD_DEV float butterfly(float (&v)[N], int t) {
   static_assert(N <= L, "more rows than lanes");
-#pragma unroll
-  for (int s = 0; (N >> s) > 1; ++s) {
-    const int n = N >> s, half = n / 2, off = L >> (s + 1);
-    // m = all ones on the upper lane of each pair: it sends v[i] and keeps
-    // v[i + half]; the lower lane the other way round.  Bit-field inserts
-    // keep both candidates in registers (a select between array elements
-    // would be turned into a computed index and a chain of compares).
-    const uint32_t m = (t & off) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + half]);
-      const float send = __uint_as_float((a & m) | (b & ~m));
-      const float keep = __uint_as_float((b & m) | (a & ~m));
-      v[i] = keep + __shfl_xor(send, off, 64);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int off = L / (2 * N); off > 0; off >>= 1) r += __shfl_xor(r, off, 64);
-  return r;
+  butterfly_levels<N, L, 0>(v, t);
+  return group_sum<L / N>(v[0]);
 }
 
 template <int FMT, int CPL>
@@ -124,9 +142,7 @@ template <int FMT, bool kCoh = false>
 MD_DEV void dig_block(float v, int n, uint32_t* ys, u32x4* planes, float* scales) {
   using D = Dig<FMT>;
   const int q = threadIdx.x;
-  float m = q < n ? fabsf(v) : 0.f;
-#pragma unroll
-  for (int off = D::NV / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const float m = group_max<D::NV>(q < n ? fabsf(v) : 0.f);
   const int s = dig_shift<FMT>(m);
   if (q < n) {
     ys[q] = dig_biased<FMT>(v, s);
