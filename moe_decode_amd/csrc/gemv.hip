@@ -122,17 +122,21 @@ GemvCfg qgemv_config(int fmt, int N, int K, int batch) {
   c.L = pow2_divisor_le64(nc);
   c.B = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
   const int G = 64 / c.L;
-  // rows per lane group: as many as keep >= 2048 waves (more independent
-  // loads in flight per lane), then split K (uneven ranges allowed) until
-  // the grid has that many waves; every K-slice keeps >= 2 chunks per lane
+  // rows per lane group: about four 16-byte row chunks in flight per lane
+  // (measured: more makes each wave's chain longer than the extra overlap
+  // gains), fewer if the grid would then hold less than 1024 waves; K is
+  // split (uneven ranges allowed, a second pass adds the slices) only for
+  // grids still below that, every K-slice keeping >= 2 chunks per lane
   const int rmax = c.B <= 2 ? 4 : 2;
-  c.R = rmax;
+  const int cpl = nc / c.L;
+  c.R = 1;
+  while (c.R < rmax && 2 * c.R * cpl <= 4) c.R *= 2;
   auto blocks = [&](int R) { return (N + kWaves * G * R - 1) / (kWaves * G * R); };
-  while (c.R > 1 && (int64_t)blocks(c.R) * kWaves < 2048) c.R /= 2;
+  while (c.R > 1 && (int64_t)blocks(c.R) * kWaves < 1024) c.R /= 2;
   c.rows_per_block = kWaves * G * c.R;
   const int bx = blocks(c.R);
   c.S = 1;
-  while ((int64_t)bx * kWaves * c.S < 2048 && nc / (2 * c.S) >= 2 * c.L && c.S < 16) c.S *= 2;
+  while ((int64_t)bx * kWaves * c.S < 1024 && nc / (2 * c.S) >= 2 * c.L && c.S < 16) c.S *= 2;
   c.grid = dim3(bx, c.S);
   return c;
 }

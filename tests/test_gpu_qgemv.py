@@ -125,16 +125,26 @@ def test_one_hot_x_is_bitwise_one_weight(orc, fmt):
         assert np.array_equal(_run(m, x), y_ref), (fmt, c)
 
 
+def _split_matrix():
+    """A short, wide matrix (64 x 5632 Q8_0) that md_qgemv splits over K."""
+    import moe_decode_amd as md
+    from moe_decode_amd.upload import upload_matrix
+    m = upload_matrix(_random_qmatrix(np.random.default_rng(77), "q8_0", 64, 5632))
+    assert md.qgemv_workspace_size(m, 1) > 0, "expected the split-K path"
+    return m
+
+
 def test_deterministic_repeat():
     import moe_decode_amd as md
     import torch
     from synth.device import x_tensor
     sp = W.spec("c1")
-    x = x_tensor(W.dense_x(sp, 2048, 1))
-    a = md.qgemv(dense_matrix("c1", "k"), x)      # split-K path
-    b = md.qgemv(dense_matrix("c1", "k"), x)
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    for m in (dense_matrix("c1", "k"), _split_matrix()):
+        x = x_tensor(W.dense_x(sp, m.cols, 1))
+        a = md.qgemv(m, x)
+        b = md.qgemv(m, x)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("T", [9, 32, 128])
@@ -160,7 +170,7 @@ def test_qgemv_graph_replays_match_eager():
     import torch
     from synth.device import x_tensor
     sp = W.spec("c1")
-    mats = [dense_matrix("c1", "gate"), dense_matrix("c1", "k")]
+    mats = [dense_matrix("c1", "gate"), _split_matrix()]
     xs = [x_tensor(W.dense_x(sp, m.cols, 1, salt=3)) for m in mats]
     wss = [torch.empty(max(md.qgemv_workspace_size(m, 1), 1), dtype=torch.uint8, device="cuda") for m in mats]
     eager = [md.qgemv(m, x, workspace=w).clone() for m, x, w in zip(mats, xs, wss)]
