@@ -342,7 +342,9 @@ __global__ __launch_bounds__(512) void k_down_t1(DownT1 a) {
 // routed gate/up launch (its own format and geometry, same workgroup size),
 // and its down rows in the routed down launch as one more wave per workgroup,
 // added after the gated routed rows -- the same order and arithmetic as the
-// separate launches, in two launches fewer.
+// separate launches, in two launches fewer.  These layers are small (a few
+// waves per SIMD), so every wave issues all its row loads up front: one
+// memory round trip instead of a chain of them.
 struct SharedGU {
   const uint8_t* gq;
   const uint8_t* uq;
@@ -358,7 +360,7 @@ struct SharedGU {
 // Blocks [0, T*k*rtiles): routed pair bid / rtiles, row tile bid % rtiles;
 // then T*ntiles shared blocks (token, row tile).
 template <int FMT, int L, int kNP, int SFMT, int SL, int SNP>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_gateup_rs(GateUpT1 a,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gateup_rs(GateUpT1 a,
                                                                                              SharedGU sh,
                                                                                              int rtiles, int T) {
   extern __shared__ float lds[];
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
                    Fmt<FMT>::ROW ? a.gs + (int64_t)e * a.F : nullptr, Fmt<FMT>::ROW ? a.us + (int64_t)e * a.F : nullptr,
                    a.F, a.H, a.act, a.KS, a.RGW, a.xd + (int64_t)tok * ngx * D::NPL, a.xsc + (int64_t)tok * ngx,
                    a.hd + (int64_t)pair * ngh * D::NPL, a.hsc + (int64_t)pair * ngh};
-    gu_tile<FMT, L, kNP>(u, tile * (a.RGW * G * kNP), lds, ys);
+    gu_tile<FMT, L, kNP, false, kNP>(u, tile * (a.RGW * G * kNP), lds, ys);
   } else {
     using D = Dig<SFMT>;
     constexpr int G = 64 / SL;
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
     const GuTile u{sh.gq, sh.uq, sh.gs, sh.us, sh.F, a.H, sh.act, sh.KS, sh.RGW,
                    sh.xd + (int64_t)tok * ngx * D::NPL, sh.xsc + (int64_t)tok * ngx,
                    sh.hd + (int64_t)tok * ngh * D::NPL, sh.hsc + (int64_t)tok * ngh};
-    gu_tile<SFMT, SL, SNP>(u, tile * (sh.RGW * G * SNP), lds, ys);
+    gu_tile<SFMT, SL, SNP, false, SNP>(u, tile * (sh.RGW * G * SNP), lds, ys);
   }
 }
 
@@ -571,6 +573,7 @@ static bool rs_geom(int fmt, int H, int F, int sfmt, int Fs, int k, int T, RsGeo
   if (k + 1 > 9) return false;
   if (!gu_geom(fmt, F, H, T * k, g.r) || !gu_geom(sfmt, Fs, H, T, g.s)) return false;
   if (g.r.KS * g.r.RGW != g.s.KS * g.s.RGW) return false;   // one workgroup size
+  if (g.r.KS * g.r.RGW > 4) return false;                   // at most 256 threads (the kernel's bound)
   const int ncd = nchunks(fmt, F), ncs = nchunks(sfmt, Fs);
   g.Ld = pow2_div(ncd);
   g.Lsd = pow2_div(ncs);

@@ -275,7 +275,8 @@ MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __res
 // values, then 2*KS per row of slice sums) and leaves as digit planes of the
 // down matrix's format (the same format).  Waves past KS*RGW only take part
 // in the barriers; every thread of the workgroup must call it.  kCoh: the h
-// planes are read by other workgroups of the same launch.
+// planes are read by other workgroups of the same launch.  kWin: row pairs in
+// flight per lane group (kNP: every row load issued up front).
 struct GuTile {
   const uint8_t* Gm;      // the expert's gate matrix (device layout)
   const uint8_t* Um;      // its up matrix
@@ -288,7 +289,7 @@ struct GuTile {
   float* hsc;
 };
 
-template <int FMT, int L, int kNP, bool kCoh = false>
+template <int FMT, int L, int kNP, bool kCoh = false, int kWin = MD_GU_WINDOW>
 MD_DEV void gu_tile(const GuTile& a, int f0, float* lds, uint32_t* ys) {
   using D = Dig<FMT>;
   constexpr int G = 64 / L;
@@ -316,7 +317,7 @@ MD_DEV void gu_tile(const GuTile& a, int f0, float* lds, uint32_t* ys) {
     float pg[kNP], pu[kNP];
     {
       // rolling window: kD row pairs in flight while one pair is decoded
-      constexpr int kD = kNP < MD_GU_WINDOW ? kNP : MD_GU_WINDOW;
+      constexpr int kD = kNP < kWin ? kNP : kWin;
       RowBuf<FMT, 1> bg[kD], bu[kD];
       DigAcc<FMT> ra;  // one running state serves the gate and up rows alike
       auto rowp = [&](const uint8_t* M, int p) { return M + (int64_t)min(fb + p, a.F - 1) * rb; };
