@@ -47,7 +47,7 @@ constexpr int kMaxK = 8;
 constexpr int kMaxBatch = 8;
 // Up to this many tokens, every (token, slot) pair runs as its own one-token
 // problem in one launch; above it the pairs are grouped by expert.
-constexpr int kMaxPairT = 8;
+using md::kMaxPairT;
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -119,8 +119,16 @@ struct MoeWs {
 
 // Few tokens on shapes the one-token kernels cover: independent (token, slot)
 // pairs; otherwise the grouped GEMM on the matrix cores.
+// Measured crossover (MI355X, µs per layer call, one-token kernels vs grouped
+// GEMMs): 256 experts of 19 MB (int4): 10 tokens 355 vs 354, 12: 410 vs 398;
+// of 38 MB (int8): 10 tokens 554 vs 539; 128 experts of 2.65 MB with a shared
+// expert: 12 tokens 122 vs 148, 16: 158 vs 163.
+int pair_limit(const md_moe_layer* L) {
+  const int64_t expert = 2 * (int64_t)L->F * md::row_bytes(L->type, L->H) + (int64_t)L->H * md::row_bytes(L->type, L->F);
+  return (int64_t)L->E * expert <= md::kSmallExpertSet ? md::kMaxPairTSmall : kMaxPairT;
+}
 bool use_pairs(const md_moe_layer* L, int T) {
-  return T <= kMaxPairT && md::t1_supported(L->type, L->H, L->F) &&
+  return T <= pair_limit(L) && md::t1_supported(L->type, L->H, L->F) &&
          (!L->has_shared || md::t1_supported(L->shared.gate.type, L->H, L->shared.gate.rows));
 }
 
@@ -128,9 +136,9 @@ bool use_pairs(const md_moe_layer* L, int T) {
 // set in the environment at call time (the separate one-token kernels are the
 // default: they are faster on the shapes measured so far).  The workspace
 // size does not depend on the choice.
-bool use_fused(const md_moe_layer* L) {
+bool use_fused(const md_moe_layer* L, int T) {
   const char* v = getenv("MD_FUSED");
-  if (!v || v[0] != '1') return false;
+  if (!v || v[0] != '1' || T > 8) return false;
   return md::fused_supported(L->type, L->H, L->F, L->has_shared ? L->shared.gate.type : 0,
                              L->has_shared ? L->shared.gate.rows : 0, L->has_shared != 0);
 }
@@ -140,7 +148,7 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
   const int E = L->E, k = L->k, H = L->H, F = L->F;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-  w.part = take(sizeof(double) * (size_t)T * E * md::router_plan(T, H, E).S);
+  w.part = take(sizeof(double) * (size_t)T * E * md::router_plan(T, H, E, use_pairs(L, T)).S);
   w.logits = take(sizeof(float) * T * E);
   w.idx = take(sizeof(int) * T * k);
   w.gates = take(sizeof(float) * T * k);
@@ -541,7 +549,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     // few tokens: the router kernel also writes x's digit planes; selection
     // happens inside the gate/up kernel, the combine inside the down kernel;
     // each (token, slot) pair is an independent one-token problem
-    const md::RouterPlan rp = md::router_plan(T, H, E);
+    const md::RouterPlan rp = md::router_plan(T, H, E, true);
     if (rp.gemm) return fail(MD_ERR_UNSUPPORTED, "router partial layout does not match the one-token kernels");
     double* part = static_cast<double*>(P(w.part));
     const DigBuf xd = dig_buf_at(ws + w.xd, fmt, T, H);
@@ -554,7 +562,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       shd = dig_buf_at(ws + w.shd, sfmt, T, L->shared.gate.rows);
       js = dig_job(x, T, H, sfmt, sxd);
     }
-    const bool fused = use_fused(L);
+    const bool fused = use_fused(L, T);
     md::ZeroJob zj{};
     if (fused) zj = md::ZeroJob{static_cast<int*>(P(w.fctr)), md::fused_counter_words(T, k, H)};
     if (!mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");

@@ -37,6 +37,18 @@ struct DispOut {
 
 constexpr int kTokTile = 16;  // positions per matrix-core tile of the grouped GEMMs
 
+// Most tokens per call on the one-token kernels ((token, slot) pairs; the
+// router's partial-sum plan); more go to the grouped GEMMs.
+#ifndef MD_MAX_PAIR_T
+#define MD_MAX_PAIR_T 8
+#endif
+constexpr int kMaxPairT = MD_MAX_PAIR_T;
+// The same for layers whose whole expert set is small (at most 512 MB): their
+// frequently chosen experts stay in the 256 MB Infinity Cache, so re-reading
+// an expert once per (token, slot) pair stays cheaper than grouping.
+constexpr int kMaxPairTSmall = 16;
+constexpr int64_t kSmallExpertSet = int64_t(512) << 20;
+
 // Bound on the work items: sum over active experts of ceil(n_e / 16) is at
 // most T*k / 16 + (active experts).
 inline int max_tiles(int T, int k, int n_active_max) { return n_active_max + (T * k + kTokTile - 1) / kTokTile; }
@@ -86,7 +98,9 @@ struct RouterPlan {
   int S;
   int64_t ps, pt, pe;
 };
-RouterPlan router_plan(int T, int H, int E);
+// pairs: the one-token kernels consume the partials (partial-sum plan for any
+// T up to kMaxPairTSmall); otherwise the plan follows T alone.
+RouterPlan router_plan(int T, int H, int E, bool pairs = false);
 int router_splits(int H, int E);
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
                               const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st);

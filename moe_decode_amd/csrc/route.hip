@@ -92,9 +92,9 @@ __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x
 #define MD_ROUTER_GEMM_BLOCKS 256
 #endif
 
-RouterPlan router_plan(int T, int H, int E) {
+RouterPlan router_plan(int T, int H, int E, bool pairs) {
   RouterPlan p{};
-  if (T <= 8) {  // one block per (expert, K-slice); partials [t][e][s]
+  if (T <= kMaxPairT || (pairs && T <= kMaxPairTSmall)) {  // one block per (expert, K-slice); partials [t][e][s]
     p.gemm = false;
     p.S = router_splits(H, E);
     p.ps = 1;

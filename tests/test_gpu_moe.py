@@ -97,7 +97,10 @@ def _moe_gpu(key, x):
 
 
 @pytest.mark.parametrize("key,T", [("c0", 1), ("c3", 1), ("c4_i4", 1), ("c4_i4", 4), ("c4_i8", 1), ("c4_i8", 4),
-                                   ("c3", 128)])
+                                   ("c3", 128),
+                                   # verify-sized batches: small layers stay on the one-token kernels up to
+                                   # 16 tokens, the large ones group by expert above 8
+                                   ("c0", 16), ("c3", 12), ("c3", 16), ("c4_i4", 12)])
 def test_moe_layer_matches_oracle(orc_mt, key, T):
     sp = W.spec(key)
     x = W.moe_x(sp, T)
