@@ -274,7 +274,7 @@ def main():
 
     modes = {}
     if args.modes:
-        for Tm in (1, 4, 128):
+        for Tm in (1, 4, 16, 128):   # 16: a speculative-decoding verify batch
             if Tm == T:
                 continue
             m = run_mode(layer, sp, Tm, max(10, args.steps // (4 if Tm > 1 else 1)), 5)
@@ -288,7 +288,7 @@ def main():
             m = run_dense(key, name, batch, max(20, args.steps), 10)
             modes[f"{key}_{name}_b{batch}"] = m
             log(f"[bench] {key} {name} batch {batch}: {m['ms_per_call'] * 1e3:.1f} us ({m['weight_GBps']:.0f} GB/s)")
-        for key, Ts in (("c4_i8", (1, 4, 128)), ("c3", (1, 128))):
+        for key, Ts in (("c4_i8", (1, 4, 128)), ("c3", (1, 16, 128))):
             s2 = W.spec(key)
             l2 = device_moe(s2)
             for T in Ts:
