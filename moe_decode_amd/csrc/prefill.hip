@@ -138,7 +138,8 @@ MD_DEV bf16x8 load_b(const u16* tile, int j, int s, int q) {
 #endif
 // RT: 16-row MFMA tiles per wave; each activation fragment read from LDS
 // feeds RT products (64*RT rows per block; gate/up: 32*RT gate + 32*RT up).
-template <int FMT, int GU, int RT>
+// LO: the activations carry a low bf16 half (a_lo != nullptr).
+template <int FMT, int GU, int RT, bool LO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES))) void k_moe_mfma(MfmaArgs a) {
   using TL = Tile<FMT>;
   constexpr int BR = 64 * RT;
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       ahi = a.a_hi + (int64_t)row * a.K;
       alo = a.a_lo ? a.a_lo + (int64_t)row * a.K : nullptr;
     }
-    const bool has_lo = a.a_lo != nullptr;
+    constexpr bool has_lo = LO;
     // two register sets: tile kt+1 waits in one while tile kt+2 is in flight
     u32x4 rw[2][WPT];
     u32x4 rs[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
@@ -261,11 +262,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
             z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
             if (has_lo) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              float d = h2f(s_sc[buf][(wr + 16 * rt + 4 * q + v) * 8 + s]);
-              if constexpr (FMT == Q4_0) d *= 0.0625f;
-              acc[rt][v] = fmaf(d, z[v], acc[rt][v]);
-            }
+            for (int v = 0; v < 4; ++v)
+              acc[rt][v] = fmaf(h2f(s_sc[buf][(wr + 16 * rt + 4 * q + v) * 8 + s]), z[v], acc[rt][v]);
           } else {
             acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rt], 0, 0, 0);
             if (has_lo) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rt], 0, 0, 0);
@@ -291,6 +289,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       __syncthreads();
     }
 
+    // 4-bit codes entered as 16 * value: one exact power-of-two scaling of
+    // the sums instead of one per step
+    if constexpr (FMT == Q4_0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[rt][v] *= 0.0625f;
+    }
     // epilogue: lane holds rows wr + 16 rt + 4q + v (v < 4) of token column li
     const int j = li;
     if constexpr (GU) {
@@ -363,8 +369,10 @@ hipError_t launch_mfma_gemv(int fmt, const uint8_t* wq, const float* ws, int M, 
   MfmaArgs a{wq, nullptr, ws, nullptr, 0, M, K, 0, d, a_hi, a_lo, 0, out, nullptr, nullptr, ks};
   const int RT = (fmt == Q4_0 || fmt == I4_ROW) ? 2 : 1;
   const dim3 grid((M + 64 * RT - 1) / (64 * RT), 1, ks);
-  if (fmt == Q8_0) hipLaunchKernelGGL((k_moe_mfma<Q8_0, 0, 1>), grid, dim3(256), 0, st, a);
-  else if (fmt == Q4_0) hipLaunchKernelGGL((k_moe_mfma<Q4_0, 0, 2>), grid, dim3(256), 0, st, a);
+  if (fmt == Q8_0 && a_lo) hipLaunchKernelGGL((k_moe_mfma<Q8_0, 0, 1, true>), grid, dim3(256), 0, st, a);
+  else if (fmt == Q8_0) hipLaunchKernelGGL((k_moe_mfma<Q8_0, 0, 1, false>), grid, dim3(256), 0, st, a);
+  else if (fmt == Q4_0 && a_lo) hipLaunchKernelGGL((k_moe_mfma<Q4_0, 0, 2, true>), grid, dim3(256), 0, st, a);
+  else if (fmt == Q4_0) hipLaunchKernelGGL((k_moe_mfma<Q4_0, 0, 2, false>), grid, dim3(256), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -381,12 +389,14 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
   // token tiles: an expert holds at most T tokens (one per token)
   const int tiles = d.items ? 1 : (d.T + kTok - 1) / kTok;
   const dim3 grid((M + rows_per_block - 1) / rows_per_block, d.items ? n_items : 1, tiles);
+  // (the per-row formats take the int8 path below)
+  if (!a_lo) return hipErrorInvalidValue;
 #define MD_MF(F_, RT_) \
   if (fmt == F_ && RT == RT_) { \
-    if (gateup) hipLaunchKernelGGL((k_moe_mfma<F_, 1, RT_>), grid, dim3(256), 0, st, a); \
-    else hipLaunchKernelGGL((k_moe_mfma<F_, 0, RT_>), grid, dim3(256), 0, st, a); \
+    if (gateup) hipLaunchKernelGGL((k_moe_mfma<F_, 1, RT_, true>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((k_moe_mfma<F_, 0, RT_, true>), grid, dim3(256), 0, st, a); \
     return hipGetLastError(); }
-  MD_MF(Q8_0, 1) MD_MF(Q4_0, 2) MD_MF(I8_ROW, 1) MD_MF(I4_ROW, 2)
+  MD_MF(Q8_0, 1) MD_MF(Q4_0, 2)
 #undef MD_MF
   return hipErrorInvalidValue;
 }
