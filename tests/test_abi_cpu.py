@@ -136,9 +136,9 @@ def test_ffn_and_layout_errors():
     L = md.lib()
     sz = ctypes.c_size_t(0)
     f = md.FFNDesc(0, _qm(rows=512, cols=256), _qm(rows=512, cols=256), _qm(rows=256, cols=512))
-    # fp32 h, then Q8_0 digit planes (64 B per 16 values) and their scales, of x and of h,
-    # each part rounded up to 256 bytes
-    want = 3 * 512 * 4 + (3 * 16 * 64 + 256) + (3 * 32 * 64 + 512)
+    # fp32 h, then Q8_0 digit planes (three planes of 16 B per 16 values) and their scales,
+    # of x and of h, each part rounded up to 256 bytes
+    want = 3 * 512 * 4 + (3 * 16 * 48 + 256) + (3 * 32 * 48 + 512)
     assert L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz)) == 0 and sz.value == want
     f.down = _qm(rows=256, cols=768)
     assert _status(L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz))) == "MD_ERR_SHAPE"
