@@ -263,7 +263,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void 
       int sel[8];
       float gts[8];
       const bool first = blockIdx.x == 0 && slot == 0;
-      wave_topk(a.part + (int64_t)tok * a.E * a.S, a.S, a.bias, a.E, a.k, lane, sel, gts, first);
+      wave_topk(a.part + (int64_t)tok * a.E * a.S, a.S, a.bias, a.E, a.k, lane, sel, gts, first, slot + 1);
       if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       int sel[8];
       float gts[8];
       const bool first = tile == 0 && slot == 0;
-      wave_topk(a.part + (int64_t)tok * a.E * a.S, a.S, a.bias, a.E, a.k, lane, sel, gts, first);
+      wave_topk(a.part + (int64_t)tok * a.E * a.S, a.S, a.bias, a.E, a.k, lane, sel, gts, first, slot + 1);
       if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {

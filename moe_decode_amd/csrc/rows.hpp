@@ -166,8 +166,10 @@ MD_DEV void dig_block(float v, int n, uint32_t* ys, u32x4* planes, float* scales
 // rows (each row of 16 lanes then holds its maximum), then the row broadcasts
 // carry it to lane 63, which is read back.
 MD_DEV uint32_t wave_max_u32(uint32_t v) {
+  // lanes a row broadcast does not write read 0, the identity of the maximum
+  // (so each lane move can fold into the max instruction as a DPP operand)
   auto step = [&](auto ctrl, auto row_mask) {
-    const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, decltype(ctrl)::value,
+    const uint32_t p = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctrl)::value,
                                                               decltype(row_mask)::value, 0xF, false);
     v = p > v ? p : v;
   };
@@ -193,12 +195,13 @@ MD_DEV float key_logit(uint32_t k) { return __uint_as_float((k & 0x80000000u) ? 
 // above it).  Each round takes the wave maximum of the keys; among the experts
 // that hold it (an exact tie) the lowest index wins: the first of the four
 // slots with a match, and within it the lowest lane.  sel[j] (every lane) is
-// the j-th winner; lane j's my_l is its logit.
-MD_DEV void topk_rounds(uint32_t (&key)[4], int k, int lane, int (&sel)[8], float& my_l) {
+// the j-th winner; lane j's my_l is its logit.  Only the first nr <= k
+// winners are formed (sel[j] = 0 for j >= nr).
+MD_DEV void topk_rounds(uint32_t (&key)[4], int nr, int lane, int (&sel)[8], float& my_l) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     sel[j] = 0;
-    if (j >= k) continue;
+    if (j >= nr) continue;
     const uint32_t best = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
     int e = 0;
     bool found = false;
@@ -221,11 +224,12 @@ MD_DEV void topk_rounds(uint32_t (&key)[4], int k, int lane, int (&sel)[8], floa
 // Wave-level top-k of one token's E logits (E <= 256), formed from the S
 // router partials of each expert (added in slice order, plus the bias,
 // rounded once to fp32), by topk_rounds over order-preserving 32-bit images
-// of the logits.  All lanes return the same k experts in selection order
-// and, when asked, their gates: lane j forms exp(l_j - l_0) in fp64, the sum
+// of the logits.  All lanes return the same experts in selection order (the
+// first min(k, need) of them; all k when the gates are asked for) and, when
+// asked, the gates: lane j forms exp(l_j - l_0) in fp64, the sum
 // runs over j in order, gate j = its term / sum, rounded to fp32.
 MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __restrict__ bias, int E, int k, int lane,
-                      int (&sel)[8], float (&gts)[8], bool want_gates) {
+                      int (&sel)[8], float (&gts)[8], bool want_gates, int need = 8) {
   // every load is issued before the first use (indices clamped, results of
   // lanes past E dropped), so the logits cost one memory round trip per slice
   double a[4];
@@ -250,7 +254,7 @@ MD_DEV void wave_topk(const double* __restrict__ part, int S, const float* __res
     key[i] = lane + 64 * i < E ? order_key32((float)a[i]) : 0u;
   }
   float my_l = 0.f;
-  topk_rounds(key, k, lane, sel, my_l);
+  topk_rounds(key, want_gates ? k : min(k, need), lane, sel, my_l);
   if (want_gates) {
     const double m = (double)__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(my_l)));
     const double ex = lane < k ? exp((double)my_l - m) : 0.0;
