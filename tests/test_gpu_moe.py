@@ -262,3 +262,39 @@ def test_layer_ties_through_decode(orc_mt, key):
         experts = {int(e): W.moe_expert(sp, int(e)) for e in np.unique(i_ref)}
         y_ref, _, _, S = orc_mt.moe_forward(sp.H, sp.F, sp.E, sp.k, sp.act, Wr, b, experts, W.moe_shared(sp), xt)
         assert_within(y.cpu().numpy(), y_ref, S, f"{key} ties")
+
+
+# Layers of unusual shape: widths that are odd multiples of 256, expert counts
+# that are not multiples of 64, k = 2, 3, 5, a shared expert outside the merged
+# family, and an int4 layer whose FFN width the one-token kernels do not take
+# (so every token count goes to the grouped GEMMs).
+_RAGGED = {
+    "q8_e40_k3": W.MoESpec("q8_e40_k3", 41, 1280, 768, 40, 3, "silu", "q8_0", (1e-3, 1e-2), 0.05, 0.5, (1,)),
+    "i4_e72_k5": W.MoESpec("i4_e72_k5", 42, 768, 1280, 72, 5, "gelu_tanh", "i4_row", (1e-3, 1e-2), 0.05, None, (1,)),
+    "q4_e24_k2_sh": W.MoESpec("q4_e24_k2_sh", 43, 1536, 512, 24, 2, "gelu_tanh", "q4_0", (1e-3, 2e-2), 0.05, None,
+                              (1,), shared_F=768, shared_fmt="q8_0", shared_d_range=(1e-3, 1e-2)),
+}
+_ragged_layers = {}
+
+
+@pytest.mark.parametrize("name", sorted(_RAGGED))
+@pytest.mark.parametrize("T", [1, 3, 9, 33])
+def test_moe_ragged_shapes(orc_mt, name, T):
+    import moe_decode_amd as md
+    import torch
+    from synth.device import device_moe
+    sp = _RAGGED[name]
+    if name not in _ragged_layers:
+        _ragged_layers[name] = device_moe(sp)
+    layer = _ragged_layers[name]
+    x = W.moe_x(sp, T)
+    say(f"[moe ragged] {name} T={T}")
+    idx = torch.empty(T, sp.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, sp.k, dtype=torch.float32, device="cuda")
+    y = md.moe_layer_forward(layer, _t(x), idx=idx, gates=gates)
+    torch.cuda.synchronize()
+    y_ref, i_ref, g_ref, S = oracle_moe(orc_mt, sp, x)
+    assert np.array_equal(idx.cpu().numpy(), i_ref)
+    assert np.max(np.abs(gates.cpu().numpy() - g_ref)) <= 1e-6
+    ratio = assert_within(y.cpu().numpy(), y_ref, S, f"{name} T={T}")
+    say(f"[moe ragged] {name} T={T} max err/S {ratio:.2e}")
