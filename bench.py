@@ -216,6 +216,63 @@ def run_dense(key, name, batch, steps, warmup):
             "weight_GBps": nbytes / (ms / 1e3) / 1e9}
 
 
+def run_stack(key, n_layers, reps):
+    """A stack of n_layers distinct layers of workload `key`, one token, each
+    layer's output added to its input (md_moe_layer_forward_residual),
+    captured in one HIP graph;
+    the graph's replay is timed: per-layer time at model depth with no host
+    work between layers.  The selected experts of all layers (n_layers x k
+    experts) far exceed the Infinity Cache, so each replay reads HBM."""
+    from dataclasses import replace
+    import numpy as np
+    import torch
+    import moe_decode_amd as md
+    from synth import workloads as W
+    from synth.device import device_moe
+    base = W.spec(key)
+    specs = [replace(base, key=f"{key}_layer{l}", variant=base.variant + 100 + l) for l in range(n_layers)]
+    t_gen = time.perf_counter()
+    layers = [device_moe(sp) for sp in specs]
+    torch.cuda.synchronize()
+    log(f"[bench] stack of {n_layers} {key} layers resident ({time.perf_counter() - t_gen:.1f} s)")
+    T = 1
+    x = torch.from_numpy(np.random.default_rng([base.index, 780]).standard_normal((T, base.H)).astype(np.float32))
+    x = x.cuda()
+    wss = [torch.empty(md.moe_workspace_size(l, T), dtype=torch.uint8, device="cuda") for l in layers]
+    curs = [x] + [torch.empty(T, base.H, device="cuda") for _ in layers]
+
+    def run():
+        for l, layer in enumerate(layers):  # the residual joins each layer's last kernel
+            md.moe_layer_forward(layer, curs[l], y=curs[l + 1], workspace=wss[l], residual=curs[l])
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            run()
+    torch.cuda.current_stream().wait_stream(s_)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    nbytes = n_layers * (base.k * base.expert_bytes() + base.router_bytes())
+    del g, layers
+    torch.cuda.empty_cache()
+    return {"workload": key, "layers": n_layers, "tokens": T, "ms_per_stack": ms,
+            "us_per_layer": ms * 1e3 / n_layers, "tokens_per_s": T / (ms / 1e3),
+            "weight_GBps": nbytes / (ms / 1e3) / 1e9,
+            "timing": "HIP graph of the stack (layer forward with the residual add per layer), replayed"}
+
+
 def copy_calibration(nbytes=1 << 30):
     """A plain 16-byte copy kernel of known size (the library's per-row-format
     layout pass, which is a copy): reads nbytes, writes nbytes."""
@@ -242,6 +299,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--modes", action="store_true", help="also time the other layer shapes")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--stack", type=int, default=0,
+                    help="also time a stack of this many distinct layers (one token) captured in one HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -346,6 +405,9 @@ def main():
     }
     if modes:
         out["modes"] = modes
+    if args.stack > 0:
+        out["stack"] = run_stack(args.workload, args.stack, 20)
+        log(f"[bench] stack: {out['stack']['us_per_layer']:.1f} us per layer")
     print(json.dumps(out))
 
 

@@ -196,6 +196,28 @@ md_status md_moe_layer_forward_timed(const md_moe_layer *L /*host*/, const float
                                      void *workspace, size_t workspace_bytes, hipStream_t stream,
                                      int32_t stage, hipEvent_t start, hipEvent_t stop);
 
+/* md_moe_layer_forward with a residual: y = residual + layer(x), residual an
+ * fp32 [T][H] device buffer (it may be x or y itself).  The residual is added
+ * in the layer's last kernel (the down projection or the combine, after the
+ * shared expert's output), so layers stack without an extra launch each (the
+ * Camelid README, "Gemma 4": resident layer weights and a captured decode
+ * graph).  Errors: as md_moe_layer_forward; a null residual ->
+ * MD_ERR_INVALID_ARG; not 16-byte aligned -> MD_ERR_ALIGNMENT. */
+md_status md_moe_layer_forward_residual(const md_moe_layer *L /*host*/, const float *x, int32_t T,
+                                        const float *residual, float *y, int32_t *idx_out, float *gates_out,
+                                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* y = a + b over n fp32 values (device pointers; y may alias a or b): the
+ * residual add that joins stacked layers, so a stack of layers (each layer's
+ * output added to its input) runs as one sequence of this library's kernels
+ * that a caller can capture in a HIP graph and replay without host
+ * synchronization (the Camelid README, "Gemma 4": a GPU-resident decode path
+ * with resident layer weights and a captured decode graph; "Ornith 1.0 9B": a
+ * device-side decode loop, the host synchronizing once per token chunk).
+ * Errors: n <= 0 -> MD_ERR_SHAPE; a null pointer -> MD_ERR_INVALID_ARG;
+ * pointers not 16-byte aligned -> MD_ERR_ALIGNMENT. */
+md_status md_add(const float *a, const float *b, float *y, int64_t n, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ STATUS = {0: "MD_OK", 1: "MD_ERR_INVALID_ARG", 2: "MD_ERR_SHAPE", 3: "MD_ERR_UNS
 EXPORTS = ("md_abi_version", "md_status_string", "md_last_error_detail", "md_row_bytes", "md_prepare_layout",
            "md_qgemv_workspace_size", "md_qgemv", "md_route_workspace_size", "md_moe_route_topk",
            "md_ffn_workspace_size", "md_ffn_forward", "md_moe_workspace_size", "md_moe_layer_forward",
-           "md_moe_layer_forward_timed")
+           "md_moe_layer_forward_timed", "md_moe_layer_forward_residual", "md_add")
 STAGES = {"shared": 0, "router": 1, "select": 2, "gateup": 3, "down": 4, "combine": 5}
 
 
@@ -81,6 +81,8 @@ def lib():
             "md_moe_workspace_size": (i32, [vp, i32, psz]),
             "md_moe_layer_forward": (i32, [vp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "md_moe_layer_forward_timed": (i32, [vp, vp, i32, vp, vp, vp, vp, sz, vp, i32, vp, vp]),
+            "md_moe_layer_forward_residual": (i32, [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "md_add": (i32, [vp, vp, vp, ctypes.c_int64, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -258,7 +260,9 @@ def moe_workspace_size(layer, T):
     return need.value
 
 
-def moe_layer_forward(layer, x, y=None, idx=None, gates=None, workspace=None, stream=None):
+def moe_layer_forward(layer, x, y=None, idx=None, gates=None, workspace=None, stream=None, residual=None):
+    """y = layer(x), or residual + layer(x) when a residual ([T][H] fp32,
+    possibly x or y) is given."""
     import torch
     T = x.shape[0]
     dev = x.device
@@ -266,8 +270,12 @@ def moe_layer_forward(layer, x, y=None, idx=None, gates=None, workspace=None, st
     if y is None:
         y = torch.empty(T, layer.H, dtype=torch.float32, device=dev)
     ws, wsb = _workspace(moe_workspace_size(layer, T), dev, workspace)
-    _check(lib().md_moe_layer_forward(ctypes.byref(d), _ptr(x), T, _ptr(y), _ptr(idx), _ptr(gates), _ptr(ws), wsb,
-                                      _stream(stream)))
+    if residual is None:
+        _check(lib().md_moe_layer_forward(ctypes.byref(d), _ptr(x), T, _ptr(y), _ptr(idx), _ptr(gates), _ptr(ws), wsb,
+                                          _stream(stream)))
+    else:
+        _check(lib().md_moe_layer_forward_residual(ctypes.byref(d), _ptr(x), T, _ptr(residual), _ptr(y), _ptr(idx),
+                                                   _ptr(gates), _ptr(ws), wsb, _stream(stream)))
     return y
 
 
@@ -288,3 +296,12 @@ def moe_layer_forward_timed(layer, x, stage, start, stop, y=None, idx=None, gate
                                             stop.cuda_event))
     return y
 
+
+def add(a, b, out=None, stream=None):
+    """out = a + b (fp32 tensors of the same size on the device): the residual
+    add between stacked layers."""
+    import torch
+    if out is None:
+        out = torch.empty_like(a)
+    _check(lib().md_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
+    return out

@@ -115,6 +115,7 @@ struct MoeWs {
   size_t xs_dig, xs_exp;  // x digits in the shared expert's order
   size_t xd, sxd, hd, shd;  // digit planes of x and h for the one-token kernels (routed, shared formats)
   size_t fo, fctr;          // fused kernel: per-pair down outputs, counters
+  size_t rcopy;             // the residual's copy where y, which it may be, is written before it is added
 };
 
 // Few tokens on shapes the one-token kernels cover: independent (token, slot)
@@ -171,6 +172,7 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
     }
     w.fo = take(sizeof(float) * (size_t)T * (k + 1) * H);
     w.fctr = take(sizeof(int) * (size_t)md::fused_counter_words(T, k, H));
+    w.rcopy = take(sizeof(float) * (size_t)T * H);
   } else {
     w.items = take(sizeof(int4) * (size_t)md::max_tiles(T, k, max_active(T, E, k)));
     w.o = take(sizeof(float) * (size_t)T * k * H);
@@ -513,9 +515,10 @@ md_status md_moe_workspace_size(const md_moe_layer* L, int32_t T, size_t* bytes)
   return ok();
 }
 
+// residual: nullable [T][H], added to y (it may be y itself).
 static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
                              float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                             int32_t stage, hipEvent_t ev0, hipEvent_t ev1) {
+                             int32_t stage, hipEvent_t ev0, hipEvent_t ev1, const float* residual = nullptr) {
   md_status s = check_moe(L, T);
   if (s != MD_OK) return s;
   if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
@@ -563,6 +566,16 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       js = dig_job(x, T, H, sfmt, sxd);
     }
     const bool fused = use_fused(L, T);
+    // the paths that add the residual in a launch of its own after y is
+    // written keep a copy of it when it is y itself
+    const float* res_late = residual;
+    auto keep_residual = [&]() -> bool {
+      if (residual != y) return true;
+      float* c = static_cast<float*>(P(w.rcopy));
+      if (md::launch_copy_f32(residual, c, (int64_t)T * H, stream) != hipSuccess) return false;
+      res_late = c;
+      return true;
+    };
     md::ZeroJob zj{};
     if (fused) zj = md::ZeroJob{static_cast<int*>(P(w.fctr)), md::fused_counter_words(T, k, H)};
     if (!mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
@@ -612,8 +625,13 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       fl.idx_out = idx;
       fl.gates_out = gates;
       fl.ctr = static_cast<int*>(P(w.fctr));
+      if (residual && !keep_residual()) return hip_fail(hipGetLastError(), "residual copy");
       e = md::launch_moe_fused(fl, stream);
       if (e != hipSuccess) return hip_fail(e, "fused launch");
+      if (residual) {
+        e = md::launch_add(y, res_late, y, (int64_t)T * H, stream);
+        if (e != hipSuccess) return hip_fail(e, "residual launch");
+      }
       if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0) || !mark(MD_STAGE_DOWN, ev1) ||
           !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
         return hip_fail(e, "event record");
@@ -647,7 +665,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       rl.sds = row_type(sf.gate.type) ? sf.down.row_scale : nullptr;
       rl.Fs = sf.gate.rows; rl.sact = sf.act;
       rl.sxd = sxd.planes; rl.sxsc = sxd.scales; rl.shd = shd.planes; rl.shsc = shd.scales;
-      rl.idx = idx; rl.gates = gates; rl.y = y;
+      rl.idx = idx; rl.gates = gates; rl.y = y; rl.residual = residual;
       e = md::launch_moe_rs(rl, stream);
       if (e != hipSuccess) return hip_fail(e, "routed+shared launch");
       if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0) || !mark(MD_STAGE_DOWN, ev1) ||
@@ -668,9 +686,14 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
                              xd.planes, xd.scales, hd.planes, hd.scales, idx, gates, stream);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
     if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
+    if (y_s && residual && !keep_residual()) return hip_fail(hipGetLastError(), "residual copy");
     e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
-                           gates, hd.planes, hd.scales, y_s, y, stream);
+                           gates, hd.planes, hd.scales, y_s ? y_s : residual, y, stream);
     if (e != hipSuccess) return hip_fail(e, "down launch");
+    if (y_s && residual) {  // the addend slot held the shared output
+      e = md::launch_add(y, res_late, y, (int64_t)T * H, stream);
+      if (e != hipSuccess) return hip_fail(e, "residual launch");
+    }
     if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
       return hip_fail(e, "event record");
     return ok();
@@ -760,7 +783,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
   if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0)) return hip_fail(e, "event record");
-  e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, y, stream);
+  e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, residual, y, stream);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   if (!mark(MD_STAGE_COMBINE, ev1)) return hip_fail(e, "event record");
   return ok();
@@ -776,6 +799,23 @@ md_status md_moe_layer_forward_timed(const md_moe_layer* L, const float* x, int3
                                      int32_t stage, hipEvent_t start, hipEvent_t stop) {
   if (stage < 0) return fail(MD_ERR_INVALID_ARG, "stage %d", stage);
   return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, stage, start, stop);
+}
+
+md_status md_moe_layer_forward_residual(const md_moe_layer* L, const float* x, int32_t T, const float* residual,
+                                        float* y, int32_t* idx_out, float* gates_out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (!residual) return fail(MD_ERR_INVALID_ARG, "residual is null");
+  if (!aligned16(residual)) return fail(MD_ERR_ALIGNMENT, "residual not 16-byte aligned");
+  return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr,
+                     residual);
+}
+
+md_status md_add(const float* a, const float* b, float* y, int64_t n, hipStream_t stream) {
+  if (n <= 0) return fail(MD_ERR_SHAPE, "n = %lld must be positive", (long long)n);
+  if (!a || !b || !y) return fail(MD_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(y)) return fail(MD_ERR_ALIGNMENT, "pointers not 16-byte aligned");
+  const hipError_t e = md::launch_add(a, b, y, n, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "add launch");
 }
 
 }  // extern "C"

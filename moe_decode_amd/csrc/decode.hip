@@ -443,6 +443,7 @@ __global__ __launch_bounds__(576) void k_down_rs(DownT1 a, SharedDN sh) {
       float v = 0.f;
       for (int q = 0; q < a.k; ++q) v = fmaf(a.gates[tok * a.k + q], red[q][threadIdx.x], v);
       v += red[a.k][threadIdx.x];
+      if (a.y_add) v += a.y_add[(int64_t)tok * a.H + i];  // the residual (may be y itself)
       a.y[(int64_t)tok * a.H + i] = v;
     }
   }
@@ -605,7 +606,8 @@ hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st) {
                      rtiles, L.T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  DownT1 d{L.dq, L.ds, L.dn_bytes, L.H, L.F, L.k, L.idx, L.gates, static_cast<const u32x4*>(L.hd), L.hsc, nullptr, L.y};
+  DownT1 d{L.dq, L.ds, L.dn_bytes, L.H, L.F, L.k, L.idx, L.gates, static_cast<const u32x4*>(L.hd), L.hsc, L.residual,
+           L.y};
   SharedDN sd{L.sdq, L.sds, L.Fs, static_cast<const u32x4*>(L.shd), L.shsc};
   hipLaunchKernelGGL((k_down_rs<Q4_0, 8, 3, Q8_0, 64, 2>), dim3((L.H + kNRW - 1) / kNRW, L.T), dim3(64 * (L.k + 1)), 0,
                      st, d, sd);

@@ -295,10 +295,11 @@ __global__ __launch_bounds__(kBlock) void k_down(const uint8_t* __restrict__ dq,
   }
 }
 
-// y[t][i] = sum_j g[t][j] * o[pos(t,j)][i]  (+ y_shared[t][i]), slot order.
+// y[t][i] = sum_j g[t][j] * o[pos(t,j)][i]  (+ y_shared[t][i]) (+ y_residual[t][i]),
+// slot order, then the shared output, then the residual.
 __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o, const int* __restrict__ pos_of_pair,
                                                     const float* __restrict__ gates, int T, int k, int H,
-                                                    const float* __restrict__ ys, float* __restrict__ y) {
+                                                    const float* __restrict__ ys, const float* yr, float* y) {
   const int H4 = H / 4;
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= (int64_t)T * H4) return;
@@ -311,6 +312,10 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
   }
   if (ys) {
     const float4 v = reinterpret_cast<const float4*>(ys + (int64_t)t * H)[c];
+    a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+  }
+  if (yr) {  // may be y itself: read before the write by the same thread
+    const float4 v = reinterpret_cast<const float4*>(yr + (int64_t)t * H)[c];
     a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
   }
   reinterpret_cast<float4*>(y + (int64_t)t * H)[c] = a;
@@ -406,11 +411,41 @@ hipError_t launch_down(int fmt, const GemvCfg& c, const uint8_t* dq, const float
   return hipErrorInvalidValue;
 }
 
+// y = a + b, fp32, n values (16-byte chunks, then the tail).
+__global__ __launch_bounds__(kBlock) void k_add(const float* __restrict__ a, const float* __restrict__ b,
+                                                float* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t n4 = n / 4;
+  if (i < n4) {
+    const float4 u = reinterpret_cast<const float4*>(a)[i], v = reinterpret_cast<const float4*>(b)[i];
+    reinterpret_cast<float4*>(y)[i] = make_float4(u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w);
+  } else if (i < n4 + (n & 3)) {
+    const int64_t j = 4 * n4 + (i - n4);
+    y[j] = a[j] + b[j];
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_copy_f32(const float* __restrict__ a, float* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i < n) y[i] = a[i];
+}
+
+hipError_t launch_copy_f32(const float* a, float* y, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, a, y, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_add(const float* a, const float* b, float* y, int64_t n, hipStream_t st) {
+  const int64_t threads = n / 4 + (n & 3);
+  hipLaunchKernelGGL(k_add, dim3((unsigned)((threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, a, b, y, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
-                          const float* y_shared, float* y, hipStream_t st) {
+                          const float* y_shared, const float* y_residual, float* y, hipStream_t st) {
   const int64_t n = (int64_t)T * (H / 4);
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, o, pos_of_pair,
-                     gates, T, k, H, y_shared, y);
+                     gates, T, k, H, y_shared, y_residual, y);
   return hipGetLastError();
 }
 

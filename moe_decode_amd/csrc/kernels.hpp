@@ -149,6 +149,7 @@ struct RsLaunch {
   int* idx;
   float* gates;
   float* y;
+  const float* residual;                    // added to y, or nullptr
 };
 bool rs_supported(int fmt, int H, int F, int sfmt, int Fs, int k, int T);
 hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st);
@@ -216,7 +217,9 @@ GemvCfg down_config(int fmt, int H, int F, int max_active, int T);
 hipError_t launch_down(int fmt, const GemvCfg& c, const uint8_t* dq, const float* ds, int64_t mat_bytes,
                        int H, int F, const Disp& d, const float* h, float* o, hipStream_t st);
 
+hipError_t launch_add(const float* a, const float* b, float* y, int64_t n, hipStream_t st);
+hipError_t launch_copy_f32(const float* a, float* y, int64_t n, hipStream_t st);
 hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
-                          const float* y_shared, float* y, hipStream_t st);
+                          const float* y_shared, const float* y_residual, float* y, hipStream_t st);
 
 }  // namespace md

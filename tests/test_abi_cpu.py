@@ -148,3 +148,22 @@ def test_ffn_and_layout_errors():
     assert _status(L.md_prepare_layout(md.Q8_0, 4, 256, 1, FAKE, FAKE_ODD, None)) == "MD_ERR_ALIGNMENT"
     assert _status(L.md_prepare_layout(md.Q8_0, 4, 100, 1, FAKE, FAKE + 4096, None)) == "MD_ERR_UNSUPPORTED"
     assert _status(L.md_prepare_layout(0, 4, 256, 1, FAKE, FAKE + 4096, None)) == "MD_ERR_INVALID_ARG"
+
+
+def test_add_errors():
+    L = md.lib()
+    assert _status(L.md_add(FAKE, FAKE, FAKE, 0, None)) == "MD_ERR_SHAPE"
+    assert _status(L.md_add(FAKE, None, FAKE, 8, None)) == "MD_ERR_INVALID_ARG"
+    assert _status(L.md_add(FAKE, FAKE_ODD, FAKE, 8, None)) == "MD_ERR_ALIGNMENT"
+
+
+def test_residual_forward_errors():
+    L = md.lib()
+    d = _layer()
+    f = L.md_moe_layer_forward_residual
+    assert _status(f(ctypes.byref(d), FAKE, 1, None, FAKE, None, None, FAKE, 1 << 30, None)) == "MD_ERR_INVALID_ARG"
+    assert _status(f(ctypes.byref(d), FAKE, 1, FAKE_ODD, FAKE, None, None, FAKE, 1 << 30, None)) == "MD_ERR_ALIGNMENT"
+    # the layer's own checks still apply
+    assert _status(f(ctypes.byref(d), FAKE, 0, FAKE, FAKE, None, None, FAKE, 1 << 30, None)) == "MD_ERR_SHAPE"
+    bad = _layer(k=9)
+    assert _status(f(ctypes.byref(bad), FAKE, 1, FAKE, FAKE, None, None, FAKE, 1 << 30, None)) == "MD_ERR_SHAPE"
