@@ -273,6 +273,9 @@ _RAGGED = {
     "i4_e72_k5": W.MoESpec("i4_e72_k5", 42, 768, 1280, 72, 5, "gelu_tanh", "i4_row", (1e-3, 1e-2), 0.05, None, (1,)),
     "q4_e24_k2_sh": W.MoESpec("q4_e24_k2_sh", 43, 1536, 512, 24, 2, "gelu_tanh", "q4_0", (1e-3, 2e-2), 0.05, None,
                               (1,), shared_F=768, shared_fmt="q8_0", shared_d_range=(1e-3, 1e-2)),
+    # the widest hidden size the library takes (16384)
+    "q8_h16384": W.MoESpec("q8_h16384", 44, 16384, 256, 8, 2, "gelu_tanh", "q8_0", (1e-3, 1e-2), 0.05, None, (1,)),
+    "i4_h16384": W.MoESpec("i4_h16384", 45, 16384, 512, 16, 4, "silu", "i4_row", (1e-3, 1e-2), 0.05, 0.5, (1,)),
 }
 _ragged_layers = {}
 

@@ -191,3 +191,28 @@ def test_qgemv_graph_replays_match_eager():
         torch.cuda.synchronize()
         for y, e in zip(ys, eager):
             assert torch.equal(y, e), f"replay {rep}"
+
+
+@pytest.mark.parametrize("fmt", F.FORMATS)
+@pytest.mark.parametrize("batch", [1, 8])
+def test_qgemv_widest_rows(orc_mt, fmt, batch):
+    """The widest rows the library takes (16384 columns)."""
+    rng = np.random.default_rng([31, F.FORMATS.index(fmt), batch])
+    m = _random_qmatrix(rng, fmt, 48, 16384)
+    x = rng.standard_normal((batch, 16384)).astype(np.float32)
+    y_ref, S = orc_mt.qgemv(m, x)
+    assert_within(_run(m, x), y_ref, S, f"{fmt} 48x16384 b{batch}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "i8_row"])
+def test_qgemv_most_rows(orc_mt, fmt):
+    """The most rows the library takes (65536); every 97th row is compared."""
+    rng = np.random.default_rng([32, F.FORMATS.index(fmt)])
+    m = _random_qmatrix(rng, fmt, 65536, 256)
+    x = rng.standard_normal((2, 256)).astype(np.float32)
+    y = _run(m, x)
+    rows = np.arange(0, 65536, 97)
+    sub = F.QMatrix(fmt=m.fmt, rows=len(rows), cols=m.cols, data=np.ascontiguousarray(m.data[rows]),
+                    scales=None if m.scales is None else np.ascontiguousarray(m.scales[rows]))
+    y_ref, S = orc_mt.qgemv(sub, x)
+    assert_within(y[:, rows], y_ref, S, f"{fmt} 65536x256 sampled rows")
