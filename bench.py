@@ -52,9 +52,12 @@ def gateup_bytes(sp, idx):
     return len(np.unique(idx)) * 2 * matrix_bytes(sp.fmt, sp.F, sp.H)
 
 
-def run_mode(layer, sp, T, steps, warmup, stage="gateup"):
+def run_mode(layer, sp, T, steps, warmup, stage="gateup", graph=False):
     """Time `steps` forwards of T tokens (token pools cycled).  Returns a dict
-    with per-step ms, tokens/s, weight bytes and the stage's event time."""
+    with per-step ms, tokens/s, weight bytes, the stage's event time, the
+    per-step event-time percentiles and the host time per call; with graph,
+    also the time per step of the same sequence of forwards captured in one
+    HIP graph and replayed back to back."""
     import numpy as np
     import torch
     import moe_decode_amd as md
@@ -79,18 +82,51 @@ def run_mode(layer, sp, T, steps, warmup, stage="gateup"):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
+    h0 = time.perf_counter()
     for i in range(steps):
         md.moe_layer_forward(layer, xs[i % pool], y=y, idx=idx[i % pool], gates=gates, workspace=ws)
+    host_s = time.perf_counter() - h0
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    # the same steps again with HIP events around one stage on the kernels' stream
+    # the same steps again with HIP events around one stage (recorded by the
+    # library on the kernels' stream)
     for i in range(steps):
         a, b = ev[i]
         md.moe_layer_forward_timed(layer, xs[i % pool], stage, a, b, y=y, idx=idx[i % pool], gates=gates,
                                    workspace=ws)
     torch.cuda.synchronize()
     stage_ms = [a.elapsed_time(b) for a, b in ev]
+    # per-step percentiles from a third pass with one event between
+    # consecutive steps (step i = the interval from event i to event i+1)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    sev[0].record()
+    for i in range(steps):
+        md.moe_layer_forward(layer, xs[i % pool], y=y, idx=idx[i % pool], gates=gates, workspace=ws)
+        sev[i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(steps)])
+    graph_ms = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s_ = torch.cuda.Stream()
+        s_.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_):
+            with torch.cuda.graph(g, stream=s_):
+                for i in range(steps):
+                    md.moe_layer_forward(layer, xs[i % pool], y=y, idx=idx[i % pool], gates=gates, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s_)
+        g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(3):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (3 * steps)
+        del g
     idx_np = idx.cpu().numpy()
     wb = [step_weight_bytes(sp, idx_np[i % pool]) for i in range(steps)]
     gb = [gateup_bytes(sp, idx_np[i % pool]) for i in range(steps)]
@@ -103,6 +139,9 @@ def run_mode(layer, sp, T, steps, warmup, stage="gateup"):
         "stage_bytes_avg": float(np.mean(gb)),
         "stage_GBps": float(np.sum(gb)) / (np.sum(stage_ms) / 1e3) / 1e9,
         "pool": pool,
+        "step_ms_p10_p50_p90": [float(v) for v in np.percentile(step_ms, [10, 50, 90])],
+        "host_us_per_call": host_s / steps * 1e6,
+        "graph_ms_per_step": graph_ms,
     }
 
 
@@ -157,17 +196,23 @@ def traffic_record(kernel, workload):
     text = open(path).read()
     m = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
     h = re.search(r"^source_sha256:\s*([0-9a-f]+)\s*$", text, re.M)
-    if not m or not h or h.group(1) != kernel_source_hash():
+    if not m or not h or h.group(1) != kernel_source_hash(kernel):
         return None
     return float(m.group(1))
 
 
-def kernel_source_hash():
+KERNEL_SOURCE = {"k_gateup_t1": "decode.hip", "k_moe_mfma": "prefill.hip", "k_moe_mfma_i8": "prefill.hip"}
+
+
+def kernel_source_hash(kernel=None):
+    """SHA-256 of the source file that defines `kernel` and of every header
+    (all HIP/C++ sources when kernel is None)."""
     import hashlib
     d = os.path.join(ROOT, "moe_decode_amd", "csrc")
     hs = hashlib.sha256()
     for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
+        if name.endswith(".hpp") or (name.endswith((".hip", ".cpp")) and kernel is None) or \
+                name == KERNEL_SOURCE.get(kernel):
             hs.update(name.encode())
             hs.update(open(os.path.join(d, name), "rb").read())
     return hs.hexdigest()
@@ -273,6 +318,43 @@ def run_stack(key, n_layers, reps):
             "timing": "HIP graph of the stack (layer forward with the residual add per layer), replayed"}
 
 
+def hbm_probe(nbytes=4 << 30, reps=5):
+    """Attainable HBM read bandwidth: the library's streaming-read kernel over
+    a 4 GiB buffer of random bytes (16x the Infinity Cache), a short sweep of
+    grid sizes, each timed with HIP events over `reps` back-to-back reads."""
+    import torch
+    import moe_decode_amd as md
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sweep = []
+    for wg in (1024, 2048, 4096, 8192, 16384):
+        md.hbm_read_probe(src, sink, workgroups=wg)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            md.hbm_read_probe(src, sink, workgroups=wg)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        sweep.append({"workgroups": wg, "ms": ms, "GBps": nbytes / (ms / 1e3) / 1e9})
+    del src
+    torch.cuda.empty_cache()
+    best = max(sweep, key=lambda r: r["GBps"])
+    return {"bytes": nbytes, "reps": reps, "GBps": best["GBps"], "workgroups": best["workgroups"], "sweep": sweep}
+
+
+def environment():
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    return {"torch": torch.__version__, "hip": torch.version.hip, "device": pr.name,
+            "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "hbm_bytes": pr.total_memory, "kernel_source_sha256": kernel_source_hash(),
+            "host_cpus": os.cpu_count()}
+
+
 def copy_calibration(nbytes=1 << 30):
     """A plain 16-byte copy kernel of known size (the library's per-row-format
     layout pass, which is a copy): reads nbytes, writes nbytes."""
@@ -328,7 +410,7 @@ def main():
     log(f"[bench] {sp.key} resident in HBM ({time.time() - t:.1f} s to generate and upload)")
 
     T = args.tokens
-    r = run_mode(layer, sp, T, args.steps, args.warmup)
+    r = run_mode(layer, sp, T, args.steps, args.warmup, graph=(T == 1))
     log(f"[bench] {sp.key} T={T}: {r['ms_per_step'] * 1e3:.1f} us/step, gate/up {r['stage_ms_avg'] * 1e3:.1f} us")
 
     modes = {}
@@ -361,6 +443,9 @@ def main():
     if not args.no_cpu_baseline and T == 1:
         cpu = cpu_baseline(sp)
         log(f"[bench] oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
+
+    probe = hbm_probe()
+    log(f"[bench] HBM read probe: {probe['GBps']:.0f} GB/s over {probe['bytes'] >> 30} GiB")
 
     achieved = r["stage_bytes_avg"] / (r["stage_ms_avg"] / 1e3) / 1e9
     kernel = "k_gateup_t1" if T <= 8 else ("k_moe_mfma_i8" if sp.fmt.endswith("_row") else "k_moe_mfma")
@@ -400,8 +485,18 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": r["stage_bytes_avg"],
             "avg_launch_ms": r["stage_ms_avg"],
+            "hbm_read_probe_GBps": probe["GBps"],
+            "frac_of_probe": achieved / probe["GBps"],
         },
         "cpu_baseline": cpu,
+        "timing": {
+            "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
+            "graph_ms_per_step": r["graph_ms_per_step"],
+            "host_us_per_call": r["host_us_per_call"],
+            "weight_frac_of_probe": r["weight_GBps"] / probe["GBps"],
+            "hbm_read_probe": probe,
+        },
+        "env": environment(),
     }
     if modes:
         out["modes"] = modes

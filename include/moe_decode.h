@@ -218,6 +218,19 @@ md_status md_moe_layer_forward_residual(const md_moe_layer *L /*host*/, const fl
  * pointers not 16-byte aligned -> MD_ERR_ALIGNMENT. */
 md_status md_add(const float *a, const float *b, float *y, int64_t n, hipStream_t stream);
 
+/* Measurement aid: reads nbytes of device memory at src once, in address
+ * order, with every compute unit busy, and writes nothing unless some lane's
+ * xor of the 32-bit words it read equals key (then that lane stores key at
+ * sink[0]; for zeroed memory any nonzero key keeps sink untouched).  Timed over a buffer far larger than the caches it gives the HBM
+ * read bandwidth this device attains, the practical ceiling of the weight
+ * streams above (the Camelid README, "Gemma 4": GPU-resident decode runs at
+ * the memory-bandwidth wall).  workgroups: 0 picks the default (2048).
+ * Errors: null pointer -> MD_ERR_INVALID_ARG; nbytes 0 or not a multiple of
+ * 16 -> MD_ERR_SHAPE; src not 16-byte aligned -> MD_ERR_ALIGNMENT;
+ * workgroups < 0 or > 2^20 -> MD_ERR_INVALID_ARG. */
+md_status md_hbm_read_probe(const void *src, size_t nbytes, uint32_t key, uint32_t *sink, int32_t workgroups,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

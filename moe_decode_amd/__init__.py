@@ -22,7 +22,8 @@ STATUS = {0: "MD_OK", 1: "MD_ERR_INVALID_ARG", 2: "MD_ERR_SHAPE", 3: "MD_ERR_UNS
 EXPORTS = ("md_abi_version", "md_status_string", "md_last_error_detail", "md_row_bytes", "md_prepare_layout",
            "md_qgemv_workspace_size", "md_qgemv", "md_route_workspace_size", "md_moe_route_topk",
            "md_ffn_workspace_size", "md_ffn_forward", "md_moe_workspace_size", "md_moe_layer_forward",
-           "md_moe_layer_forward_timed", "md_moe_layer_forward_residual", "md_add")
+           "md_moe_layer_forward_timed", "md_moe_layer_forward_residual", "md_add",
+           "md_hbm_read_probe")
 STAGES = {"shared": 0, "router": 1, "select": 2, "gateup": 3, "down": 4, "combine": 5}
 
 
@@ -83,6 +84,7 @@ def lib():
             "md_moe_layer_forward_timed": (i32, [vp, vp, i32, vp, vp, vp, vp, sz, vp, i32, vp, vp]),
             "md_moe_layer_forward_residual": (i32, [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "md_add": (i32, [vp, vp, vp, ctypes.c_int64, vp]),
+            "md_hbm_read_probe": (i32, [vp, ctypes.c_size_t, ctypes.c_uint32, vp, i32, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -305,3 +307,12 @@ def add(a, b, out=None, stream=None):
         out = torch.empty_like(a)
     _check(lib().md_add(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
     return out
+
+
+def hbm_read_probe(src, sink, key=0xFFFFFFFF, workgroups=0, stream=None):
+    """Reads every byte of the device tensor src once (a bandwidth
+    measurement).  Nothing is written unless some lane's xor of the words it
+    read equals key: for zeroed src, any nonzero key leaves sink (a device
+    tensor of at least 4 bytes) untouched."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().md_hbm_read_probe(_ptr(src), nbytes, key, _ptr(sink), workgroups, _stream(stream)))

@@ -818,4 +818,16 @@ md_status md_add(const float* a, const float* b, float* y, int64_t n, hipStream_
   return e == hipSuccess ? ok() : hip_fail(e, "add launch");
 }
 
+md_status md_hbm_read_probe(const void* src, size_t nbytes, uint32_t key, uint32_t* sink, int32_t workgroups,
+                             hipStream_t stream) {
+  if (!src || !sink) return fail(MD_ERR_INVALID_ARG, "null pointer");
+  if (nbytes == 0 || nbytes % 16) return fail(MD_ERR_SHAPE, "nbytes = %zu must be a positive multiple of 16", nbytes);
+  if (!aligned16(src)) return fail(MD_ERR_ALIGNMENT, "src not 16-byte aligned");
+  if (workgroups < 0 || workgroups > (1 << 20))
+    return fail(MD_ERR_INVALID_ARG, "workgroups = %d outside 0..1048576", workgroups);
+  const hipError_t e = md::launch_read_probe(src, (int64_t)(nbytes / 16), key, sink,
+                                             workgroups ? workgroups : 2048, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "read probe launch");
+}
+
 }  // extern "C"

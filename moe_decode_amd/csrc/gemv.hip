@@ -441,6 +441,41 @@ hipError_t launch_add(const float* a, const float* b, float* y, int64_t n, hipSt
   return hipGetLastError();
 }
 
+// The attainable HBM read bandwidth, the practical ceiling of every weight
+// stream here: each workgroup reads tiles of kBlock x kProbeU 16-byte chunks,
+// all kProbeU loads of a lane issued before any is used, tiles taken in
+// address order across the grid.  Indexes past the end are clamped (the last
+// chunk is read again) so no load waits on a branch.  A lane stores the xor
+// of the words it read only when that equals `key`, which the caller picks so
+// that it does not happen for the data; the loads cannot be dropped.
+constexpr int kProbeU = 8;
+
+__global__ __launch_bounds__(kBlock) void k_read_probe(const uint4* __restrict__ src, int64_t n16, uint32_t key,
+                                                       uint32_t* sink) {
+  constexpr int64_t tile = (int64_t)kBlock * kProbeU;
+  uint32_t acc = 0;
+  for (int64_t base = (int64_t)blockIdx.x * tile; base < n16; base += (int64_t)gridDim.x * tile) {
+    uint4 v[kProbeU];
+#pragma unroll
+    for (int j = 0; j < kProbeU; ++j) {
+      const int64_t i = base + j * kBlock + threadIdx.x;
+      v[j] = src[i < n16 ? i : n16 - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < kProbeU; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == key) sink[0] = acc;
+}
+
+hipError_t launch_read_probe(const void* src, int64_t n16, uint32_t key, uint32_t* sink, int grid,
+                             hipStream_t st) {
+  const int64_t tiles = (n16 + (int64_t)kBlock * kProbeU - 1) / ((int64_t)kBlock * kProbeU);
+  const int g = (int)std::min<int64_t>(grid, tiles);
+  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)g), dim3(kBlock), 0, st, static_cast<const uint4*>(src), n16,
+                     key, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
                           const float* y_shared, const float* y_residual, float* y, hipStream_t st) {
   const int64_t n = (int64_t)T * (H / 4);

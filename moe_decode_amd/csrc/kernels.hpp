@@ -218,6 +218,10 @@ hipError_t launch_down(int fmt, const GemvCfg& c, const uint8_t* dq, const float
                        int H, int F, const Disp& d, const float* h, float* o, hipStream_t st);
 
 hipError_t launch_add(const float* a, const float* b, float* y, int64_t n, hipStream_t st);
+// Streams nbytes = 16 * n16 of src through the CUs with `grid` workgroups
+// (no write unless a lane's words xor to key).
+hipError_t launch_read_probe(const void* src, int64_t n16, uint32_t key, uint32_t* sink, int grid,
+                             hipStream_t st);
 hipError_t launch_copy_f32(const float* a, float* y, int64_t n, hipStream_t st);
 hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
                           const float* y_shared, const float* y_residual, float* y, hipStream_t st);

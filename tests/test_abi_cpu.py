@@ -157,6 +157,16 @@ def test_add_errors():
     assert _status(L.md_add(FAKE, FAKE_ODD, FAKE, 8, None)) == "MD_ERR_ALIGNMENT"
 
 
+def test_read_probe_errors():
+    L = md.lib()
+    f = L.md_hbm_read_probe
+    assert _status(f(None, 1024, 1, FAKE, 0, None)) == "MD_ERR_INVALID_ARG"
+    assert _status(f(FAKE, 1024, 1, None, 0, None)) == "MD_ERR_INVALID_ARG"
+    assert _status(f(FAKE, 0, 1, FAKE, 0, None)) == "MD_ERR_SHAPE"
+    assert _status(f(FAKE, 1000, 1, FAKE, 0, None)) == "MD_ERR_SHAPE"
+    assert _status(f(FAKE_ODD, 1024, 1, FAKE, 0, None)) == "MD_ERR_ALIGNMENT"
+    assert _status(f(FAKE, 1024, 1, FAKE, -1, None)) == "MD_ERR_INVALID_ARG"
+
 def test_residual_forward_errors():
     L = md.lib()
     d = _layer()

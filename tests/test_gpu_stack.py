@@ -49,6 +49,35 @@ def test_add_is_exact():
         assert np.array_equal(y.cpu().numpy(), a + b), n
 
 
+
+def test_read_probe_reads_everything():
+    """The bandwidth probe covers whole tiles, a ragged tail and grids larger
+    and smaller than the tile count; it writes only on a key match."""
+    import moe_decode_amd as md
+    import torch
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    for nbytes in (16, 16 * 1000, 1 << 20, (1 << 20) + 48):
+        src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        for wg in (0, 1, 3):
+            md.hbm_read_probe(src, sink, key=1, workgroups=wg)
+            torch.cuda.synchronize()
+            assert sink[0].item() == 7, (nbytes, wg)
+        # every lane's xor of zeroed memory is 0: key 0 must be stored
+        md.hbm_read_probe(src, sink, key=0)
+        torch.cuda.synchronize()
+        assert sink[0].item() == 0, nbytes
+        sink.fill_(7)
+    # one word set to 5 in the first, a middle and the last whole-tile chunk:
+    # only the lane that reads that chunk holds 5, and it stores key 5
+    src = torch.zeros((1 << 20) + 48, dtype=torch.uint8, device="cuda")
+    for chunk in (0, 30000, 65535):
+        src.zero_()
+        src[chunk * 16 + 4] = 5
+        sink.fill_(7)
+        md.hbm_read_probe(src, sink, key=5, workgroups=3)
+        torch.cuda.synchronize()
+        assert sink[0].item() == 5, chunk
+
 @pytest.mark.parametrize("T", [1, 3])
 def test_stack_eager_matches_oracle(orc_mt, T):
     import moe_decode_amd as md
