@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle.so")
 SRC = os.path.join(HERE, "oracle.c")
 
-FMT = {"q8_0": 1, "q4_0": 2, "i8_row": 3, "i4_row": 4}
+FMT = {"q8_0": 1, "q4_0": 2, "i8_row": 3, "i4_row": 4, "q4_1": 5, "i2_row": 6}
 ACT = {"gelu_tanh": 0, "silu": 1}
 XT = {"f32": 0, "bf16": 1}
 ERR = {0: "ok", 1: "invalid argument", 2: "non-finite logit", 3: "selected expert not supplied"}

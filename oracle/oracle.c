@@ -49,6 +49,8 @@ int or_row_bytes(int fmt, int cols) {
     case OR_Q4_0: return cols % 32 ? -1 : cols / 32 * 18;
     case OR_I8_ROW: return cols;
     case OR_I4_ROW: return cols % 2 ? -1 : cols / 2;
+    case OR_Q4_1: return cols % 32 ? -1 : cols / 32 * 20;
+    case OR_I2_ROW: return cols % 4 ? -1 : cols / 4;
     default: return -1;
     }
 }
@@ -80,7 +82,13 @@ static double bf16_value(uint16_t b) {
  *   I8_ROW: int8 q per weight, fp32 scale s per row;          w = s * q
  *   I4_ROW: byte j holds weight 2j (low nibble) and 2j+1 (high nibble) as
  *          two's-complement 4-bit integers v in [-8, 7];      w = s * v
- * All products are exact in double. */
+ *   Q4_1:  blocks of 20 bytes = fp16 d, fp16 m, 16 bytes of nibbles in the
+ *          Q4_0 order, codes n in 0..15 without offset;       w = d * n + m
+ *   I2_ROW: byte j holds weights 4j..4j+3, weight 4j+i in bits 2i..2i+1, as
+ *          two's-complement 2-bit integers v in [-2, 1];      w = s * v
+ * All products are exact in double, and so is the Q4_1 sum: d * n and m are
+ * both multiples of 2^-24 (the smallest binary16 step) below 2^21, so their
+ * sum needs at most 45 significant bits. */
 int or_decode_row(int fmt, const uint8_t *row, float scale, int K, double *w) {
     if (!row || !w || K <= 0 || or_row_bytes(fmt, K) < 0) return OR_EINVAL;
     if (fmt == OR_Q8_0) {
@@ -99,6 +107,23 @@ int or_decode_row(int fmt, const uint8_t *row, float scale, int K, double *w) {
                 w[32 * b + j + 16] = d * (double)(hi - 8);
             }
         }
+    } else if (fmt == OR_Q4_1) {
+        for (int b = 0; b < K / 32; ++b) {
+            const uint8_t *blk = row + 20 * b;
+            double d = half_value((uint16_t)(blk[0] | (blk[1] << 8)));
+            double m = half_value((uint16_t)(blk[2] | (blk[3] << 8)));
+            for (int j = 0; j < 16; ++j) {
+                w[32 * b + j] = d * (double)(blk[4 + j] & 15) + m;
+                w[32 * b + j + 16] = d * (double)(blk[4 + j] >> 4) + m;
+            }
+        }
+    } else if (fmt == OR_I2_ROW) {
+        for (int j = 0; j < K / 4; ++j) {
+            for (int i = 0; i < 4; ++i) {
+                int c = (row[j] >> (2 * i)) & 3;
+                w[4 * j + i] = (double)scale * (double)(c >= 2 ? c - 4 : c);
+            }
+        }
     } else if (fmt == OR_I8_ROW) {
         for (int c = 0; c < K; ++c) w[c] = (double)scale * (double)(int8_t)row[c];
     } else { /* OR_I4_ROW */
@@ -115,12 +140,12 @@ int or_decode_row(int fmt, const uint8_t *row, float scale, int K, double *w) {
 static int qmat_ok(const or_qmat *W) {
     if (!W || !W->data || W->rows <= 0 || W->cols <= 0) return 0;
     if (or_row_bytes(W->fmt, W->cols) < 0) return 0;
-    if ((W->fmt == OR_I8_ROW || W->fmt == OR_I4_ROW) && !W->scales) return 0;
+    if ((W->fmt == OR_I8_ROW || W->fmt == OR_I4_ROW || W->fmt == OR_I2_ROW) && !W->scales) return 0;
     return 1;
 }
 
 static float row_scale(const or_qmat *W, int r) {
-    return (W->fmt == OR_I8_ROW || W->fmt == OR_I4_ROW) ? W->scales[r] : 0.0f;
+    return (W->fmt == OR_I8_ROW || W->fmt == OR_I4_ROW || W->fmt == OR_I2_ROW) ? W->scales[r] : 0.0f;
 }
 
 static const uint8_t *row_ptr(const or_qmat *W, int r) {

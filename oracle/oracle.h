@@ -18,7 +18,7 @@
 extern "C" {
 #endif
 
-enum { OR_Q8_0 = 1, OR_Q4_0 = 2, OR_I8_ROW = 3, OR_I4_ROW = 4 };
+enum { OR_Q8_0 = 1, OR_Q4_0 = 2, OR_I8_ROW = 3, OR_I4_ROW = 4, OR_Q4_1 = 5, OR_I2_ROW = 6 };
 enum { OR_X_F32 = 0, OR_X_BF16 = 1 };
 enum { OR_ACT_GELU_TANH = 0, OR_ACT_SILU = 1 };
 enum { OR_OK = 0, OR_EINVAL = 1, OR_ENONFINITE = 2, OR_EMISSING = 3 };

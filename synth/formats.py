@@ -16,6 +16,14 @@ formats of the colibri summary, "model execution and memory tiers"):
 ``i4_row``  ``cols/2`` bytes per row; weight 2j is the low nibble of byte j,
             weight 2j+1 its high nibble; nibbles are two's-complement in
             [-8, 7]; one fp32 scale per row kept in a separate array.
+``q4_1``    blocks of 32 weights, 20 bytes: fp16 scale d, fp16 minimum m, then
+            16 bytes qs in the q4_0 nibble order; codes n in 0..15 carry no
+            offset (the value is d * n + m).  The GGUF block the Camelid
+            README names for its bit-exact q4_1 GEMV ("Experimental" rows).
+``i2_row``  ``cols/4`` bytes per row; weight 4j+i sits in bits 2i..2i+1 of
+            byte j as a two's-complement integer in [-2, 1]; one fp32 scale per
+            row kept in a separate array (the packed int2 per-row format of
+            the colibri summary, "model execution and memory tiers").
 """
 
 from dataclasses import dataclass
@@ -23,12 +31,13 @@ from typing import Optional
 
 import numpy as np
 
-FORMATS = ("q8_0", "q4_0", "i8_row", "i4_row")
+FORMATS = ("q8_0", "q4_0", "i8_row", "i4_row", "q4_1", "i2_row")
+ROW_FORMATS = ("i8_row", "i4_row", "i2_row")
 _BLOCK = 32
 
 
 def blocks_per_row(fmt: str, cols: int) -> int:
-    if fmt not in ("q8_0", "q4_0"):
+    if fmt not in ("q8_0", "q4_0", "q4_1"):
         raise ValueError(f"{fmt} has no blocks")
     if cols % _BLOCK:
         raise ValueError("cols must be a multiple of 32")
@@ -47,12 +56,18 @@ def row_bytes(fmt: str, cols: int) -> int:
         if cols % 2:
             raise ValueError("i4_row needs an even number of columns")
         return cols // 2
+    if fmt == "q4_1":
+        return blocks_per_row(fmt, cols) * 20
+    if fmt == "i2_row":
+        if cols % 4:
+            raise ValueError("i2_row needs a multiple of 4 columns")
+        return cols // 4
     raise ValueError(f"unknown format {fmt!r}")
 
 
 def matrix_bytes(fmt: str, rows: int, cols: int) -> int:
     """Weight bytes of a matrix, including the per-row fp32 scales."""
-    extra = 4 * rows if fmt in ("i8_row", "i4_row") else 0
+    extra = 4 * rows if fmt in ROW_FORMATS else 0
     return rows * row_bytes(fmt, cols) + extra
 
 
@@ -129,6 +144,40 @@ def pack_i4_row(scales, v) -> QMatrix:
     code = (v & 0xF).astype(np.uint8)            # two's-complement nibble
     data = code[:, 0::2] | (code[:, 1::2] << 4)
     return QMatrix("i4_row", rows, cols, np.ascontiguousarray(data),
+                   np.asarray(scales, dtype=np.float32).reshape(rows))
+
+
+def pack_q4_1(d_bits, m_bits, n) -> QMatrix:
+    """Lay out Q4_1 blocks.  ``d_bits``, ``m_bits``: (rows, cols/32) fp16 (or
+    their uint16 bits); ``n``: (rows, cols) unsigned codes 0..15."""
+    n = np.asarray(n).astype(np.uint8)
+    if n.max(initial=0) > 15:
+        raise ValueError("q4_1 codes must be in 0..15")
+    rows, cols = n.shape
+    nb = blocks_per_row("q4_1", cols)
+    d = _as_u16(d_bits).reshape(rows, nb)
+    m = _as_u16(m_bits).reshape(rows, nb)
+    nn = n.reshape(rows, nb, 32)
+    out = np.empty((rows, nb, 20), dtype=np.uint8)
+    out[:, :, 0] = (d & 0xFF).astype(np.uint8)
+    out[:, :, 1] = (d >> 8).astype(np.uint8)
+    out[:, :, 2] = (m & 0xFF).astype(np.uint8)
+    out[:, :, 3] = (m >> 8).astype(np.uint8)
+    out[:, :, 4:] = nn[:, :, :16] | (nn[:, :, 16:] << 4)
+    return QMatrix("q4_1", rows, cols, out.reshape(rows, nb * 20))
+
+
+def pack_i2_row(scales, v) -> QMatrix:
+    """Lay out packed signed int2 rows.  ``v``: (rows, cols) integers in [-2, 1]."""
+    v = np.asarray(v).astype(np.int16)
+    if v.min(initial=0) < -2 or v.max(initial=0) > 1:
+        raise ValueError("i2_row values must be in [-2, 1]")
+    rows, cols = v.shape
+    if cols % 4:
+        raise ValueError("i2_row needs a multiple of 4 columns")
+    code = (v & 3).astype(np.uint8)               # two's-complement 2-bit code
+    data = code[:, 0::4] | (code[:, 1::4] << 2) | (code[:, 2::4] << 4) | (code[:, 3::4] << 6)
+    return QMatrix("i2_row", rows, cols, np.ascontiguousarray(data),
                    np.asarray(scales, dtype=np.float32).reshape(rows))
 
 

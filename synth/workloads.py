@@ -1,4 +1,4 @@
-"""The five synthetic workloads and their seeded generators.
+"""The synthetic workloads and their seeded generators.
 
 Every tensor is drawn from its own numpy PCG64 stream seeded with
 ``[workload index, tensor tag, expert, variant]`` (``numpy.random.default_rng``
@@ -24,6 +24,10 @@ random, not trained):
            a per-row fp32 scale (about 18.9 MB per expert, the colibri
            summary's expert size); 1, 4 and 128 tokens.
 ``c4_i8``  the same layer with int8 per-row weights.
+``q41``    dense Q4_1 GEMVs at the ``c2`` shapes, fp32 activations, batch 1
+           and 8; block minimum m = -d * U[6, 10] (rounded to fp16).
+``i2``     dense packed-int2 per-row GEMVs at the ``c4`` expert shapes
+           (2048x6144 and 6144x2048), fp32 activations, batch 1 and 4.
 """
 
 from dataclasses import dataclass
@@ -31,7 +35,7 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
-from .formats import QMatrix, pack_q8_0, pack_i8_row, row_bytes, f32_to_bf16_bits
+from .formats import QMatrix, ROW_FORMATS, pack_q8_0, pack_i8_row, row_bytes, f32_to_bf16_bits
 
 # tensor tags (part of every seed)
 TAG_ROUTER, TAG_BIAS, TAG_GATE, TAG_UP, TAG_DOWN = 1, 2, 3, 4, 5
@@ -121,6 +125,14 @@ SPECS: Dict[str, object] = {
                      d_range=ROW_S, router_std=0.05, bias_std=None, tokens=(1, 4, 128), variant=0),
     "c4_i8": MoESpec("c4_i8", 4, H=6144, F=2048, E=256, k=8, act="gelu_tanh", fmt="i8_row",
                      d_range=ROW_S, router_std=0.05, bias_std=None, tokens=(1, 4, 128), variant=1),
+    # the two further codecs, on dense GEMVs: Q4_1 at the Q4_0 workload's
+    # shapes, packed int2 per-row at the 256-expert layer's expert shapes
+    "q41": DenseSpec("q41", 5, "q4_1", Q4_D,
+                     (("w_10240x2560", 10240, 2560), ("w_2560x10240", 2560, 10240)),
+                     x_dtype="f32", batches=(1, 8)),
+    "i2": DenseSpec("i2", 6, "i2_row", ROW_S,
+                    (("gate_2048x6144", 2048, 6144), ("down_6144x2048", 6144, 2048)),
+                    x_dtype="f32", batches=(1, 4)),
 }
 
 
@@ -174,6 +186,25 @@ def _gen_qmatrix(fmt, rows, cols, rng, d_range) -> QMatrix:
         # two independent uniform signed nibbles per byte == a uniform byte
         data = _uniform_bytes(rng, rows * cols // 2).reshape(rows, cols // 2)
         return QMatrix("i4_row", rows, cols, data, s)
+    if fmt == "q4_1":
+        nb = cols // 32
+        d = rng.uniform(lo, hi, (rows, nb)).astype(np.float16)
+        # the block minimum sits 6..10 steps below zero, so values span both signs
+        m = (-d.astype(np.float64) * rng.uniform(6.0, 10.0, (rows, nb))).astype(np.float16)
+        qs = _uniform_bytes(rng, rows * nb * 16).reshape(rows, nb, 16)
+        d, m = d.view(np.uint16), m.view(np.uint16)
+        out = np.empty((rows, nb, 20), dtype=np.uint8)
+        out[:, :, 0] = (d & 0xFF).astype(np.uint8)
+        out[:, :, 1] = (d >> 8).astype(np.uint8)
+        out[:, :, 2] = (m & 0xFF).astype(np.uint8)
+        out[:, :, 3] = (m >> 8).astype(np.uint8)
+        out[:, :, 4:] = qs
+        return QMatrix("q4_1", rows, cols, out.reshape(rows, nb * 20))
+    if fmt == "i2_row":
+        s = rng.uniform(lo, hi, rows).astype(np.float32)
+        # four independent uniform 2-bit codes per byte == a uniform byte
+        data = _uniform_bytes(rng, rows * cols // 4).reshape(rows, cols // 4)
+        return QMatrix("i2_row", rows, cols, data, s)
     raise ValueError(fmt)
 
 
@@ -216,7 +247,7 @@ def moe_expert_stack(sp: MoESpec, part: str, experts: Optional[Sequence[int]] = 
     n = len(experts)
     if out is None:
         out = np.empty((n, rows, rb), dtype=np.uint8)
-    per_row = sp.fmt in ("i8_row", "i4_row")
+    per_row = sp.fmt in ROW_FORMATS
     if per_row and out_scales is None:
         out_scales = np.empty((n, rows), dtype=np.float32)
     for i, e in enumerate(experts):

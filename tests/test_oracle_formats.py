@@ -1,8 +1,10 @@
 """Pins of the oracle's weight decoding against hand-built bytes.
 
 Every expected value here is written by hand from the format definitions
-(fp16 scale first, GGUF nibble order for Q4_0, low nibble = even weight and
-two's complement for packed int4), never computed by the oracle."""
+(fp16 scale first, GGUF nibble order for Q4_0 and Q4_1, Q4_1's fp16 minimum
+after the scale, low nibble = even weight and two's complement for packed
+int4, low bit pair first and two's complement for packed int2), never
+computed by the oracle."""
 import os
 
 import numpy as np
@@ -99,12 +101,49 @@ def test_i4_row_scale_product_is_exact(orc):
     assert w[0] == 7.0 * float(s) and w[1] == 7.0 * float(s)
 
 
+def test_q4_1_nibble_order_and_minimum(orc):
+    # d = 0.5 (0x3800), m = 0.25 (0x3400): w = 0.5 n + 0.25; byte 5 = 0x3A gives
+    # weight 5 the low nibble 10 and weight 21 the high nibble 3
+    qs = bytearray(16)
+    qs[5] = 0x3A
+    w = orc.decode_row("q4_1", bytes([0x00, 0x38, 0x00, 0x34]) + bytes(qs), 0.0, 32)
+    exp = np.full(32, 0.25)
+    exp[5] = 5.25
+    exp[21] = 1.75
+    assert np.array_equal(w, exp)
+
+
+def test_q4_1_extremes_and_second_block(orc):
+    # block 0: d = 1, m = -8 (0xC800), all codes 15 -> 7; block 1: d = 2
+    # (0x4000), m = 0, all codes 0 -> 0
+    row = bytes([0x00, 0x3C, 0x00, 0xC8]) + bytes([0xFF] * 16) + bytes([0x00, 0x40, 0x00, 0x00]) + bytes(16)
+    w = orc.decode_row("q4_1", row, 0.0, 64)
+    assert np.all(w[:32] == 7.0) and np.all(w[32:] == 0.0)
+
+
+def test_q4_1_sum_is_exact(orc):
+    # d = 2^-24 (smallest subnormal, 0x0001), m = 1024 (0x6400), codes 15:
+    # w = 1024 + 15 * 2^-24 exactly (fp32 could not hold it)
+    w = orc.decode_row("q4_1", bytes([0x01, 0x00, 0x00, 0x64]) + bytes([0xFF] * 16), 0.0, 32)
+    assert np.all(w - 1024.0 == 15 * 2.0 ** -24)
+
+
+def test_i2_row_order_and_sign(orc):
+    # byte 0xE4 = 0b11_10_01_00: weights 0..3 = 0, 1, -2, -1;
+    # byte 0x1B = 0b00_01_10_11: weights 4..7 = -1, -2, 1, 0
+    w = orc.decode_row("i2_row", bytes([0xE4, 0x1B, 0x00, 0xFF]), 0.5, 16)
+    assert list(w) == [0.0, 0.5, -1.0, -0.5, -0.5, -1.0, 0.5, 0.0, 0.0, 0.0, 0.0, 0.0, -0.5, -0.5, -0.5, -0.5]
+
+
 def test_row_bytes(orc):
     assert orc.row_bytes("q8_0", 256) == 272 == F.row_bytes("q8_0", 256)
     assert orc.row_bytes("q4_0", 768) == 432 == F.row_bytes("q4_0", 768)
     assert orc.row_bytes("i8_row", 2048) == 2048 == F.row_bytes("i8_row", 2048)
     assert orc.row_bytes("i4_row", 6144) == 3072 == F.row_bytes("i4_row", 6144)
+    assert orc.row_bytes("q4_1", 2560) == 1600 == F.row_bytes("q4_1", 2560)
+    assert orc.row_bytes("i2_row", 6144) == 1536 == F.row_bytes("i2_row", 6144)
     assert orc.row_bytes("q8_0", 33) == -1
+    assert orc.row_bytes("i2_row", 6) == -1
 
 
 # ---- the generator's packers, checked through the (now pinned) decoder ----
@@ -134,6 +173,17 @@ def test_packers_round_trip(orc):
     for r in range(rows):
         w = orc.decode_row("i8_row", m.data[r], float(m.scales[r]), cols)
         assert np.array_equal(w, float(s[r]) * q[r])
+    mn = (-d.astype(np.float64) * 7).astype(np.float16)
+    m = F.pack_q4_1(d, mn, n)
+    for r in range(rows):
+        w = orc.decode_row("q4_1", m.data[r], 0.0, cols)
+        exp = np.repeat(d[r].astype(np.float64), 32) * n[r] + np.repeat(mn[r].astype(np.float64), 32)
+        assert np.array_equal(w, exp)
+    v2 = rng.integers(-2, 2, (rows, cols))
+    m = F.pack_i2_row(s, v2)
+    for r in range(rows):
+        w = orc.decode_row("i2_row", m.data[r], float(m.scales[r]), cols)
+        assert np.array_equal(w, float(s[r]) * v2[r])
 
 
 def test_bf16_rounding_of_inputs():

@@ -42,6 +42,34 @@ def test_q4_0_nine_is_one_and_eight_is_zero(orc):
     assert np.all(y0 == 0.0) and np.all(S0 == 0.0)
 
 
+def test_q4_1_code_times_d_cancels_minimum(orc):
+    # codes all 4 and m = -4 d: every weight is exactly zero; codes all 0:
+    # y = sum over blocks of m times the block's sum of x
+    rng = np.random.default_rng(8)
+    rows, K = 5, 96
+    d = rng.uniform(1e-3, 2e-2, (rows, 3)).astype(np.float16)
+    mn = (-4 * d.astype(np.float64)).astype(np.float16)      # exact: a power-of-two multiple
+    assert np.array_equal(mn.astype(np.float64), -4 * d.astype(np.float64))
+    x = _x(rng, 2, K)
+    y, S = orc.qgemv(F.pack_q4_1(d, mn, np.full((rows, K), 4)), x)
+    assert np.all(y == 0.0) and np.all(S == 0.0)
+    y, S = orc.qgemv(F.pack_q4_1(d, mn, np.zeros((rows, K), dtype=np.int64)), x)
+    for b in range(2):
+        exact = (mn.astype(np.float64) * x[b].astype(np.float64).reshape(3, 32).sum(1)).sum(1)
+        assert _fp32_ok(y[b], exact, S[b])
+
+
+def test_i2_row_alternating_signs(orc):
+    # weights +1, -1, +1, -1, ... (codes 1, 3): y = s * (x0 - x1 + x2 - x3 ...)
+    s = np.array([0.25, 0.003], dtype=np.float32)
+    v = np.tile([1, -1], (2, 128))
+    rng = np.random.default_rng(9)
+    x = _x(rng, 1, 256)
+    y, S = orc.qgemv(F.pack_i2_row(s, v), x)
+    alt = x[0].astype(np.float64)[0::2].sum() - x[0].astype(np.float64)[1::2].sum()
+    assert _fp32_ok(y[0], s.astype(np.float64) * alt, S[0])
+
+
 def test_i8_row_ones_times_ones(orc):
     s = np.array([0.5, 0.001, 0.0037], dtype=np.float32)
     m = F.pack_i8_row(s, np.ones((3, 256), dtype=np.int64))
@@ -72,10 +100,20 @@ def _random_matrix(rng, fmt, rows, K):
         d = rng.uniform(1e-3, 2e-2, (rows, K // 32)).astype(np.float16)
         n = rng.integers(0, 16, (rows, K))
         return F.pack_q4_0(d, n), np.repeat(d.astype(np.float64), 32, axis=1) * (n - 8)
+    if fmt == "q4_1":
+        d = rng.uniform(1e-3, 2e-2, (rows, K // 32)).astype(np.float16)
+        mn = rng.uniform(-0.2, 0.05, (rows, K // 32)).astype(np.float16)
+        n = rng.integers(0, 16, (rows, K))
+        return (F.pack_q4_1(d, mn, n),
+                np.repeat(d.astype(np.float64), 32, axis=1) * n + np.repeat(mn.astype(np.float64), 32, axis=1))
     s = rng.uniform(1e-3, 1e-2, rows).astype(np.float32)
     if fmt == "i8_row":
         q = rng.integers(-127, 128, (rows, K))
         return F.pack_i8_row(s, q), s.astype(np.float64)[:, None] * q
+    if fmt == "i2_row":
+        v = rng.integers(-2, 2, (rows, K))
+        return F.pack_i2_row(s, v), s.astype(np.float64)[:, None] * v
+    assert fmt == "i4_row"
     v = rng.integers(-8, 8, (rows, K))
     return F.pack_i4_row(s, v), s.astype(np.float64)[:, None] * v
 
