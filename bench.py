@@ -425,7 +425,11 @@ def main():
         torch.cuda.empty_cache()
         for key, name, batch in (("c1", "gate", 1), ("c1", "down", 1), ("c1", "q", 1), ("c1", "k", 1),
                                  ("c2", "w_10240x2560", 1), ("c2", "w_10240x2560", 8),
-                                 ("c2", "w_2560x10240", 1), ("c2", "w_2560x10240", 8)):
+                                 ("c2", "w_2560x10240", 1), ("c2", "w_2560x10240", 8),
+                                 ("q41", "w_10240x2560", 1), ("q41", "w_10240x2560", 8),
+                                 ("q41", "w_2560x10240", 1), ("q41", "w_2560x10240", 8),
+                                 ("i2", "gate_2048x6144", 1), ("i2", "gate_2048x6144", 4),
+                                 ("i2", "down_6144x2048", 1), ("i2", "down_6144x2048", 4)):
             m = run_dense(key, name, batch, max(20, args.steps), 10)
             modes[f"{key}_{name}_b{batch}"] = m
             log(f"[bench] {key} {name} batch {batch}: {m['ms_per_call'] * 1e3:.1f} us ({m['weight_GBps']:.0f} GB/s)")

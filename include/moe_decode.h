@@ -71,16 +71,31 @@ typedef enum md_status {
  *   MD_I4_ROW rows of cols/2 bytes; weight 2j is the low nibble of byte j and
  *             2j+1 the high nibble, two's complement in [-8, 7]; one fp32
  *             scale s per row;  w = s * v.
+ *   MD_Q4_1   rows of cols/32 blocks of 20 bytes: fp16 d, fp16 m, then 16
+ *             bytes qs in the MD_Q4_0 nibble order, codes n in 0..15 with no
+ *             offset;  w = d * n + m  (the Camelid README's bit-exact q4_1
+ *             GEMV, "Experimental" rows).
+ *   MD_I2_ROW rows of cols/4 bytes; weight 4j+i sits in bits 2i..2i+1 of byte
+ *             j, two's complement in [-2, 1]; one fp32 scale s per row;
+ *             w = s * v  (the colibri summary's packed int2 per-row format,
+ *             "model execution and memory tiers").
  * Device layout (what every compute entry point reads; produced from the
  * canonical layout by md_prepare_layout, same byte count, same row stride):
  *   MD_Q8_0   per row: the cols int8 q of all blocks in order, then the
  *             cols/32 fp16 scales in order.
  *   MD_Q4_0   per row: the 16-byte qs of all blocks in order, then the
  *             cols/32 fp16 scales in order.
- *   MD_I8_ROW, MD_I4_ROW: identical to the canonical layout.
+ *   MD_Q4_1   per row: the 16-byte qs of all blocks in order, then the
+ *             cols/32 (d, m) fp16 pairs in order.
+ *   MD_I8_ROW, MD_I4_ROW, MD_I2_ROW: identical to the canonical layout.
  * Every row therefore starts a run of 16-byte quant chunks that a wavefront
- * streams with coalesced 16-byte loads, scales kept out of the way. */
-typedef enum md_qtype { MD_Q8_0 = 1, MD_Q4_0 = 2, MD_I8_ROW = 3, MD_I4_ROW = 4 } md_qtype;
+ * streams with coalesced 16-byte loads, scales kept out of the way.
+ * MD_Q4_1 and MD_I2_ROW are taken by md_row_bytes, md_prepare_layout and
+ * md_qgemv (+ its workspace size); the FFN and MoE entry points return
+ * MD_ERR_UNSUPPORTED for them. */
+typedef enum md_qtype {
+  MD_Q8_0 = 1, MD_Q4_0 = 2, MD_I8_ROW = 3, MD_I4_ROW = 4, MD_Q4_1 = 5, MD_I2_ROW = 6
+} md_qtype;
 
 typedef enum md_xtype { MD_X_F32 = 0, MD_X_BF16 = 1 } md_xtype;
 

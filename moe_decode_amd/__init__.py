@@ -11,8 +11,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBPATH = os.path.join(HERE, "libmoe_decode.so")
 
-Q8_0, Q4_0, I8_ROW, I4_ROW = 1, 2, 3, 4
-TYPES = {"q8_0": Q8_0, "q4_0": Q4_0, "i8_row": I8_ROW, "i4_row": I4_ROW}
+Q8_0, Q4_0, I8_ROW, I4_ROW, Q4_1, I2_ROW = 1, 2, 3, 4, 5, 6
+TYPES = {"q8_0": Q8_0, "q4_0": Q4_0, "i8_row": I8_ROW, "i4_row": I4_ROW, "q4_1": Q4_1, "i2_row": I2_ROW}
+ROW_TYPES = (I8_ROW, I4_ROW, I2_ROW)
 ACTS = {"gelu_tanh": 0, "silu": 1}
 X_F32, X_BF16 = 0, 1
 

@@ -7,12 +7,19 @@
 //   Q4_0   one block: 32 nibbles (low nibbles = weights 0..15, high = 16..31)
 //   I8_ROW 16 int8 weights (scale per row)
 //   I4_ROW 32 two's-complement nibbles, low nibble of byte b = weight 2b
+//   Q4_1   one block: 32 unsigned nibbles in the Q4_0 order; scale d and
+//          minimum m of the block (w = d n + m; dense GEMV only)
+//   I2_ROW 64 two's-complement bit pairs, bits 2i..2i+1 of byte b = weight
+//          4b+i (scale per row; dense GEMV only)
 // Decoding happens in VGPRs.  int8 goes through the sign-extending byte
 // convert.  A 4-bit code is made a two's-complement nibble (Q4_0: n XOR 8 is
 // n - 8) and moved into the high half of a byte with a 0xF0F0F0F0 mask, so each
 // byte holds exactly 16 * value as an int8 and converts with the same
 // sign-extending byte convert; the factor 1/16 is folded into the scale.  No
-// offset correction is needed, so an all-zero row gives exactly zero.
+// offset correction is needed, so an all-zero row gives exactly zero.  Q4_1
+// codes carry no offset: masked the same way they convert with the unsigned
+// byte convert, and the block's m times the block's sum of activations is
+// added.  A 2-bit code moved into the top two bits of a byte is 64 * value.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,7 +30,7 @@
 
 namespace md {
 
-enum : int { Q8_0 = 1, Q4_0 = 2, I8_ROW = 3, I4_ROW = 4 };
+enum : int { Q8_0 = 1, Q4_0 = 2, I8_ROW = 3, I4_ROW = 4, Q4_1 = 5, I2_ROW = 6 };
 enum : int { ACT_GELU_TANH = 0, ACT_SILU = 1 };
 enum : int { XF32 = 0, XBF16 = 1 };
 
@@ -34,14 +41,20 @@ template <> struct Fmt<Q8_0>   { static constexpr int WPC = 16; static constexpr
 template <> struct Fmt<Q4_0>   { static constexpr int WPC = 32; static constexpr bool ROW = false; };
 template <> struct Fmt<I8_ROW> { static constexpr int WPC = 16; static constexpr bool ROW = true; };
 template <> struct Fmt<I4_ROW> { static constexpr int WPC = 32; static constexpr bool ROW = true; };
+template <> struct Fmt<Q4_1>   { static constexpr int WPC = 32; static constexpr bool ROW = false; };
+template <> struct Fmt<I2_ROW> { static constexpr int WPC = 64; static constexpr bool ROW = true; };
 
 __host__ __device__ constexpr int64_t row_bytes(int fmt, int K) {
   return fmt == Q8_0 ? (int64_t)K / 32 * 34
        : fmt == Q4_0 ? (int64_t)K / 32 * 18
        : fmt == I8_ROW ? (int64_t)K
+       : fmt == Q4_1 ? (int64_t)K / 32 * 20
+       : fmt == I2_ROW ? (int64_t)K / 4
        : (int64_t)K / 2;
 }
-__host__ __device__ constexpr int wpc(int fmt) { return (fmt == Q8_0 || fmt == I8_ROW) ? 16 : 32; }
+__host__ __device__ constexpr int wpc(int fmt) {
+  return (fmt == Q8_0 || fmt == I8_ROW) ? 16 : fmt == I2_ROW ? 64 : 32;
+}
 __host__ __device__ constexpr int nchunks(int fmt, int K) { return K / wpc(fmt); }
 
 // Hide known bits from the optimizer so each masked byte converts with one
@@ -71,13 +84,20 @@ MD_DEV float chunk_scale(const uint8_t* row, int K, int c) {
     return h2f(*reinterpret_cast<const uint16_t*>(row + K + 2 * (c >> 1)));
   } else if constexpr (FMT == Q4_0) {
     return h2f(*reinterpret_cast<const uint16_t*>(row + (K / 32) * 16 + 2 * c)) * 0.0625f;
+  } else if constexpr (FMT == Q4_1) {
+    return h2f(*reinterpret_cast<const uint16_t*>(row + (K / 32) * 16 + 4 * c)) * 0.0625f;
   } else {
     return 1.0f;
   }
 }
 
+// Q4_1: the minimum m of block c.
+MD_DEV float chunk_min_q4_1(const uint8_t* row, int K, int c) {
+  return h2f(*reinterpret_cast<const uint16_t*>(row + (K / 32) * 16 + 4 * c + 2));
+}
+
 template <int FMT>
-constexpr float row_post() { return FMT == I4_ROW ? 0.0625f : 1.0f; }
+constexpr float row_post() { return FMT == I4_ROW ? 0.0625f : FMT == I2_ROW ? 0.015625f : 1.0f; }
 
 // Load the WPC activations of chunk c (fp32 or bf16 source).
 template <int FMT, int XT>
@@ -129,6 +149,34 @@ MD_DEV float dot_chunk(u32x4 w, const float* xv) {
       for (int b = 0; b < 4; ++b) {
         a0 = fmaf((float)(signed char)(lo >> (8 * b)), xv[4 * m + b], a0);
         a1 = fmaf((float)(signed char)(hi >> (8 * b)), xv[16 + 4 * m + b], a1);
+      }
+    }
+  } else if constexpr (FMT == Q4_1) {
+    // the Q4_0 order, unsigned codes: each masked byte is 16 * n
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned lo = opaque((w[m] << 4) & 0xF0F0F0F0u), hi = opaque(w[m] & 0xF0F0F0F0u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        a0 = fmaf((float)(unsigned char)(lo >> (8 * b)), xv[4 * m + b], a0);
+        a1 = fmaf((float)(unsigned char)(hi >> (8 * b)), xv[16 + 4 * m + b], a1);
+      }
+    }
+  } else if constexpr (FMT == I2_ROW) {
+    // byte b of word m holds weights 16m+4b+i in bits 2i..2i+1; plane i moves
+    // them to the top of each byte: 64 * value as an int8
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned p[4] = {opaque((w[m] << 6) & 0xC0C0C0C0u), opaque((w[m] << 4) & 0xC0C0C0C0u),
+                             opaque((w[m] << 2) & 0xC0C0C0C0u), opaque(w[m] & 0xC0C0C0C0u)};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = (float)(signed char)(p[i] >> (8 * b));
+          if (i & 1) a1 = fmaf(v, xv[16 * m + 4 * b + i], a1);
+          else a0 = fmaf(v, xv[16 * m + 4 * b + i], a0);
+        }
       }
     }
   } else {  // I4_ROW: byte b of word m: low nibble = weight 8m+2b, high = 8m+2b+1

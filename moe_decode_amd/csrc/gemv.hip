@@ -33,14 +33,25 @@ MD_DEV void rows_dot(const uint8_t* const (&rowp)[R], int K, int c0, int c1, int
     for (int r = 0; r < R; ++r) w[r] = ld_stream(rowp[r] + 16 * (int64_t)c);
 #pragma unroll
     for (int r = 0; r < R; ++r) sc[r] = chunk_scale<FMT>(rowp[r], K, c);
+    float mn[R];
+    if constexpr (FMT == Q4_1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) mn[r] = chunk_min_q4_1(rowp[r], K, c);
+    }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float xv[W];
       load_x<FMT, XT>(xp[b], c, xv);
+      float sx = 0.f;  // Q4_1: the block's sum of activations, for its minimum
+      if constexpr (FMT == Q4_1) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) sx += xv[i];
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float d = dot_chunk<FMT>(w[r], xv);
         if constexpr (Fmt<FMT>::ROW) acc[r][b] += d;
+        else if constexpr (FMT == Q4_1) acc[r][b] = fmaf(sc[r], d, fmaf(mn[r], sx, acc[r][b]));
         else acc[r][b] = fmaf(sc[r], d, acc[r][b]);
       }
     }
@@ -119,7 +130,10 @@ static int pow2_divisor_le64(int n) {
 GemvCfg qgemv_config(int fmt, int N, int K, int batch) {
   GemvCfg c{};
   const int nc = nchunks(fmt, K);
-  c.L = pow2_divisor_le64(nc);
+  // lanes per row group: the largest power of two (8..64) dividing the chunk
+  // count, so lanes share the chunks evenly; at least 8 (rows of fewer chunks,
+  // packed int2 at 256 columns, leave lanes idle)
+  c.L = std::max(8, pow2_divisor_le64(nc));
   c.B = batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8;
   const int G = 64 / c.L;
   // rows per lane group: about four 16-byte row chunks in flight per lane
@@ -127,7 +141,8 @@ GemvCfg qgemv_config(int fmt, int N, int K, int batch) {
   // gains), fewer if the grid would then hold less than 1024 waves; K is
   // split (uneven ranges allowed, a second pass adds the slices) only for
   // grids still below that, every K-slice keeping >= 2 chunks per lane
-  const int rmax = c.B <= 2 ? 4 : 2;
+  // (packed int2 at batch 2: four rows would spill, 64 activations a chunk)
+  const int rmax = c.B <= 2 && !(fmt == I2_ROW && c.B == 2) ? 4 : 2;
   const int cpl = nc / c.L;
   c.R = 1;
   while (c.R < rmax && 2 * c.R * cpl <= 4) c.R *= 2;
@@ -163,7 +178,7 @@ hipError_t launch_qgemv(int fmt, int xt, const GemvCfg& c, const uint8_t* W, con
 #define MD_F(F_) \
   if (fmt == F_) e = xt == XF32 ? qgemv_fx<F_, XF32>(c, W, scales, N, K, x, batch, out, st) \
                                 : qgemv_fx<F_, XBF16>(c, W, scales, N, K, x, batch, out, st);
-  MD_F(Q8_0) MD_F(Q4_0) MD_F(I8_ROW) MD_F(I4_ROW)
+  MD_F(Q8_0) MD_F(Q4_0) MD_F(I8_ROW) MD_F(I4_ROW) MD_F(Q4_1) MD_F(I2_ROW)
 #undef MD_F
   if (e != hipSuccess || c.S == 1) return e;
   const int64_t n = (int64_t)batch * N;

@@ -266,8 +266,8 @@ hipError_t launch_dispatch(const int* idx, int T, int E, int k, const DispOut& d
 
 // -------------------------------------------------------------- layout
 
-// Canonical -> device layout, one thread per 32-weight block (Q8_0, Q4_0) or
-// per 16 bytes (per-row formats, a plain copy).
+// Canonical -> device layout, one thread per 32-weight block (Q8_0, Q4_0,
+// Q4_1) or per 16 bytes (per-row formats, a plain copy).
 __global__ __launch_bounds__(256) void k_prepare_q(int fmt, int64_t nblocks, int nb, const uint8_t* __restrict__ src,
                                                    uint8_t* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -280,12 +280,17 @@ __global__ __launch_bounds__(256) void k_prepare_q(int fmt, int64_t nblocks, int
     for (int b = 0; b < 32; ++b) r[32 * j + b] = s[2 + b];
     r[32 * nb + 2 * j] = s[0];
     r[32 * nb + 2 * j + 1] = s[1];
-  } else {
+  } else if (fmt == Q4_0) {
     const uint8_t* s = src + row * (int64_t)nb * 18 + (int64_t)j * 18;
     uint8_t* r = dst + row * (int64_t)nb * 18;
     for (int b = 0; b < 16; ++b) r[16 * j + b] = s[2 + b];
     r[16 * nb + 2 * j] = s[0];
     r[16 * nb + 2 * j + 1] = s[1];
+  } else {  // Q4_1: qs, then the (d, m) pair
+    const uint8_t* s = src + row * (int64_t)nb * 20 + (int64_t)j * 20;
+    uint8_t* r = dst + row * (int64_t)nb * 20;
+    for (int b = 0; b < 16; ++b) r[16 * j + b] = s[4 + b];
+    for (int b = 0; b < 4; ++b) r[16 * nb + 4 * j + b] = s[b];
   }
 }
 
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(256) void k_copy16(int64_t n16, const uint4* __rest
 hipError_t launch_prepare_layout(int fmt, int rows, int cols, int count, const void* src, void* dst,
                                  hipStream_t st) {
   const int64_t nrows = (int64_t)rows * count;
-  if (fmt == Q8_0 || fmt == Q4_0) {
+  if (fmt == Q8_0 || fmt == Q4_0 || fmt == Q4_1) {
     const int nb = cols / 32;
     const int64_t n = nrows * nb;
     hipLaunchKernelGGL(k_prepare_q, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, fmt, n, nb,

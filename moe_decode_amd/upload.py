@@ -6,7 +6,7 @@ whole multi-GB stack."""
 import numpy as np
 import torch
 
-from . import DevQMatrix, prepare_layout, row_bytes, TYPES
+from . import DevQMatrix, prepare_layout, row_bytes, ROW_TYPES, TYPES
 
 
 def upload_stack(type_, rows, cols, count, fetch, device="cuda"):
@@ -16,7 +16,7 @@ def upload_stack(type_, rows, cols, count, fetch, device="cuda"):
     rb = row_bytes(t, cols)
     per = rows * rb
     src = torch.empty(count * per, dtype=torch.uint8, device=device)
-    per_row = t in (TYPES["i8_row"], TYPES["i4_row"])
+    per_row = t in ROW_TYPES
     sc = torch.empty(count * rows, dtype=torch.float32, device=device) if per_row else None
     pinned = torch.empty(per, dtype=torch.uint8, pin_memory=True)
     for i in range(count):

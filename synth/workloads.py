@@ -24,8 +24,8 @@ random, not trained):
            a per-row fp32 scale (about 18.9 MB per expert, the colibri
            summary's expert size); 1, 4 and 128 tokens.
 ``c4_i8``  the same layer with int8 per-row weights.
-``q41``    dense Q4_1 GEMVs at the ``c2`` shapes, fp32 activations, batch 1
-           and 8; block minimum m = -d * U[6, 10] (rounded to fp16).
+``q41``    dense Q4_1 GEMVs at the ``c2`` shapes and activations (bf16), batch
+           1 and 8; block minimum m = -d * U[6, 10] (rounded to fp16).
 ``i2``     dense packed-int2 per-row GEMVs at the ``c4`` expert shapes
            (2048x6144 and 6144x2048), fp32 activations, batch 1 and 4.
 """
@@ -129,7 +129,7 @@ SPECS: Dict[str, object] = {
     # shapes, packed int2 per-row at the 256-expert layer's expert shapes
     "q41": DenseSpec("q41", 5, "q4_1", Q4_D,
                      (("w_10240x2560", 10240, 2560), ("w_2560x10240", 2560, 10240)),
-                     x_dtype="f32", batches=(1, 8)),
+                     x_dtype="bf16", batches=(1, 8)),
     "i2": DenseSpec("i2", 6, "i2_row", ROW_S,
                     (("gate_2048x6144", 2048, 6144), ("down_6144x2048", 6144, 2048)),
                     x_dtype="f32", batches=(1, 4)),

@@ -39,7 +39,10 @@ def test_basic_queries():
     assert md.row_bytes("q4_0", 768) == 432
     assert md.row_bytes("i4_row", 6144) == 3072
     assert md.row_bytes("i8_row", 6144) == 6144
+    assert md.row_bytes("q4_1", 2560) == 1600
+    assert md.row_bytes("i2_row", 6144) == 1536
     assert md.row_bytes(9, 256) == -1
+    assert md.row_bytes(0, 256) == -1
 
 
 def _qm(type_=md.Q8_0, rows=64, cols=256, q=FAKE, scale=None):
@@ -67,6 +70,12 @@ def test_qgemv_errors():
     assert _status(L.md_qgemv_workspace_size(ctypes.byref(q), 1, ctypes.byref(sz))) == "MD_ERR_INVALID_ARG"
     assb = L.md_last_error_detail().decode()
     assert "row_scale" in assb
+    q = _qm(type_=md.I2_ROW)
+    assert _status(L.md_qgemv_workspace_size(ctypes.byref(q), 1, ctypes.byref(sz))) == "MD_ERR_INVALID_ARG"
+    q = _qm(type_=md.I2_ROW, scale=FAKE)
+    assert L.md_qgemv_workspace_size(ctypes.byref(q), 1, ctypes.byref(sz)) == 0
+    q = _qm(type_=md.Q4_1, rows=4096, cols=2560)
+    assert L.md_qgemv_workspace_size(ctypes.byref(q), 8, ctypes.byref(sz)) == 0
     q = _qm()
     assert _status(L.md_qgemv(ctypes.byref(q), FAKE, 7, 1, FAKE, None, 0, None)) == "MD_ERR_INVALID_ARG"
     assert _status(L.md_qgemv(ctypes.byref(q), FAKE_ODD, 0, 1, FAKE, None, 0, None)) == "MD_ERR_ALIGNMENT"
@@ -117,6 +126,9 @@ def test_moe_errors():
         (dict(down_q=FAKE_ODD), 1, "MD_ERR_ALIGNMENT"),
         (dict(type=md.I8_ROW), 1, "MD_ERR_INVALID_ARG"),
         (dict(has_shared=1), 1, "MD_ERR_INVALID_ARG"),
+        (dict(type=md.Q4_1), 1, "MD_ERR_UNSUPPORTED"),           # md_qgemv only
+        (dict(type=md.I2_ROW, gate_scale=FAKE, up_scale=FAKE, down_scale=FAKE), 1, "MD_ERR_UNSUPPORTED"),
+        (dict(type=7), 1, "MD_ERR_INVALID_ARG"),
         ({}, 0, "MD_ERR_SHAPE"),
         ({}, 129, "MD_ERR_UNSUPPORTED"),
     ]
@@ -143,6 +155,9 @@ def test_ffn_and_layout_errors():
     f.down = _qm(rows=256, cols=768)
     assert _status(L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz))) == "MD_ERR_SHAPE"
     f.down = _qm(type_=md.Q4_0, rows=256, cols=512)
+    assert _status(L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz))) == "MD_ERR_UNSUPPORTED"
+    f = md.FFNDesc(0, _qm(type_=md.Q4_1, rows=512, cols=256), _qm(type_=md.Q4_1, rows=512, cols=256),
+                   _qm(type_=md.Q4_1, rows=256, cols=512))
     assert _status(L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz))) == "MD_ERR_UNSUPPORTED"
     assert _status(L.md_prepare_layout(md.Q8_0, 4, 256, 1, FAKE, FAKE + 64, None)) == "MD_ERR_INVALID_ARG"
     assert _status(L.md_prepare_layout(md.Q8_0, 4, 256, 1, FAKE, FAKE_ODD, None)) == "MD_ERR_ALIGNMENT"

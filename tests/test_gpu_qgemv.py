@@ -24,9 +24,16 @@ def _random_qmatrix(rng, fmt, rows, cols):
     if fmt == "q4_0":
         return F.pack_q4_0(rng.uniform(1e-3, 2e-2, (rows, cols // 32)).astype(np.float16),
                            rng.integers(0, 16, (rows, cols)))
+    if fmt == "q4_1":
+        d = rng.uniform(1e-3, 2e-2, (rows, cols // 32)).astype(np.float16)
+        mn = (-d.astype(np.float64) * rng.uniform(6.0, 10.0, (rows, cols // 32))).astype(np.float16)
+        return F.pack_q4_1(d, mn, rng.integers(0, 16, (rows, cols)))
     s = rng.uniform(1e-3, 1e-2, rows).astype(np.float32)
     if fmt == "i8_row":
         return F.pack_i8_row(s, rng.integers(-127, 128, (rows, cols)))
+    if fmt == "i2_row":
+        return F.pack_i2_row(s, rng.integers(-2, 2, (rows, cols)))
+    assert fmt == "i4_row"
     return F.pack_i4_row(s, rng.integers(-8, 8, (rows, cols)))
 
 
@@ -105,6 +112,25 @@ def test_dense_q4_0_bf16(orc_mt, name, batch):
     y = md.qgemv(dense_matrix("c2", name), x_tensor(x))
     torch.cuda.synchronize()
     assert_within(y.cpu().numpy(), y_ref, S, f"c2 {name} b{batch}")
+
+
+@pytest.mark.parametrize("key,name,batch", [("q41", "w_10240x2560", 1), ("q41", "w_10240x2560", 8),
+                                            ("q41", "w_2560x10240", 1), ("q41", "w_2560x10240", 8),
+                                            ("i2", "gate_2048x6144", 1), ("i2", "gate_2048x6144", 4),
+                                            ("i2", "down_6144x2048", 1), ("i2", "down_6144x2048", 4)])
+def test_dense_more_codecs(orc_mt, key, name, batch):
+    """The Q4_1 and packed-int2 dense workloads at full size."""
+    import moe_decode_amd as md
+    import torch
+    from synth.device import x_tensor
+    sp = W.spec(key)
+    say(f"[{key}] {name} batch {batch}")
+    m = W.dense_matrix(sp, name)
+    x = W.dense_x(sp, m.cols, batch)
+    y_ref, S = orc_mt.qgemv(m, x, sp.x_dtype)
+    y = md.qgemv(dense_matrix(key, name), x_tensor(x))
+    torch.cuda.synchronize()
+    assert_within(y.cpu().numpy(), y_ref, S, f"{key} {name} b{batch}")
 
 
 def test_q4_0_code_eight_is_exact_zero():
@@ -204,7 +230,7 @@ def test_qgemv_widest_rows(orc_mt, fmt, batch):
     assert_within(_run(m, x), y_ref, S, f"{fmt} 48x16384 b{batch}")
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "i8_row"])
+@pytest.mark.parametrize("fmt", ["q4_0", "i8_row", "q4_1", "i2_row"])
 def test_qgemv_most_rows(orc_mt, fmt):
     """The most rows the library takes (65536); every 97th row is compared."""
     rng = np.random.default_rng([32, F.FORMATS.index(fmt)])
