@@ -38,8 +38,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_type(int32_t t) { return t >= MD_Q8_0 && t <= MD_I2_ROW; }
 bool row_type(int32_t t) { return t == MD_I8_ROW || t == MD_I4_ROW || t == MD_I2_ROW; }
-// the formats the FFN and MoE kernels take (Q4_1 and I2_ROW: md_qgemv only)
-bool layer_type(int32_t t) { return t >= MD_Q8_0 && t <= MD_I4_ROW; }
+// the formats the FFN and MoE kernels take (Q4_1: md_qgemv only)
+bool layer_type(int32_t t) { return (t >= MD_Q8_0 && t <= MD_I4_ROW) || t == MD_I2_ROW; }
 
 constexpr int kMaxCols = 16384;
 constexpr int kMaxRows = 65536;
@@ -260,7 +260,7 @@ md_status run_ffn_mfma(const md_ffn* f, const ChunkAct& xa, int T, float* h, u16
                                           static_cast<const uint8_t*>(f->up.q), f->gate.row_scale, f->up.row_scale, 0,
                                           F, H, f->act, d, 1, xa.dig, xa.expo, true, h, st);
     if (e != hipSuccess) return hip_fail(e, "ffn gate/up launch");
-    e = md::launch_limbs(h, T, F, fmt == MD_I4_ROW, h_dig, h_exp, st);
+    e = md::launch_limbs(h, T, F, fmt, h_dig, h_exp, st);
     if (e != hipSuccess) return hip_fail(e, "digit launch");
     e = md::launch_moe_mfma_i8(fmt, false, static_cast<const uint8_t*>(f->down.q), nullptr, f->down.row_scale, nullptr,
                                0, H, F, f->act, d, 1, h_dig, h_exp, false, y, st);
@@ -505,7 +505,7 @@ md_status md_ffn_forward(const md_ffn* f, const float* x, int32_t T, float* y, v
   int8_t* h_dig = reinterpret_cast<int8_t*>(ws + off); off += align256(4 * T * F);
   int* x_exp = reinterpret_cast<int*>(ws + off); off += align256(sizeof(int) * T);
   int* h_exp = reinterpret_cast<int*>(ws + off);
-  hipError_t e = row_type(f->gate.type) ? md::launch_limbs(x, T, H, f->gate.type == MD_I4_ROW, x_dig, x_exp, stream)
+  hipError_t e = row_type(f->gate.type) ? md::launch_limbs(x, T, H, f->gate.type, x_dig, x_exp, stream)
                                         : md::launch_split_bf16(x, (int64_t)T * H, x_hi, x_lo, stream);
   if (e != hipSuccess) return hip_fail(e, "activation split launch");
   s = run_ffn_mfma(f, ChunkAct{x_hi, x_lo, x_dig, x_exp}, T, h, h_hi, h_lo, h_dig, h_exp, y, stream);
@@ -718,7 +718,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       xa.lo = static_cast<u16*>(P(w.x_lo));
     }
     if (need_dig) {
-      e = md::launch_limbs(x, T, H, fmt == MD_I4_ROW, static_cast<int8_t*>(P(w.x_dig)), static_cast<int*>(P(w.x_exp)),
+      e = md::launch_limbs(x, T, H, fmt, static_cast<int8_t*>(P(w.x_dig)), static_cast<int*>(P(w.x_exp)),
                            stream);
       if (e != hipSuccess) return hip_fail(e, "digit launch");
       xa.dig = static_cast<int8_t*>(P(w.x_dig));
@@ -729,7 +729,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     ChunkAct xs = xa;
     const int sfmt = L->shared.gate.type;
     if (row_type(sfmt)) {  // x digits in the shared expert's own column order
-      e = md::launch_limbs(x, T, H, sfmt == MD_I4_ROW, static_cast<int8_t*>(P(w.xs_dig)),
+      e = md::launch_limbs(x, T, H, sfmt, static_cast<int8_t*>(P(w.xs_dig)),
                            static_cast<int*>(P(w.xs_exp)), stream);
       if (e != hipSuccess) return hip_fail(e, "digit launch");
       xs.dig = static_cast<int8_t*>(P(w.xs_dig));
@@ -770,7 +770,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
                                stream);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
     if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
-    e = md::launch_limbs(h, T * k, F, fmt == MD_I4_ROW, h_dig, h_exp, stream);
+    e = md::launch_limbs(h, T * k, F, fmt, h_dig, h_exp, stream);
     if (e != hipSuccess) return hip_fail(e, "digit launch");
     e = md::launch_moe_mfma_i8(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
                                dn_bytes, H, F, L->act, d, A, h_dig, h_exp, false, o, stream);

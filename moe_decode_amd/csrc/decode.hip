@@ -60,6 +60,7 @@ MD_DEV void dig_rows(const DigJob& j, uint32_t* ys, int b, int nb) {
       case Q8_0: dig_block<Q8_0>(v, n, ys, j.planes + g0 * Dig<Q8_0>::NPL, j.scales + g0); break;
       case Q4_0: dig_block<Q4_0>(v, n, ys, j.planes + g0 * Dig<Q4_0>::NPL, j.scales + g0); break;
       case I8_ROW: dig_block<I8_ROW>(v, n, ys, j.planes + g0 * Dig<I8_ROW>::NPL, j.scales + g0); break;
+      case I2_ROW: dig_block<I2_ROW>(v, n, ys, j.planes + g0 * Dig<I2_ROW>::NPL, j.scales + g0); break;
       default: dig_block<I4_ROW>(v, n, ys, j.planes + g0 * Dig<I4_ROW>::NPL, j.scales + g0); break;
     }
   }
@@ -243,9 +244,11 @@ struct GateUpT1 {
 // in LDS.  blockIdx.y = t * slots + j: token t's slot j (each pair of a
 // several-token call is an independent one-token problem).  The block's rows
 // are whole digit groups of h, whose planes it writes for the down kernel.
-// At least 6 waves per SIMD (<= 80 VGPRs): two 12-wave workgroups per CU.
+// At least 6 waves per SIMD (<= 80 VGPRs): two 12-wave workgroups per CU
+// (packed int2: 4 waves, <= 128 VGPRs, for its twelve activation planes).
 template <int FMT, int L, int kNP, bool kLoop>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6))) void k_gateup_t1(GateUpT1 a) {
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(FMT == I2_ROW ? 4 : 6))) void k_gateup_t1(
+    GateUpT1 a) {
   using D = Dig<FMT>;
   constexpr int G = 64 / L;
   extern __shared__ float lds[];  // [npairs] h values, then [RGW][G][kNP][KS][2] slice sums
@@ -536,7 +539,7 @@ hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const
 #define MD_GUL(F_) MD_GU(F_, 64, 8) MD_GU(F_, 32, 8) MD_GU(F_, 16, 8) MD_GU(F_, 8, 8) \
                    MD_GU(F_, 64, 4) MD_GU(F_, 32, 4) MD_GU(F_, 16, 4) MD_GU(F_, 8, 4) \
                    MD_GU(F_, 64, 2) MD_GU(F_, 32, 2) MD_GU(F_, 16, 2) MD_GU(F_, 8, 2)
-  MD_GUL(Q8_0) MD_GUL(Q4_0) MD_GUL(I8_ROW) MD_GUL(I4_ROW)
+  MD_GUL(Q8_0) MD_GUL(Q4_0) MD_GUL(I8_ROW) MD_GUL(I4_ROW) MD_GUL(I2_ROW)
 #undef MD_GUL
 #undef MD_GU
   return hipErrorInvalidConfiguration;
@@ -554,7 +557,7 @@ hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t m
     hipLaunchKernelGGL((k_down_t1<F_, L_, C_>), grid, block, 0, st, a); return hipGetLastError(); }
 #define MD_DNL(F_, L_) MD_DN(F_, L_, 1) MD_DN(F_, L_, 2) MD_DN(F_, L_, 3)
 #define MD_DNF(F_) MD_DNL(F_, 64) MD_DNL(F_, 32) MD_DNL(F_, 16) MD_DNL(F_, 8)
-  MD_DNF(Q8_0) MD_DNF(Q4_0) MD_DNF(I8_ROW) MD_DNF(I4_ROW)
+  MD_DNF(Q8_0) MD_DNF(Q4_0) MD_DNF(I8_ROW) MD_DNF(I4_ROW) MD_DNF(I2_ROW)
 #undef MD_DNF
 #undef MD_DNL
 #undef MD_DN

@@ -8,7 +8,8 @@
 // (three digits in [-128, 127], 8-bit weights): adding the bias
 // B = sum_j 8*16^j (or 128*256^j) makes every nibble (byte) of Y = X + B the
 // digit plus 8 (128), so flipping its top bit gives the digit as a two's-
-// complement nibble (byte).  Plane j packs digit j of every value of the group
+// complement nibble (byte).  (Packed int2 weights use base 16 with two planes
+// per digit, one for the even and one for the odd weights of each nibble.)  Plane j packs digit j of every value of the group
 // into the nibble or byte position of the weight it multiplies, so one dot
 // instruction per weight word forms  sum_i w_i * d_j(X_i)  exactly in int32,
 // and  sum_j base^j * P_j = sum_i w_i X_i.  The chunk's value is that integer
@@ -22,27 +23,46 @@
 
 namespace md {
 
+// Plane p holds digit digit(p) of the group's values; nibble (byte) i of its
+// word m belongs to value pos(p, m, i).
 template <int FMT> struct Dig;
 template <> struct Dig<Q4_0> {
   static constexpr int NV = 32, NPL = 6, SB = 22, SH = 4, PER = 8;
   static constexpr uint32_t BIAS = 0x00888888u, FLIP = 0x88888888u;
+  static constexpr int digit(int p) { return p; }
   // word m, nibble i <- value: low nibble of byte b is weight 4m+b, high is 16+4m+b
-  static constexpr int pos(int m, int i) { return (i & 1) ? 16 + 4 * m + (i >> 1) : 4 * m + (i >> 1); }
+  static constexpr int pos(int, int m, int i) { return (i & 1) ? 16 + 4 * m + (i >> 1) : 4 * m + (i >> 1); }
 };
 template <> struct Dig<I4_ROW> {
   static constexpr int NV = 32, NPL = 6, SB = 22, SH = 4, PER = 8;
   static constexpr uint32_t BIAS = 0x00888888u, FLIP = 0x88888888u;
-  static constexpr int pos(int m, int i) { return 8 * m + i; }
+  static constexpr int digit(int p) { return p; }
+  static constexpr int pos(int, int m, int i) { return 8 * m + i; }
+};
+// Packed int2: a 16-byte chunk holds 64 weights; nibble i of weight word m
+// holds weights 16m+2i (bits 0-1) and 16m+2i+1 (bits 2-3).  Each digit has
+// two planes: plane 2j pairs digit j of the even weights' activations with
+// those nibbles, plane 2j+1 digit j of the odd ones'.
+template <> struct Dig<I2_ROW> {
+  static constexpr int NV = 64, NPL = 12, SB = 22, SH = 4, PER = 8;
+  static constexpr uint32_t BIAS = 0x00888888u, FLIP = 0x88888888u;
+  static constexpr int digit(int p) { return p >> 1; }
+  static constexpr int pos(int p, int m, int i) { return 16 * m + 2 * i + (p & 1); }
 };
 template <> struct Dig<Q8_0> {
   static constexpr int NV = 16, NPL = 3, SB = 22, SH = 8, PER = 4;
   static constexpr uint32_t BIAS = 0x00808080u, FLIP = 0x80808080u;
-  static constexpr int pos(int m, int i) { return 4 * m + i; }
+  static constexpr int digit(int p) { return p; }
+  static constexpr int pos(int, int m, int i) { return 4 * m + i; }
 };
 template <> struct Dig<I8_ROW> : Dig<Q8_0> {};
 
-__host__ __device__ constexpr int dig_nv(int fmt) { return (fmt == Q8_0 || fmt == I8_ROW) ? 16 : 32; }
-__host__ __device__ constexpr int dig_npl(int fmt) { return (fmt == Q8_0 || fmt == I8_ROW) ? 3 : 6; }
+__host__ __device__ constexpr int dig_nv(int fmt) {
+  return (fmt == Q8_0 || fmt == I8_ROW) ? 16 : fmt == I2_ROW ? 64 : 32;
+}
+__host__ __device__ constexpr int dig_npl(int fmt) {
+  return (fmt == Q8_0 || fmt == I8_ROW) ? 3 : fmt == I2_ROW ? 12 : 6;
+}
 // bytes of digit planes per group, and per K activations
 __host__ __device__ constexpr int64_t dig_group_bytes(int fmt) { return 16 * dig_npl(fmt); }
 __host__ __device__ constexpr int64_t dig_bytes(int fmt, int K) { return (int64_t)(K / dig_nv(fmt)) * dig_group_bytes(fmt); }
@@ -63,14 +83,15 @@ MD_DEV uint32_t dig_biased(float v, int s) {
   return (uint32_t)(int)rintf(ldexpf(v, s)) + Dig<FMT>::BIAS;
 }
 
-// Word (plane j, weight word m) of a group from the biased images Y[0..NV).
+// Word (plane p, weight word m) of a group from the biased images Y[0..NV).
 template <int FMT, typename GetY>
-MD_DEV uint32_t dig_word(int j, int m, GetY Y) {
+MD_DEV uint32_t dig_word(int p, int m, GetY Y) {
   using D = Dig<FMT>;
   constexpr uint32_t mask = (1u << D::SH) - 1u;
+  const int j = D::digit(p);
   uint32_t w = 0;
 #pragma unroll
-  for (int i = 0; i < D::PER; ++i) w |= ((Y(D::pos(m, i)) >> (D::SH * j)) & mask) << (D::SH * i);
+  for (int i = 0; i < D::PER; ++i) w |= ((Y(D::pos(p, m, i)) >> (D::SH * j)) & mask) << (D::SH * i);
   return w ^ D::FLIP;
 }
 
@@ -113,6 +134,28 @@ struct DigAcc {
 template <int FMT>
 MD_DEV float dig_chunk(u32x4 w, const u32x4* d, float sc, DigAcc<FMT>& r) {
   using D = Dig<FMT>;
+  if constexpr (FMT == I2_ROW) {
+    // even weights sign-extended from bits 0-1 to whole nibbles; odd weights
+    // stay in bits 2-3, i.e. nibbles of 4 * value: 4 * sum = sum_j 16^j (4 E_j + O_j)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t e = w[m] & 0x33333333u, sg = e & 0x22222222u;
+      const uint32_t we = e | (sg << 1) | (sg << 2), wo = w[m] & 0xCCCCCCCCu;
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        r.a[2 * j] = __builtin_amdgcn_sdot8((int)we, (int)d[2 * j][m], r.a[2 * j], false);
+        r.a[2 * j + 1] = __builtin_amdgcn_sdot8((int)wo, (int)d[2 * j + 1][m], r.a[2 * j + 1], false);
+      }
+    }
+    uint32_t p[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) p[j] = 4u * (uint32_t)r.a[2 * j] + (uint32_t)r.a[2 * j + 1];
+    const uint32_t lo = p[0] + 16u * (p[1] + 16u * (p[2] + 16u * p[3])), hi = p[4] + 16u * p[5];
+    const int dlo = (int)(lo - (uint32_t)r.lo), dhi = (int)(hi - (uint32_t)r.hi);
+    r.lo = (int)lo;
+    r.hi = (int)hi;
+    return fmaf((float)dhi, sc * 16384.0f, (float)dlo * (sc * 0.25f));
+  }
   if constexpr (FMT == Q4_0) w ^= u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};  // n - 8
 #pragma unroll
   for (int j = 0; j < D::NPL; ++j) {

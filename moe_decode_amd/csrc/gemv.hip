@@ -347,7 +347,7 @@ static int choose_R(int rows, int G, int experts, const int* opts, int nopt) {
 
 GemvCfg gateup_config(int fmt, int F, int H, int max_active, int T) {
   GemvCfg c{};
-  c.L = pow2_divisor_le64(nchunks(fmt, H));
+  c.L = std::max(8, pow2_divisor_le64(nchunks(fmt, H)));
   const int G = 64 / c.L;
   c.B = T == 1 ? 1 : 4;
   const int opts1[] = {2, 1};
@@ -361,7 +361,7 @@ GemvCfg gateup_config(int fmt, int F, int H, int max_active, int T) {
 
 GemvCfg down_config(int fmt, int H, int F, int max_active, int T) {
   GemvCfg c{};
-  c.L = pow2_divisor_le64(nchunks(fmt, F));
+  c.L = std::max(8, pow2_divisor_le64(nchunks(fmt, F)));
   const int G = 64 / c.L;
   c.B = T == 1 ? 1 : 4;
   const int opts[] = {4, 2, 1};
@@ -397,6 +397,7 @@ hipError_t launch_gateup(int fmt, const GemvCfg& c, const uint8_t* gq, const uin
     case Q4_0: return gateup_f<Q4_0>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
     case I8_ROW: return gateup_f<I8_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
     case I4_ROW: return gateup_f<I4_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
+    case I2_ROW: return gateup_f<I2_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
   }
   return hipErrorInvalidValue;
 }
@@ -422,6 +423,7 @@ hipError_t launch_down(int fmt, const GemvCfg& c, const uint8_t* dq, const float
     case Q4_0: return down_f<Q4_0>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
     case I8_ROW: return down_f<I8_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
     case I4_ROW: return down_f<I4_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
+    case I2_ROW: return down_f<I2_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
   }
   return hipErrorInvalidValue;
 }

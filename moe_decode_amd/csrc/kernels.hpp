@@ -202,7 +202,7 @@ hipError_t launch_mfma_gemv(int fmt, const uint8_t* wq, const float* ws, int M, 
                             const uint16_t* a_lo, int ks, float* out, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int S, int64_t n, float* y, hipStream_t st);
 
-hipError_t launch_limbs(const float* a, int R, int K, bool perm4, int8_t* digits, int* expo, hipStream_t st);
+hipError_t launch_limbs(const float* a, int R, int K, int fmt, int8_t* digits, int* expo, hipStream_t st);
 hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uint8_t* wq2, const float* ws,
                               const float* ws2, int64_t mat_bytes, int M, int K, int act, const Disp& d,
                               int n_items, const int8_t* digits, const int* expo, bool act_by_token, float* out,

@@ -61,7 +61,7 @@ hipError_t launch_split_bf16(const float* x, int64_t n, u16* hi, u16* lo, hipStr
 template <int FMT>
 struct Tile {
   static constexpr bool B8 = (FMT == Q8_0 || FMT == I8_ROW);
-  static constexpr int WB = B8 ? kKT : kKT / 2;       // weight bytes per row per K tile
+  static constexpr int WB = B8 ? kKT : FMT == I2_ROW ? kKT / 4 : kKT / 2;  // weight bytes per row per K tile
   static constexpr int WSTR = WB + 16;                 // LDS row stride (bank spread)
   static constexpr int WCH = kRows * WB / 16;          // 16-byte weight chunks per tile
   static constexpr int WPT = WCH / 256;                // chunks per thread (2 or 4)
@@ -416,10 +416,12 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
 
 constexpr int kLST = kKT + 16;    // LDS stride of a digit plane row (bank spread)
 
-// Digit planes [R][4][K] (int8) and exponents [R].  Within every 8 columns
-// the 4-bit layout stores the even columns first (the order in which a
-// packed-int4 word's low and high nibbles are laid out as bytes).
-__global__ __launch_bounds__(256) void k_limbs(const float* __restrict__ a, int K, int perm4,
+// Digit planes [R][4][K] (int8) and exponents [R].  perm 1 (packed int4):
+// within every 8 columns the even columns come first (the order in which a
+// packed-int4 word's low and high nibbles are laid out as bytes); perm 2
+// (packed int2): within every 16 columns, column 4b + i goes to 4i + b (bit
+// pair i of the 4 bytes of a weight word forms one byte lane each).
+__global__ __launch_bounds__(256) void k_limbs(const float* __restrict__ a, int K, int perm,
                                                int8_t* __restrict__ digits, int* __restrict__ expo) {
   __shared__ float red[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -439,9 +441,12 @@ __global__ __launch_bounds__(256) void k_limbs(const float* __restrict__ a, int 
     const int X = (int)rintf(ldexpf(row[c], 30 - E));
     const unsigned Y = (unsigned)X + 0x00808080u;
     int p = c;
-    if (perm4) {
+    if (perm == 1) {
       const int w = c & 7;
       p = (c & ~7) + ((w & 1) ? 4 + (w >> 1) : (w >> 1));
+    } else if (perm == 2) {
+      const int w = c & 15;
+      p = (c & ~15) + 4 * (w & 3) + (w >> 2);
     }
     out[p] = (int8_t)((Y & 0xFFu) ^ 0x80u);
     out[K + p] = (int8_t)(((Y >> 8) & 0xFFu) ^ 0x80u);
@@ -450,8 +455,9 @@ __global__ __launch_bounds__(256) void k_limbs(const float* __restrict__ a, int 
   }
 }
 
-hipError_t launch_limbs(const float* a, int R, int K, bool perm4, int8_t* digits, int* expo, hipStream_t st) {
-  hipLaunchKernelGGL(k_limbs, dim3(R), dim3(256), 0, st, a, K, perm4 ? 1 : 0, digits, expo);
+hipError_t launch_limbs(const float* a, int R, int K, int fmt, int8_t* digits, int* expo, hipStream_t st) {
+  const int perm = fmt == I4_ROW ? 1 : fmt == I2_ROW ? 2 : 0;
+  hipLaunchKernelGGL(k_limbs, dim3(R), dim3(256), 0, st, a, K, perm, digits, expo);
   return hipGetLastError();
 }
 
@@ -476,6 +482,14 @@ template <int FMT>
 MD_DEV i32x4 decode_a8(const uint8_t* p) {
   if constexpr (FMT == I8_ROW) {
     return *reinterpret_cast<const i32x4*>(p);
+  } else if constexpr (FMT == I2_ROW) {  // 4 bytes = 16 weights; bytes 64*v, bit pair i of every byte first
+    const unsigned u = *reinterpret_cast<const unsigned*>(p);
+    i32x4 r;
+    r[0] = (int)opaque((u << 6) & 0xC0C0C0C0u);
+    r[1] = (int)opaque((u << 4) & 0xC0C0C0C0u);
+    r[2] = (int)opaque((u << 2) & 0xC0C0C0C0u);
+    r[3] = (int)opaque(u & 0xC0C0C0C0u);
+    return r;
   } else {  // I4_ROW: 8 bytes = 16 weights; bytes 16*v, even weights first in every 8
     const uint2 u = *reinterpret_cast<const uint2*>(p);
     i32x4 r;
@@ -502,7 +516,7 @@ MD_DEV i32x4 decode_a8(const uint8_t* p) {
 template <int FMT, int GU, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES))) void k_moe_mfma_i8(MfmaI8Args a) {
   using TL = Tile<FMT>;
-  constexpr int KB = TL::B8 ? 16 : 8;  // weight bytes per lane per 64-wide step
+  constexpr int KB = TL::B8 ? 16 : FMT == I2_ROW ? 4 : 8;  // weight bytes per lane per 64-wide step
   constexpr int BR = 64 * RT;          // weight rows per block
   constexpr int WCH = BR * TL::WB / 16, WPT = WCH / 256;
   __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BR * TL::WSTR];
@@ -681,7 +695,7 @@ hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uin
   MfmaI8Args a{wq, wq2, ws, ws2, mat_bytes, M, K, act, d, digits, expo, act_by_token ? 1 : 0, out, 1};
   // int4 weights: two row tiles per wave (LDS reads of the activation digits
   // per weight byte halve); int8: one (its weight tiles are twice as large)
-  const int RT = fmt == I4_ROW ? 2 : 1;
+  const int RT = fmt == I4_ROW || fmt == I2_ROW ? 2 : 1;
   const int rows_per_block = (gateup ? 32 : 64) * RT;
   const int tiles = d.items ? 1 : (d.T + kTok - 1) / kTok;
   // row blocks per workgroup: short rows (few K tiles) stream several row
@@ -695,7 +709,7 @@ hipError_t launch_moe_mfma_i8(int fmt, bool gateup, const uint8_t* wq, const uin
     if (gateup) hipLaunchKernelGGL((k_moe_mfma_i8<F_, 1, RT_>), grid, dim3(256), 0, st, a); \
     else hipLaunchKernelGGL((k_moe_mfma_i8<F_, 0, RT_>), grid, dim3(256), 0, st, a); \
     return hipGetLastError(); }
-  MD_MF8(I8_ROW, 1) MD_MF8(I4_ROW, 2)
+  MD_MF8(I8_ROW, 1) MD_MF8(I4_ROW, 2) MD_MF8(I2_ROW, 2)
 #undef MD_MF8
   return hipErrorInvalidValue;
 }

@@ -127,7 +127,7 @@ def test_moe_errors():
         (dict(type=md.I8_ROW), 1, "MD_ERR_INVALID_ARG"),
         (dict(has_shared=1), 1, "MD_ERR_INVALID_ARG"),
         (dict(type=md.Q4_1), 1, "MD_ERR_UNSUPPORTED"),           # md_qgemv only
-        (dict(type=md.I2_ROW, gate_scale=FAKE, up_scale=FAKE, down_scale=FAKE), 1, "MD_ERR_UNSUPPORTED"),
+        (dict(type=md.I2_ROW), 1, "MD_ERR_INVALID_ARG"),          # per-row type without scales
         (dict(type=7), 1, "MD_ERR_INVALID_ARG"),
         ({}, 0, "MD_ERR_SHAPE"),
         ({}, 129, "MD_ERR_UNSUPPORTED"),
@@ -137,6 +137,8 @@ def test_moe_errors():
         assert _status(L.md_moe_workspace_size(ctypes.byref(d), T, ctypes.byref(sz))) == want, (kw, T)
         assert _status(L.md_moe_layer_forward(ctypes.byref(d), FAKE, T, FAKE, None, None, FAKE, 1 << 30, None)) == \
             want, (kw, T)
+    i2 = _layer(type=md.I2_ROW, gate_scale=FAKE, up_scale=FAKE, down_scale=FAKE)   # packed int2 experts
+    assert L.md_moe_workspace_size(ctypes.byref(i2), 4, ctypes.byref(sz)) == 0 and sz.value > 0
     d = _layer()
     assert _status(L.md_moe_layer_forward(ctypes.byref(d), FAKE, 1, FAKE, None, None, FAKE, 16, None)) == \
         "MD_ERR_WORKSPACE"

@@ -100,7 +100,9 @@ def _moe_gpu(key, x):
                                    ("c3", 128),
                                    # verify-sized batches: small layers stay on the one-token kernels up to
                                    # 16 tokens, the large ones group by expert above 8
-                                   ("c0", 16), ("c3", 12), ("c3", 16), ("c4_i4", 12)])
+                                   ("c0", 16), ("c3", 12), ("c3", 16), ("c4_i4", 12),
+                                   # packed int2 experts: one token, a batch, a verify batch
+                                   ("c4_i2", 1), ("c4_i2", 4), ("c4_i2", 12)])
 def test_moe_layer_matches_oracle(orc_mt, key, T):
     sp = W.spec(key)
     x = W.moe_x(sp, T)
@@ -113,7 +115,7 @@ def test_moe_layer_matches_oracle(orc_mt, key, T):
     say(f"[moe] {key} T={T} max err/S {ratio:.2e}")
 
 
-@pytest.mark.parametrize("key", ["c4_i4", "c4_i8"])
+@pytest.mark.parametrize("key", ["c4_i4", "c4_i8", "c4_i2"])
 def test_moe_prefill_chunk_sampled(orc_mt, key):
     """128-token chunk at full size: routing of every token checked, outputs
     of a sample of tokens checked (tokens are independent in the layer)."""
@@ -276,6 +278,15 @@ _RAGGED = {
     # the widest hidden size the library takes (16384)
     "q8_h16384": W.MoESpec("q8_h16384", 44, 16384, 256, 8, 2, "gelu_tanh", "q8_0", (1e-3, 1e-2), 0.05, None, (1,)),
     "i4_h16384": W.MoESpec("i4_h16384", 45, 16384, 512, 16, 4, "silu", "i4_row", (1e-3, 1e-2), 0.05, 0.5, (1,)),
+    # packed int2: the one-token kernels (hidden 2560: 8-lane groups, 5 slices;
+    # FFN 1536: 3 chunks a lane), a layer only the grouped GEMMs take (FFN 1280),
+    # the widest hidden size, and an int2 shared expert beside Q8_0 experts
+    "i2_e72_k5": W.MoESpec("i2_e72_k5", 46, 2560, 1536, 72, 5, "gelu_tanh", "i2_row", (1e-3, 1e-2), 0.05, None,
+                           (1,)),
+    "i2_e24_k3": W.MoESpec("i2_e24_k3", 47, 768, 1280, 24, 3, "silu", "i2_row", (1e-3, 1e-2), 0.05, 0.5, (1,)),
+    "i2_h16384": W.MoESpec("i2_h16384", 48, 16384, 512, 16, 4, "silu", "i2_row", (1e-3, 1e-2), 0.05, None, (1,)),
+    "q8_e16_sh_i2": W.MoESpec("q8_e16_sh_i2", 49, 1536, 512, 16, 2, "gelu_tanh", "q8_0", (1e-3, 1e-2), 0.05, None,
+                              (1,), shared_F=1536, shared_fmt="i2_row", shared_d_range=(1e-3, 1e-2)),
 }
 _ragged_layers = {}
 
