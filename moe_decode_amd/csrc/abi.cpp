@@ -358,7 +358,8 @@ md_status md_prepare_layout(int32_t type, int32_t rows, int32_t cols, int32_t co
 // Batches of 4 or more on block formats run on the matrix cores (the VALU
 // engine re-reads every token's activations for every weight chunk).
 static bool gemv_on_mfma(const md_qmatrix* W, int batch) {
-  return batch >= 4 && (W->type == MD_Q8_0 || W->type == MD_Q4_0) && md::mfma_supported(W->cols);
+  return batch >= 4 && (W->type == MD_Q8_0 || W->type == MD_Q4_0 || W->type == MD_Q4_1) &&
+         md::mfma_supported(W->cols);
 }
 
 // Matrix-core GEMV workspace: [ks][batch][rows] partials (ks > 1), then the

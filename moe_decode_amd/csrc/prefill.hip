@@ -20,9 +20,11 @@
 // (4-bit codes are taken as 16 * value, see common.hpp), so its bf16 image is
 // exact; activations enter as a bf16 pair hi + lo with hi = bf16(x) and
 // lo = bf16(x - hi) (16 significant bits); the MFMA accumulates in fp32.
-// A 32-wide MFMA step covers exactly one Q8_0/Q4_0 block, so the block scale
-// is applied to the step's partial sums before they join the accumulator;
-// per-row scales are applied once at the end.
+// A 32-wide MFMA step covers exactly one Q8_0/Q4_0/Q4_1 block, so the block
+// scale is applied to the step's partial sums before they join the
+// accumulator (Q4_1 adds its minimum times the block's activation sum, which
+// one more MFMA per step forms for all rows at once); per-row scales are
+// applied once at the end.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,7 +67,8 @@ struct Tile {
   static constexpr int WSTR = WB + 16;                 // LDS row stride (bank spread)
   static constexpr int WCH = kRows * WB / 16;          // 16-byte weight chunks per tile
   static constexpr int WPT = WCH / 256;                // chunks per thread (2 or 4)
-  static constexpr bool BLK = (FMT == Q8_0 || FMT == Q4_0);
+  static constexpr bool BLK = (FMT == Q8_0 || FMT == Q4_0 || FMT == Q4_1);
+  static constexpr int SCW = FMT == Q4_1 ? 16 : 8;    // fp16 words of block constants per row per K tile
 };
 
 struct MfmaArgs {
@@ -96,6 +99,15 @@ MD_DEV bf16x8 decode_a(const uint8_t* p) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int b = 0; b < 4; ++b) a[4 * h + b] = (__bf16)(float)(signed char)(w[h] >> (8 * b));
+  } else if constexpr (FMT == Q4_1) {
+    // the Q4_0 order, unsigned codes: each masked byte is 16 * n
+    const unsigned v = *reinterpret_cast<const unsigned*>(p);
+    const unsigned lo = opaque((v << 4) & 0xF0F0F0F0u), hi = opaque(v & 0xF0F0F0F0u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      a[b] = (__bf16)(float)(unsigned char)(lo >> (8 * b));
+      a[4 + b] = (__bf16)(float)(unsigned char)(hi >> (8 * b));
+    }
   } else if constexpr (FMT == Q4_0) {
     // bytes b: low nibble = step weight 4q+b, high = 16+4q+b; elements [lo0..3, hi0..3]
     const unsigned v = *reinterpret_cast<const unsigned*>(p) ^ 0x88888888u;
@@ -122,7 +134,7 @@ MD_DEV bf16x8 decode_a(const uint8_t* p) {
 template <int FMT>
 MD_DEV bf16x8 load_b(const u16* tile, int j, int s, int q) {
   const u16* r = tile + j * kAST + 32 * s;
-  if constexpr (FMT == Q4_0) {
+  if constexpr (FMT == Q4_0 || FMT == Q4_1) {
     const uint2 a = *reinterpret_cast<const uint2*>(r + 4 * q);
     const uint2 b = *reinterpret_cast<const uint2*>(r + 16 + 4 * q);
     const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
@@ -145,7 +157,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
   constexpr int BR = 64 * RT;
   constexpr int WCH = BR * TL::WB / 16, WPT = WCH / 256;
   __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BR * TL::WSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][BR * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][BR * TL::SCW];
   __shared__ __attribute__((aligned(16))) u16 s_hi[2][kTok * kAST];
   __shared__ __attribute__((aligned(16))) u16 s_lo[2][kTok * kAST];
   __shared__ float s_up[BR / 2][kTok];
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
     constexpr bool has_lo = LO;
     // two register sets: tile kt+1 waits in one while tile kt+2 is in flight
     u32x4 rw[2][WPT];
-    u32x4 rs[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    u32x4 rs[2][TL::SCW / 8] = {};
     uint4 rh[2][2], rl[2][2];
     auto gload = [&](int ktl, int set) {
       const int kt = kt_begin + ktl;
@@ -212,7 +224,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       if constexpr (TL::BLK) {
         if (tid < BR) {
           const int scoff = FMT == Q8_0 ? a.K : (a.K / 32) * 16;
-          rs[set] = *reinterpret_cast<const u32x4*>(row_ptr(tid) + scoff + 16 * kt);
+#pragma unroll
+          for (int h = 0; h < TL::SCW / 8; ++h)
+            rs[set][h] = *reinterpret_cast<const u32x4*>(row_ptr(tid) + scoff + 2 * TL::SCW * kt + 16 * h);
         }
       }
 #pragma unroll
@@ -234,7 +248,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
         *reinterpret_cast<u32x4*>(&s_w[buf][r * TL::WSTR + 16 * piece]) = rw[set][i];
       }
       if constexpr (TL::BLK) {
-        if (tid < BR) *reinterpret_cast<u32x4*>(&s_sc[buf][tid * 8]) = rs[set];
+        if (tid < BR) {
+#pragma unroll
+          for (int h = 0; h < TL::SCW / 8; ++h)
+            *reinterpret_cast<u32x4*>(&s_sc[buf][tid * TL::SCW + 8 * h]) = rs[set][h];
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -252,6 +270,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       for (int s = 0; s < kKT / 32; ++s) {
         const bf16x8 bh = load_b<FMT>(s_hi[buf], li, s, q);
         const bf16x8 bl = has_lo ? load_b<FMT>(s_lo[buf], li, s, q) : bf16x8{};
+        // Q4_1: 16 times the block's sum of each token's activations (an
+        // operand of 16.0 in every row), for the block minimum
+        f32x4 zs = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FMT == Q4_1) {
+          const bf16x8 sixteen = __builtin_bit_cast(bf16x8, u32x4{0x41804180u, 0x41804180u, 0x41804180u, 0x41804180u});
+          zs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sixteen, bh, zs, 0, 0, 0);
+          if (has_lo) zs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sixteen, bl, zs, 0, 0, 0);
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const uint8_t* wp =
@@ -262,8 +288,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
             z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
             if (has_lo) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[rt][v] = fmaf(h2f(s_sc[buf][(wr + 16 * rt + 4 * q + v) * 8 + s]), z[v], acc[rt][v]);
+            for (int v = 0; v < 4; ++v) {
+              const int row = wr + 16 * rt + 4 * q + v;
+              if constexpr (FMT == Q4_1)
+                acc[rt][v] = fmaf(h2f(s_sc[buf][row * 16 + 2 * s]), z[v],
+                                  fmaf(h2f(s_sc[buf][row * 16 + 2 * s + 1]), zs[v], acc[rt][v]));
+              else
+                acc[rt][v] = fmaf(h2f(s_sc[buf][row * 8 + s]), z[v], acc[rt][v]);
+            }
           } else {
             acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rt], 0, 0, 0);
             if (has_lo) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rt], 0, 0, 0);
@@ -289,9 +321,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       __syncthreads();
     }
 
-    // 4-bit codes entered as 16 * value: one exact power-of-two scaling of
-    // the sums instead of one per step
-    if constexpr (FMT == Q4_0) {
+    // 4-bit codes entered as 16 * value (Q4_1: its block sums as 16 * sum):
+    // one exact power-of-two scaling of the sums instead of one per step
+    if constexpr (FMT == Q4_0 || FMT == Q4_1) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -367,12 +399,15 @@ hipError_t launch_mfma_gemv(int fmt, const uint8_t* wq, const float* ws, int M, 
   if (T < 1 || T > kTok || ks < 1) return hipErrorInvalidValue;
   const Disp d{nullptr, nullptr, nullptr, nullptr, 1, T};
   MfmaArgs a{wq, nullptr, ws, nullptr, 0, M, K, 0, d, a_hi, a_lo, 0, out, nullptr, nullptr, ks};
+  // (Q4_1: one row tile per wave; two would spill with its minimum terms)
   const int RT = (fmt == Q4_0 || fmt == I4_ROW) ? 2 : 1;
   const dim3 grid((M + 64 * RT - 1) / (64 * RT), 1, ks);
   if (fmt == Q8_0 && a_lo) hipLaunchKernelGGL((k_moe_mfma<Q8_0, 0, 1, true>), grid, dim3(256), 0, st, a);
   else if (fmt == Q8_0) hipLaunchKernelGGL((k_moe_mfma<Q8_0, 0, 1, false>), grid, dim3(256), 0, st, a);
   else if (fmt == Q4_0 && a_lo) hipLaunchKernelGGL((k_moe_mfma<Q4_0, 0, 2, true>), grid, dim3(256), 0, st, a);
   else if (fmt == Q4_0) hipLaunchKernelGGL((k_moe_mfma<Q4_0, 0, 2, false>), grid, dim3(256), 0, st, a);
+  else if (fmt == Q4_1 && a_lo) hipLaunchKernelGGL((k_moe_mfma<Q4_1, 0, 1, true>), grid, dim3(256), 0, st, a);
+  else if (fmt == Q4_1) hipLaunchKernelGGL((k_moe_mfma<Q4_1, 0, 1, false>), grid, dim3(256), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
