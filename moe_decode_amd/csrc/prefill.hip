@@ -133,16 +133,10 @@ MD_DEV bf16x8 decode_a(const uint8_t* p) {
 // elements for lane group q in step s.
 template <int FMT>
 MD_DEV bf16x8 load_b(const u16* tile, int j, int s, int q) {
-  const u16* r = tile + j * kAST + 32 * s;
-  if constexpr (FMT == Q4_0 || FMT == Q4_1) {
-    const uint2 a = *reinterpret_cast<const uint2*>(r + 4 * q);
-    const uint2 b = *reinterpret_cast<const uint2*>(r + 16 + 4 * q);
-    const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
-    return __builtin_bit_cast(bf16x8, v);
-  } else {
-    const uint4 v = *reinterpret_cast<const uint4*>(r + 8 * q);
-    return __builtin_bit_cast(bf16x8, v);
-  }
+  // (4-bit blocks: the tile was staged with x[4q..4q+3] and x[16+4q..16+4q+3]
+  // of every block side by side, so one 16-byte read serves all formats)
+  const uint4 v = *reinterpret_cast<const uint4*>(tile + j * kAST + 32 * s + 8 * q);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 #ifndef MD_BF_WAVES
@@ -249,15 +243,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       }
       if constexpr (TL::BLK) {
         if (tid < BR) {
+          if constexpr (FMT == Q4_1) {
+            for (int h = 0; h < TL::SCW / 8; ++h)
+              *reinterpret_cast<u32x4*>(&s_sc[buf][tid * TL::SCW + 8 * h]) = rs[set][h];
+          } else {
+            // block scales step-major, [step][row]: the four consecutive rows
+            // of a lane's MFMA outputs read their step's scales as one 8-byte load
+            const u32x4 w = rs[set][0];
 #pragma unroll
-          for (int h = 0; h < TL::SCW / 8; ++h)
-            *reinterpret_cast<u32x4*>(&s_sc[buf][tid * TL::SCW + 8 * h]) = rs[set][h];
+            for (int s2 = 0; s2 < 8; ++s2)
+              s_sc[buf][s2 * BR + tid] = (uint16_t)(w[s2 >> 1] >> (16 * (s2 & 1)));
+          }
         }
       }
+      if constexpr (FMT == Q4_0 || FMT == Q4_1) {
+        // nibble order: x[4q..4q+3] and x[16+4q..16+4q+3] of a block side by side
+        const int base = jj * kAST + 32 * (pp >> 1) + 4 * (pp & 1);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        *reinterpret_cast<uint4*>(&s_hi[buf][jj * kAST + 16 * pp + 8 * i]) = rh[set][i];
-        *reinterpret_cast<uint4*>(&s_lo[buf][jj * kAST + 16 * pp + 8 * i]) = rl[set][i];
+        for (int i = 0; i < 2; ++i) {
+          *reinterpret_cast<uint2*>(&s_hi[buf][base + 16 * i]) = make_uint2(rh[set][i].x, rh[set][i].y);
+          *reinterpret_cast<uint2*>(&s_hi[buf][base + 16 * i + 8]) = make_uint2(rh[set][i].z, rh[set][i].w);
+          *reinterpret_cast<uint2*>(&s_lo[buf][base + 16 * i]) = make_uint2(rl[set][i].x, rl[set][i].y);
+          *reinterpret_cast<uint2*>(&s_lo[buf][base + 16 * i + 8]) = make_uint2(rl[set][i].z, rl[set][i].w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          *reinterpret_cast<uint4*>(&s_hi[buf][jj * kAST + 16 * pp + 8 * i]) = rh[set][i];
+          *reinterpret_cast<uint4*>(&s_lo[buf][jj * kAST + 16 * pp + 8 * i]) = rl[set][i];
+        }
       }
     };
 
@@ -287,14 +301,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
             if (has_lo) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
+            if constexpr (FMT == Q4_1) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int row = wr + 16 * rt + 4 * q + v;
-              if constexpr (FMT == Q4_1)
+              for (int v = 0; v < 4; ++v) {
+                const int row = wr + 16 * rt + 4 * q + v;
                 acc[rt][v] = fmaf(h2f(s_sc[buf][row * 16 + 2 * s]), z[v],
                                   fmaf(h2f(s_sc[buf][row * 16 + 2 * s + 1]), zs[v], acc[rt][v]));
-              else
-                acc[rt][v] = fmaf(h2f(s_sc[buf][row * 8 + s]), z[v], acc[rt][v]);
+              }
+            } else {
+              const uint2 sc4 = *reinterpret_cast<const uint2*>(&s_sc[buf][s * BR + wr + 16 * rt + 4 * q]);
+              const unsigned sw[2] = {sc4.x, sc4.y};
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                acc[rt][v] = fmaf(h2f((uint16_t)(sw[v >> 1] >> (16 * (v & 1)))), z[v], acc[rt][v]);
             }
           } else {
             acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rt], 0, 0, 0);
