@@ -233,6 +233,83 @@ md_status md_moe_layer_forward_residual(const md_moe_layer *L /*host*/, const fl
  * pointers not 16-byte aligned -> MD_ERR_ALIGNMENT. */
 md_status md_add(const float *a, const float *b, float *y, int64_t n, hipStream_t stream);
 
+/* The experts of a layer for a given routing: y[t] = sum_j gates[t][j] *
+ * FFN_{idx[t][j]}(x[t]) -- the layer forward without the router (the
+ * TurboFieldfare summary, "memory and expert streaming": the runtime splits
+ * the router's choices into cache hits and misses before the experts run).
+ * idx, gates: device [T][k] (int32, fp32); a token's k entries must be
+ * distinct; entries outside [0, E) are clamped into it.  Needs
+ * md_moe_workspace_size(L, T) bytes of workspace.  Layers with a shared
+ * expert -> MD_ERR_UNSUPPORTED; other errors as md_moe_layer_forward. */
+md_status md_moe_experts_forward(const md_moe_layer *L /*host*/, const float *x, int32_t T, const int32_t *idx,
+                                 const float *gates, float *y, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Host-memory expert tier with an HBM slot cache (the Camelid README,
+ * "Supported": experts kept in host RAM with a VRAM-resident expert cache;
+ * the TurboFieldfare summary, "memory and expert streaming": a fixed number
+ * of expert slots per layer, least-frequently-used replacement with a
+ * recency tie-break, the router's choices split into hits and misses; the
+ * colibri summary, "model execution and memory tiers": per-layer caches of
+ * hot experts).  The whole expert set lives in host memory (pinned, so the
+ * copies run asynchronously), S slots of the same layout in HBM.  All arrays
+ * of the struct are host memory owned by the caller. */
+typedef struct md_expert_cache {
+  int32_t E;                 /* experts of the layer                              */
+  int32_t S;                 /* HBM slots                                         */
+  int32_t *slot_of_expert;   /* [E]: the slot holding expert e, or -1             */
+  int32_t *expert_in_slot;   /* [S]: the expert a slot holds, or -1 (empty)       */
+  int64_t *uses;             /* [S]: selections of the slot's expert since loaded */
+  int64_t *last_use;         /* [S]: the plan step that last selected it          */
+  int32_t *slot_idx;         /* [T*k] scratch of md_moe_cached_forward            */
+  int64_t step;              /* plan steps so far                                 */
+  int64_t hits, misses;      /* distinct-expert hits and misses so far            */
+} md_expert_cache;
+
+/* Empties the cache (all slots free, counters zero).  Errors: a null pointer
+ * -> MD_ERR_INVALID_ARG; E or S <= 0 -> MD_ERR_SHAPE. */
+md_status md_expert_cache_reset(md_expert_cache *c /*host*/);
+
+/* One step of the replacement policy for the n = T*k expert ids in idx
+ * (host): every distinct expert already in a slot is a hit (its use count
+ * and last use updated); every other one, in order of first appearance,
+ * takes an empty slot (lowest index first) or else evicts the slot with the
+ * fewest uses, ties to the least recently used, then to the lowest index,
+ * among the slots this step has not used.  Writes slot_idx[i] = the slot of
+ * idx[i], and the misses as (miss_expert, miss_slot) pairs, *n_miss of them
+ * (host arrays of n entries).  Errors: an id outside [0, E) or a null
+ * pointer -> MD_ERR_INVALID_ARG; n outside 1..1024 -> MD_ERR_SHAPE; more
+ * distinct experts than slots -> MD_ERR_UNSUPPORTED; nothing changes on
+ * error. */
+md_status md_expert_cache_plan(md_expert_cache *c /*host*/, const int32_t *idx, int32_t n, int32_t *slot_idx,
+                               int32_t *miss_expert, int32_t *miss_slot, int32_t *n_miss);
+
+/* Enqueues the copies of the missed experts' gate, up and down matrices (and
+ * row scales) from src (E experts, usually pinned host memory) into the
+ * slots of dst (a layer descriptor whose E is the slot count, in HBM) on
+ * stream.  Errors: src and dst of different H, F, type, act or k ->
+ * MD_ERR_SHAPE; an expert or slot out of range or a null pointer ->
+ * MD_ERR_INVALID_ARG. */
+md_status md_expert_cache_fill(const md_moe_layer *src /*host*/, const md_moe_layer *dst /*host*/,
+                               const int32_t *miss_expert, const int32_t *miss_slot, int32_t n_miss,
+                               hipStream_t stream);
+
+/* The layer forward with the expert tier: the router and top-k on the GPU
+ * (src's W_r / router_bias, device memory), one read-back of the routing
+ * (this call synchronizes the stream once), the cache plan, the copies of
+ * the misses, then md_moe_experts_forward on the slots with the slot ids.
+ * idx_out / gates_out (device, nullable) receive the expert ids and gates.
+ * c->slot_idx must hold T*k entries and stay untouched until the next call
+ * on the stream (an asynchronous copy reads it).  Workspace:
+ * md_moe_cached_workspace_size.  Errors: as md_moe_layer_forward,
+ * md_expert_cache_plan and md_expert_cache_fill; a cache whose E / S differ
+ * from src->E / dst->E -> MD_ERR_SHAPE; shared experts -> MD_ERR_UNSUPPORTED. */
+md_status md_moe_cached_workspace_size(const md_moe_layer *src /*host*/, const md_moe_layer *dst /*host*/, int32_t T,
+                                       size_t *bytes /*host*/);
+md_status md_moe_cached_forward(const md_moe_layer *src /*host*/, const md_moe_layer *dst /*host*/,
+                                md_expert_cache *c /*host*/, const float *x, int32_t T, float *y, int32_t *idx_out,
+                                float *gates_out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Measurement aid: reads nbytes of device memory at src once, in address
  * order, with every compute unit busy, and writes nothing unless some lane's
  * xor of the 32-bit words it read equals key (then that lane stores key at

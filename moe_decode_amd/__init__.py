@@ -24,7 +24,8 @@ EXPORTS = ("md_abi_version", "md_status_string", "md_last_error_detail", "md_row
            "md_qgemv_workspace_size", "md_qgemv", "md_route_workspace_size", "md_moe_route_topk",
            "md_ffn_workspace_size", "md_ffn_forward", "md_moe_workspace_size", "md_moe_layer_forward",
            "md_moe_layer_forward_timed", "md_moe_layer_forward_residual", "md_add",
-           "md_hbm_read_probe")
+           "md_hbm_read_probe", "md_moe_experts_forward", "md_expert_cache_reset", "md_expert_cache_plan",
+           "md_expert_cache_fill", "md_moe_cached_workspace_size", "md_moe_cached_forward")
 STAGES = {"shared": 0, "router": 1, "select": 2, "gateup": 3, "down": 4, "combine": 5}
 
 
@@ -86,6 +87,12 @@ def lib():
             "md_moe_layer_forward_residual": (i32, [vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
             "md_add": (i32, [vp, vp, vp, ctypes.c_int64, vp]),
             "md_hbm_read_probe": (i32, [vp, ctypes.c_size_t, ctypes.c_uint32, vp, i32, vp]),
+            "md_moe_experts_forward": (i32, [vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "md_expert_cache_reset": (i32, [vp]),
+            "md_expert_cache_plan": (i32, [vp, vp, i32, vp, vp, vp, vp]),
+            "md_expert_cache_fill": (i32, [vp, vp, vp, vp, i32, vp]),
+            "md_moe_cached_workspace_size": (i32, [vp, vp, i32, psz]),
+            "md_moe_cached_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -317,3 +324,103 @@ def hbm_read_probe(src, sink, key=0xFFFFFFFF, workgroups=0, stream=None):
     tensor of at least 4 bytes) untouched."""
     nbytes = src.numel() * src.element_size()
     _check(lib().md_hbm_read_probe(_ptr(src), nbytes, key, _ptr(sink), workgroups, _stream(stream)))
+
+
+def moe_experts_forward(layer, x, idx, gates, y=None, workspace=None, stream=None):
+    """The layer's experts for a given routing (idx int32, gates fp32, [T][k]
+    on the device): y[t] = sum_j gates[t][j] * expert idx[t][j] (x[t])."""
+    import torch
+    T = x.shape[0]
+    d = layer.desc()
+    if y is None:
+        y = torch.empty(T, layer.H, dtype=torch.float32, device=x.device)
+    ws, wsb = _workspace(moe_workspace_size(layer, T), x.device, workspace)
+    _check(lib().md_moe_experts_forward(ctypes.byref(d), _ptr(x), T, _ptr(idx), _ptr(gates), _ptr(y), _ptr(ws), wsb,
+                                        _stream(stream)))
+    return y
+
+
+class ExpertCacheState(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("slot_of_expert", ctypes.c_void_p), ("expert_in_slot", ctypes.c_void_p),
+                ("uses", ctypes.c_void_p), ("last_use", ctypes.c_void_p), ("slot_idx", ctypes.c_void_p),
+                ("step", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64)]
+
+
+class ExpertCache:
+    """The replacement state of an S-slot expert cache over E experts (host
+    arrays owned here, the policy in the library)."""
+
+    def __init__(self, E, S):
+        import numpy as np
+        self.slot_of_expert = np.empty(E, dtype=np.int32)
+        self.expert_in_slot = np.empty(S, dtype=np.int32)
+        self.uses = np.empty(S, dtype=np.int64)
+        self.last_use = np.empty(S, dtype=np.int64)
+        self.slot_idx = np.empty(128 * 8, dtype=np.int32)
+        self.state = ExpertCacheState(E, S, self.slot_of_expert.ctypes.data, self.expert_in_slot.ctypes.data,
+                                      self.uses.ctypes.data, self.last_use.ctypes.data, self.slot_idx.ctypes.data,
+                                      0, 0, 0)
+        self.reset()
+
+    def reset(self):
+        _check(lib().md_expert_cache_reset(ctypes.byref(self.state)))
+
+    def plan(self, idx):
+        """One policy step for the expert ids idx (host int32): returns the slot
+        ids and the (expert, slot) pairs to load."""
+        import numpy as np
+        idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(-1)
+        n = idx.size
+        slots = np.empty(n, dtype=np.int32)
+        me = np.empty(n, dtype=np.int32)
+        ms = np.empty(n, dtype=np.int32)
+        nm = ctypes.c_int32(0)
+        _check(lib().md_expert_cache_plan(ctypes.byref(self.state), idx.ctypes.data, n, slots.ctypes.data,
+                                          me.ctypes.data, ms.ctypes.data, ctypes.byref(nm)))
+        return slots, list(zip(me[:nm.value].tolist(), ms[:nm.value].tolist()))
+
+    @property
+    def hits(self):
+        return self.state.hits
+
+    @property
+    def misses(self):
+        return self.state.misses
+
+
+class ExpertTier:
+    """A MoE layer whose experts live in (pinned) host memory, with S slots of
+    HBM caching them: `host` is a MoELayer whose expert stacks are host
+    tensors (router weights on the device); the slots are allocated here."""
+
+    def __init__(self, host, S, device="cuda"):
+        import torch
+        self.host = host
+        self.S = S
+
+        def slots_like(m, rows):
+            q = torch.empty(S * rows * row_bytes(m.type, m.cols), dtype=torch.uint8, device=device)
+            sc = None if m.row_scale is None else torch.empty(S * rows, dtype=torch.float32, device=device)
+            return DevQMatrix(m.type, m.rows, m.cols, q, sc, S)
+        self.slots = MoELayer(host.H, host.F, S, host.k, host.act, slots_like(host.gate, host.F),
+                              slots_like(host.up, host.F), slots_like(host.down, host.H), host.Wr, host.bias)
+        self.cache = ExpertCache(host.E, S)
+
+    def workspace_size(self, T):
+        need = ctypes.c_size_t(0)
+        _check(lib().md_moe_cached_workspace_size(ctypes.byref(self.host.desc()), ctypes.byref(self.slots.desc()), T,
+                                                  ctypes.byref(need)))
+        return need.value
+
+    def forward(self, x, y=None, idx=None, gates=None, workspace=None, stream=None):
+        """y = layer(x) through the cache (one synchronisation per call)."""
+        import torch
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty(T, self.host.H, dtype=torch.float32, device=x.device)
+        ws, wsb = _workspace(self.workspace_size(T), x.device, workspace)
+        _check(lib().md_moe_cached_forward(ctypes.byref(self.host.desc()), ctypes.byref(self.slots.desc()),
+                                           ctypes.byref(self.cache.state), _ptr(x), T, _ptr(y), _ptr(idx),
+                                           _ptr(gates), _ptr(ws), wsb, _stream(stream)))
+        return y

@@ -795,6 +795,87 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   return ok();
 }
 
+// The experts of a layer for a given routing (idx, gates: device [T][k]):
+// the gate/up, down and combine stages of moe_forward without the router.
+// The routing is first copied into the workspace with every entry clamped
+// into [0, E), so no entry can address outside the expert stacks.
+static md_status experts_forward(const md_moe_layer* L, const float* x, int32_t T, const int32_t* idx_in,
+                                 const float* gates_in, float* y, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  md_status s = check_moe(L, T);
+  if (s != MD_OK) return s;
+  if (L->has_shared) return fail(MD_ERR_UNSUPPORTED, "experts forward: layers without a shared expert only");
+  if (!x || !y || !idx_in || !gates_in) return fail(MD_ERR_INVALID_ARG, "null x, y, idx or gates");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(idx_in) || !aligned16(gates_in))
+    return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const MoeWs w = moe_ws(L, T);
+  if ((s = check_ws(workspace, workspace_bytes, w.total)) != MD_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  auto P = [&](size_t off) { return static_cast<void*>(ws + off); };
+  const int H = L->H, F = L->F, E = L->E, k = L->k, fmt = L->type;
+  const int64_t gu_bytes = (int64_t)F * md::row_bytes(fmt, H);
+  const int64_t dn_bytes = (int64_t)H * md::row_bytes(fmt, F);
+  int* idx = static_cast<int*>(P(w.idx));
+  hipError_t e = md::launch_clamp_idx(idx_in, T * k, E, idx, stream);
+  if (e != hipSuccess) return hip_fail(e, "routing copy launch");
+  float* h = static_cast<float*>(P(w.h));
+  if (use_pairs(L, T)) {
+    const DigBuf xd = dig_buf_at(ws + w.xd, fmt, T, H);
+    const DigBuf hd = dig_buf_at(ws + w.hd, fmt, T * k, F);
+    e = md::launch_digits(dig_job(x, T, H, fmt, xd), stream);
+    if (e != hipSuccess) return hip_fail(e, "digit launch");
+    e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                             L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, nullptr, 1, nullptr,
+                             xd.planes, xd.scales, hd.planes, hd.scales, nullptr, nullptr, stream, idx);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
+                           gates_in, hd.planes, hd.scales, nullptr, y, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "down launch");
+  }
+  ChunkAct xa{nullptr, nullptr, nullptr, nullptr};
+  if (row_type(fmt)) {
+    e = md::launch_limbs(x, T, H, fmt, static_cast<int8_t*>(P(w.x_dig)), static_cast<int*>(P(w.x_exp)), stream);
+    xa.dig = static_cast<int8_t*>(P(w.x_dig));
+    xa.expo = static_cast<int*>(P(w.x_exp));
+  } else {
+    e = md::launch_split_bf16(x, (int64_t)T * H, static_cast<u16*>(P(w.x_hi)), static_cast<u16*>(P(w.x_lo)), stream);
+    xa.hi = static_cast<u16*>(P(w.x_hi));
+    xa.lo = static_cast<u16*>(P(w.x_lo));
+  }
+  if (e != hipSuccess) return hip_fail(e, "activation launch");
+  const int n_items = md::max_tiles(T, k, max_active(T, E, k));
+  md::DispOut dout{static_cast<int*>(P(w.n_active)), static_cast<int*>(P(w.active_e)),
+                   static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos)),
+                   static_cast<int4*>(P(w.items)), n_items};
+  e = md::launch_dispatch(idx, T, E, k, dout, stream);
+  if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+  md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T, dout.items};
+  float* o = static_cast<float*>(P(w.o));
+  if (row_type(fmt)) {
+    int8_t* h_dig = static_cast<int8_t*>(P(w.h_dig));
+    int* h_exp = static_cast<int*>(P(w.h_exp));
+    e = md::launch_moe_mfma_i8(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                               L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, n_items, xa.dig, xa.expo, true,
+                               h, stream);
+    if (e == hipSuccess) e = md::launch_limbs(h, T * k, F, fmt, h_dig, h_exp, stream);
+    if (e == hipSuccess)
+      e = md::launch_moe_mfma_i8(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
+                                 dn_bytes, H, F, L->act, d, n_items, h_dig, h_exp, false, o, stream);
+  } else {
+    u16* h_hi = static_cast<u16*>(P(w.h_hi));
+    u16* h_lo = static_cast<u16*>(P(w.h_lo));
+    e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                            L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, n_items, xa.hi, xa.lo, true, h,
+                            h_hi, h_lo, stream);
+    if (e == hipSuccess)
+      e = md::launch_moe_mfma(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
+                              dn_bytes, H, F, L->act, d, n_items, h_hi, h_lo, false, o, nullptr, nullptr, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "expert launch");
+  e = md::launch_combine(o, dout.pos_of_pair, gates_in, T, k, H, nullptr, nullptr, y, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "combine launch");
+}
+
 md_status md_moe_layer_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
                                float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr);
@@ -822,6 +903,201 @@ md_status md_add(const float* a, const float* b, float* y, int64_t n, hipStream_
   if (!aligned16(a) || !aligned16(b) || !aligned16(y)) return fail(MD_ERR_ALIGNMENT, "pointers not 16-byte aligned");
   const hipError_t e = md::launch_add(a, b, y, n, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "add launch");
+}
+
+md_status md_moe_experts_forward(const md_moe_layer* L, const float* x, int32_t T, const int32_t* idx,
+                                 const float* gates, float* y, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return experts_forward(L, x, T, idx, gates, y, workspace, workspace_bytes, stream);
+}
+
+// ---- host-memory expert tier ------------------------------------------------
+
+md_status md_expert_cache_reset(md_expert_cache* c) {
+  if (!c || !c->slot_of_expert || !c->expert_in_slot || !c->uses || !c->last_use)
+    return fail(MD_ERR_INVALID_ARG, "null cache or cache array");
+  if (c->E <= 0 || c->S <= 0) return fail(MD_ERR_SHAPE, "E = %d, S = %d", c->E, c->S);
+  for (int e = 0; e < c->E; ++e) c->slot_of_expert[e] = -1;
+  for (int j = 0; j < c->S; ++j) {
+    c->expert_in_slot[j] = -1;
+    c->uses[j] = 0;
+    c->last_use[j] = 0;
+  }
+  c->step = 0;
+  c->hits = 0;
+  c->misses = 0;
+  return ok();
+}
+
+md_status md_expert_cache_plan(md_expert_cache* c, const int32_t* idx, int32_t n, int32_t* slot_idx,
+                               int32_t* miss_expert, int32_t* miss_slot, int32_t* n_miss) {
+  if (!c || !c->slot_of_expert || !c->expert_in_slot || !c->uses || !c->last_use)
+    return fail(MD_ERR_INVALID_ARG, "null cache or cache array");
+  if (!idx || !slot_idx || !miss_expert || !miss_slot || !n_miss) return fail(MD_ERR_INVALID_ARG, "null argument");
+  if (n <= 0 || n > kMaxT * kMaxK) return fail(MD_ERR_SHAPE, "n = %d outside 1..%d", n, kMaxT * kMaxK);
+  // validate everything before any state changes
+  int distinct[kMaxT * kMaxK];
+  int nd = 0;
+  for (int i = 0; i < n; ++i) {
+    const int e = idx[i];
+    if (e < 0 || e >= c->E) return fail(MD_ERR_INVALID_ARG, "idx[%d] = %d outside [0, %d)", i, e, c->E);
+    bool seen = false;
+    for (int j = 0; j < nd && !seen; ++j) seen = distinct[j] == e;
+    if (!seen) distinct[nd++] = e;
+  }
+  if (nd > c->S) return fail(MD_ERR_UNSUPPORTED, "%d distinct experts in one call, %d slots", nd, c->S);
+  const int64_t step = ++c->step;
+  // hits first: they keep their slots for this call
+  for (int j = 0; j < nd; ++j) {
+    const int sl = c->slot_of_expert[distinct[j]];
+    if (sl >= 0) {
+      c->uses[sl] += 1;
+      c->last_use[sl] = step;
+      c->hits += 1;
+    }
+  }
+  // misses in order of first appearance: an empty slot (lowest index), else
+  // the least frequently used slot not used in this call, ties to the least
+  // recently used, then to the lowest index
+  int nm = 0;
+  for (int j = 0; j < nd; ++j) {
+    const int e = distinct[j];
+    if (c->slot_of_expert[e] >= 0) continue;
+    int v = -1;
+    for (int sl = 0; sl < c->S && v < 0; ++sl)
+      if (c->expert_in_slot[sl] < 0) v = sl;
+    if (v < 0) {
+      for (int sl = 0; sl < c->S; ++sl) {
+        if (c->last_use[sl] == step) continue;
+        if (v < 0 || c->uses[sl] < c->uses[v] || (c->uses[sl] == c->uses[v] && c->last_use[sl] < c->last_use[v]))
+          v = sl;
+      }
+    }
+    // (nd <= S guarantees a victim: at most nd - 1 other slots are in use by this call)
+    if (c->expert_in_slot[v] >= 0) c->slot_of_expert[c->expert_in_slot[v]] = -1;
+    c->expert_in_slot[v] = e;
+    c->slot_of_expert[e] = v;
+    c->uses[v] = 1;
+    c->last_use[v] = step;
+    c->misses += 1;
+    miss_expert[nm] = e;
+    miss_slot[nm] = v;
+    ++nm;
+  }
+  for (int i = 0; i < n; ++i) slot_idx[i] = c->slot_of_expert[idx[i]];
+  *n_miss = nm;
+  return ok();
+}
+
+static md_status check_tier_pair(const md_moe_layer* src, const md_moe_layer* dst) {
+  if (!src || !dst) return fail(MD_ERR_INVALID_ARG, "null layer descriptor");
+  if (src->H != dst->H || src->F != dst->F || src->type != dst->type || src->act != dst->act || src->k != dst->k)
+    return fail(MD_ERR_SHAPE, "host experts and slots differ in shape, type, act or k");
+  if (!src->gate_q || !src->up_q || !src->down_q || !dst->gate_q || !dst->up_q || !dst->down_q)
+    return fail(MD_ERR_INVALID_ARG, "null expert weights");
+  if (row_type(src->type) && (!src->gate_scale || !src->up_scale || !src->down_scale || !dst->gate_scale ||
+                              !dst->up_scale || !dst->down_scale))
+    return fail(MD_ERR_INVALID_ARG, "per-row type without scales");
+  return MD_OK;
+}
+
+md_status md_expert_cache_fill(const md_moe_layer* src, const md_moe_layer* dst, const int32_t* miss_expert,
+                               const int32_t* miss_slot, int32_t n_miss, hipStream_t stream) {
+  md_status s = check_tier_pair(src, dst);
+  if (s != MD_OK) return s;
+  if (n_miss < 0) return fail(MD_ERR_SHAPE, "n_miss = %d", n_miss);
+  if (n_miss > 0 && (!miss_expert || !miss_slot)) return fail(MD_ERR_INVALID_ARG, "null miss list");
+  for (int i = 0; i < n_miss; ++i) {
+    if (miss_expert[i] < 0 || miss_expert[i] >= src->E || miss_slot[i] < 0 || miss_slot[i] >= dst->E)
+      return fail(MD_ERR_INVALID_ARG, "miss %d: expert %d / slot %d out of range", i, miss_expert[i], miss_slot[i]);
+  }
+  const int64_t gb = (int64_t)src->F * md::row_bytes(src->type, src->H);
+  const int64_t db = (int64_t)src->H * md::row_bytes(src->type, src->F);
+  auto cp = [&](const void* from, int64_t fi, void* to, int64_t ti, int64_t bytes) {
+    return hipMemcpyAsync(static_cast<char*>(to) + ti * bytes, static_cast<const char*>(from) + fi * bytes,
+                          (size_t)bytes, hipMemcpyDefault, stream);
+  };
+  for (int i = 0; i < n_miss; ++i) {
+    const int e = miss_expert[i], sl = miss_slot[i];
+    hipError_t r = cp(src->gate_q, e, const_cast<void*>(dst->gate_q), sl, gb);
+    if (r == hipSuccess) r = cp(src->up_q, e, const_cast<void*>(dst->up_q), sl, gb);
+    if (r == hipSuccess) r = cp(src->down_q, e, const_cast<void*>(dst->down_q), sl, db);
+    if (r == hipSuccess && row_type(src->type)) {
+      r = cp(src->gate_scale, e, const_cast<float*>(dst->gate_scale), sl, 4 * (int64_t)src->F);
+      if (r == hipSuccess) r = cp(src->up_scale, e, const_cast<float*>(dst->up_scale), sl, 4 * (int64_t)src->F);
+      if (r == hipSuccess) r = cp(src->down_scale, e, const_cast<float*>(dst->down_scale), sl, 4 * (int64_t)src->H);
+    }
+    if (r != hipSuccess) return hip_fail(r, "expert copy");
+  }
+  return ok();
+}
+
+// Workspace of md_moe_cached_forward: the router's, the routing (expert ids,
+// gates, slot ids), then the slot layer's experts forward.
+struct CachedWs {
+  size_t route, idx, gates, slots, experts, total;
+};
+static md_status cached_ws(const md_moe_layer* src, const md_moe_layer* dst, int T, CachedWs& w) {
+  size_t route = 0;
+  md_status s = md_route_workspace_size(T, src->H, src->E, src->k, &route);
+  if (s != MD_OK) return s;
+  if ((s = check_moe(dst, T)) != MD_OK) return s;
+  w.route = 0;
+  w.idx = align256(route);
+  w.gates = w.idx + align256(sizeof(int) * T * src->k);
+  w.slots = w.gates + align256(sizeof(float) * T * src->k);
+  w.experts = w.slots + align256(sizeof(int) * T * src->k);
+  w.total = w.experts + moe_ws(dst, T).total;
+  return MD_OK;
+}
+
+md_status md_moe_cached_workspace_size(const md_moe_layer* src, const md_moe_layer* dst, int32_t T, size_t* bytes) {
+  md_status s = check_tier_pair(src, dst);
+  if (s != MD_OK) return s;
+  if (!bytes) return fail(MD_ERR_INVALID_ARG, "null bytes");
+  CachedWs w{};
+  if ((s = cached_ws(src, dst, T, w)) != MD_OK) return s;
+  *bytes = w.total;
+  return ok();
+}
+
+md_status md_moe_cached_forward(const md_moe_layer* src, const md_moe_layer* dst, md_expert_cache* c, const float* x,
+                                int32_t T, float* y, int32_t* idx_out, float* gates_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  md_status s = check_tier_pair(src, dst);
+  if (s != MD_OK) return s;
+  if (!c || !c->slot_idx) return fail(MD_ERR_INVALID_ARG, "null cache or cache scratch");
+  if (c->E != src->E || c->S != dst->E) return fail(MD_ERR_SHAPE, "cache of %d experts / %d slots for a %d-expert "
+                                                    "layer with %d slots", c->E, c->S, src->E, dst->E);
+  if (!src->W_r) return fail(MD_ERR_INVALID_ARG, "null router weights");
+  if (src->has_shared || dst->has_shared) return fail(MD_ERR_UNSUPPORTED, "layers without a shared expert only");
+  if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
+  if (!aligned16(x) || !aligned16(y) || (idx_out && !aligned16(idx_out)) || (gates_out && !aligned16(gates_out)))
+    return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  CachedWs w{};
+  if ((s = cached_ws(src, dst, T, w)) != MD_OK) return s;
+  if ((s = check_ws(workspace, workspace_bytes, w.total)) != MD_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  const int n = T * src->k;
+  int* idx = idx_out ? idx_out : reinterpret_cast<int*>(ws + w.idx);
+  float* gates = gates_out ? gates_out : reinterpret_cast<float*>(ws + w.gates);
+  int* slots = reinterpret_cast<int*>(ws + w.slots);
+  // 1. routing on the GPU, 2. read back (the one synchronisation), 3. the
+  // cache decides hits and misses, 4. misses copied from host memory,
+  // 5. the slot ids, 6. the experts on the slots
+  s = md_moe_route_topk(x, T, src->H, src->W_r, src->router_bias, src->E, src->k, idx, gates, nullptr, ws + w.route,
+                        w.idx - w.route, stream);
+  if (s != MD_OK) return s;
+  int host_idx[kMaxT * kMaxK];
+  hipError_t e = hipMemcpyAsync(host_idx, idx, sizeof(int) * n, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "routing read-back");
+  int miss_e[kMaxT * kMaxK], miss_s[kMaxT * kMaxK], nm = 0;
+  if ((s = md_expert_cache_plan(c, host_idx, n, c->slot_idx, miss_e, miss_s, &nm)) != MD_OK) return s;
+  if ((s = md_expert_cache_fill(src, dst, miss_e, miss_s, nm, stream)) != MD_OK) return s;
+  e = hipMemcpyAsync(slots, c->slot_idx, sizeof(int) * n, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "slot ids copy");
+  return experts_forward(dst, x, T, slots, gates, y, ws + w.experts, workspace_bytes - w.experts, stream);
 }
 
 md_status md_hbm_read_probe(const void* src, size_t nbytes, uint32_t key, uint32_t* sink, int32_t workgroups,

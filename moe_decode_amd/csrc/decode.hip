@@ -245,6 +245,7 @@ struct GateUpT1 {
   int* idx_out;          // [T][k], written by the blocks with blockIdx.x == 0 and slot 0
   float* gates_out;
   int KS, RGW;           // K-slices per row, row-group waves per block
+  const int* idx_in;     // [T][k] a given routing (part == nullptr): slot j of token t is expert idx_in[t][j]
 };
 
 // Block = KS * RGW waves.  Wave (rg, ks) streams kNP row pairs (gate row f
@@ -263,12 +264,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(FMT == I2_
   __shared__ int s_sel[8];
   __shared__ uint32_t ys[256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slots = a.part ? a.k : 1;
+  const int slots = (a.part || a.idx_in) ? a.k : 1;
   const int tok = blockIdx.y / slots, slot = blockIdx.y % slots;
   const int npairs = a.RGW * G * kNP;
   const int ngx = a.H / D::NV;
 
-  int e = 0;
+  int e = a.idx_in ? a.idx_in[tok * a.k + slot] : 0;
   if (a.part) {
     if (wave == 0) {
       int sel[8];
@@ -520,12 +521,13 @@ bool t1_supported(int fmt, int H, int F) {
 hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
                             int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const double* part, int S,
                             const float* bias, const void* xd, const float* xsc, void* hd, float* hsc, int* idx_out,
-                            float* gates_out, hipStream_t st) {
-  const int slots = (part ? k : 1) * T;
+                            float* gates_out, hipStream_t st, const int* idx_in) {
+  if (part && idx_in) return hipErrorInvalidValue;
+  const int slots = ((part || idx_in) ? k : 1) * T;
   GuGeom q;
   if (!gu_geom(fmt, F, H, slots, q)) return hipErrorInvalidConfiguration;
   GateUpT1 a{gq, uq, gs, us, mat_bytes, F, H, act, E, k, part, bias, S, static_cast<const u32x4*>(xd), xsc,
-             static_cast<u32x4*>(hd), hsc, idx_out, gates_out, q.KS, q.RGW};
+             static_cast<u32x4*>(hd), hsc, idx_out, gates_out, q.KS, q.RGW, idx_in};
   const int L = q.L, NP = q.NP;
   const int pairs_per_block = q.RGW * q.G * NP;
   // row tiles per slot; the grid holds at most what is resident at once, and

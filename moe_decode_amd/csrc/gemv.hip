@@ -493,6 +493,17 @@ hipError_t launch_read_probe(const void* src, int64_t n16, uint32_t key, uint32_
   return hipGetLastError();
 }
 
+// A given routing made safe to index with: entries clamped into [0, E).
+__global__ __launch_bounds__(kBlock) void k_clamp_idx(const int* __restrict__ in, int n, int E, int* __restrict__ out) {
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  if (i < n) out[i] = min(max(in[i], 0), E - 1);
+}
+
+hipError_t launch_clamp_idx(const int* in, int n, int E, int* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_clamp_idx, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, in, n, E, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
                           const float* y_shared, const float* y_residual, float* y, hipStream_t st) {
   const int64_t n = (int64_t)T * (H / 4);

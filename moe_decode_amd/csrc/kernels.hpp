@@ -118,7 +118,7 @@ bool t1_supported(int fmt, int H, int F);
 hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const float* gs, const float* us,
                             int64_t mat_bytes, int F, int H, int act, int E, int k, int T, const double* part, int S,
                             const float* bias, const void* xd, const float* xsc, void* hd, float* hsc, int* idx_out,
-                            float* gates_out, hipStream_t st);
+                            float* gates_out, hipStream_t st, const int* idx_in = nullptr);
 hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t mat_bytes, int H, int F, int k, int T,
                           const int* idx, const float* gates, const void* hd, const float* hsc, const float* y_add,
                           float* y, hipStream_t st);
@@ -223,6 +223,8 @@ hipError_t launch_add(const float* a, const float* b, float* y, int64_t n, hipSt
 hipError_t launch_read_probe(const void* src, int64_t n16, uint32_t key, uint32_t* sink, int grid,
                              hipStream_t st);
 hipError_t launch_copy_f32(const float* a, float* y, int64_t n, hipStream_t st);
+// out[i] = in[i] clamped into [0, E), i < n
+hipError_t launch_clamp_idx(const int* in, int n, int E, int* out, hipStream_t st);
 hipError_t launch_combine(const float* o, const int* pos_of_pair, const float* gates, int T, int k, int H,
                           const float* y_shared, const float* y_residual, float* y, hipStream_t st);
 

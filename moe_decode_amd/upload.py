@@ -35,3 +35,26 @@ def upload_stack(type_, rows, cols, count, fetch, device="cuda"):
 def upload_matrix(m, device="cuda"):
     """A single canonical matrix object (fmt, rows, cols, data, scales)."""
     return upload_stack(m.fmt, m.rows, m.cols, 1, lambda i: (m.data, m.scales), device)
+
+
+def upload_stack_host(type_, rows, cols, count, fetch, device="cuda"):
+    """As upload_stack, but the result stays in pinned host memory (in the
+    device layout, which the library's layout pass produces on the GPU one
+    matrix at a time): the expert set of a host-memory tier."""
+    t = TYPES.get(type_, type_)
+    rb = row_bytes(t, cols)
+    per = rows * rb
+    host = torch.empty(count * per, dtype=torch.uint8, pin_memory=True)
+    per_row = t in ROW_TYPES
+    sc = torch.empty(count * rows, dtype=torch.float32, pin_memory=True) if per_row else None
+    src = torch.empty(per, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    for i in range(count):
+        data, scales = fetch(i)
+        src.copy_(torch.from_numpy(np.ascontiguousarray(data, dtype=np.uint8).reshape(-1)))
+        prepare_layout(t, rows, cols, 1, src, dst)
+        host[i * per:(i + 1) * per].copy_(dst)
+        if per_row:
+            sc[i * rows:(i + 1) * rows].copy_(torch.from_numpy(np.ascontiguousarray(scales, dtype=np.float32)))
+    torch.cuda.current_stream().synchronize()
+    return DevQMatrix(t, rows, cols, host, sc, count)

@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import moe_decode_amd as md
-from moe_decode_amd.upload import upload_stack, upload_matrix
+from moe_decode_amd.upload import upload_stack, upload_stack_host, upload_matrix
 
 from . import workloads as W
 
@@ -31,6 +31,22 @@ def device_moe(sp, device="cuda"):
                         upload_matrix(sh["down"], device))
     return md.MoELayer(sp.H, sp.F, sp.E, sp.k, sp.act, stacks["gate"], stacks["up"], stacks["down"], Wr_t, b_t,
                        shared)
+
+
+def host_moe(sp, device="cuda"):
+    """The layer with its expert set in pinned host memory (the router on the
+    GPU): the source of a host-memory expert tier."""
+    stacks = {}
+    for part in ("gate", "up", "down"):
+        rows, cols = (sp.H, sp.F) if part == "down" else (sp.F, sp.H)
+
+        def fetch(e, part=part):
+            m = W.moe_expert_part(sp, e, part)
+            return m.data, m.scales
+        stacks[part] = upload_stack_host(sp.fmt, rows, cols, sp.E, fetch, device)
+    Wr, b = W.moe_router(sp)
+    return md.MoELayer(sp.H, sp.F, sp.E, sp.k, sp.act, stacks["gate"], stacks["up"], stacks["down"],
+                       torch.from_numpy(Wr).to(device), None if b is None else torch.from_numpy(b).to(device))
 
 
 def device_dense(sp, name, device="cuda"):
