@@ -355,6 +355,46 @@ def environment():
             "host_cpus": os.cpu_count()}
 
 
+def run_tier(key, S, steps, warmup=16):
+    """Decode through the host-memory expert tier: the expert set in pinned
+    host memory, S slots of HBM caching it.  Tokens cycle through the seeded
+    pool of 64, so a token's experts recur every 64 steps; the report gives
+    the hit rate, the bytes copied for the misses and the rate of those
+    copies.  Wall-clock timing: every call synchronises once (the routing is
+    read back to plan the copies)."""
+    import numpy as np
+    import torch
+    import moe_decode_amd as md
+    from synth import workloads as W
+    from synth.device import host_moe
+    sp = W.spec(key)
+    t = time.time()
+    host = host_moe(sp)
+    log(f"[bench] {key} expert set in pinned host memory ({time.time() - t:.1f} s)")
+    tier = md.ExpertTier(host, S)
+    rng = np.random.default_rng([sp.index, 777, 1, sp.variant])
+    xs = torch.from_numpy(rng.standard_normal((POOL, 1, sp.H)).astype(np.float32)).cuda()
+    y = torch.empty(1, sp.H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(tier.workspace_size(1), dtype=torch.uint8, device="cuda")
+    for i in range(warmup):
+        tier.forward(xs[i % POOL], y=y, workspace=ws)
+    torch.cuda.synchronize()
+    h0, m0 = tier.cache.hits, tier.cache.misses
+    t0 = time.perf_counter()
+    for i in range(steps):
+        tier.forward(xs[(warmup + i) % POOL], y=y, workspace=ws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    hits, misses = tier.cache.hits - h0, tier.cache.misses - m0
+    miss_bytes = misses * sp.expert_bytes()
+    del tier, host
+    torch.cuda.empty_cache()
+    return {"workload": key, "slots": S, "experts": sp.E, "steps": steps, "ms_per_step": dt * 1e3 / steps,
+            "tokens_per_s": steps / dt, "hit_rate": hits / max(1, hits + misses),
+            "miss_bytes_per_step": miss_bytes / steps, "miss_GBps": miss_bytes / dt / 1e9,
+            "timing": "wall clock around the calls (each call synchronises once)"}
+
+
 def copy_calibration(nbytes=1 << 30):
     """A plain 16-byte copy kernel of known size (the library's per-row-format
     layout pass, which is a copy): reads nbytes, writes nbytes."""
@@ -383,6 +423,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--stack", type=int, default=0,
                     help="also time a stack of this many distinct layers (one token) captured in one HIP graph")
+    ap.add_argument("--tier", type=int, default=0,
+                    help="also time decode through a host-memory expert tier with this many HBM slots")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -507,6 +549,12 @@ def main():
     if args.stack > 0:
         out["stack"] = run_stack(args.workload, args.stack, 20)
         log(f"[bench] stack: {out['stack']['us_per_layer']:.1f} us per layer")
+    if args.tier > 0:
+        layer = None  # the resident copy is not needed any more
+        torch.cuda.empty_cache()
+        out["tier"] = run_tier(args.workload, args.tier, max(32, args.steps // 2))
+        log(f"[bench] tier ({args.tier} slots): {out['tier']['tokens_per_s']:.0f} tokens/s, hit rate "
+            f"{out['tier']['hit_rate']:.2f}, misses {out['tier']['miss_GBps']:.1f} GB/s")
     print(json.dumps(out))
 
 
