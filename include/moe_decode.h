@@ -15,15 +15,23 @@
  *     Camelid README, "Gemma 4": 128 experts, sparse top-8 plus a dense shared
  *     expert; the TurboFieldfare summary, "memory and expert streaming":
  *     router-chosen experts, shared branch computed alongside, prefill in
- *     chunks of at most 128 tokens reusing each expert across rows).
+ *     chunks of at most 128 tokens reusing each expert across rows);
+ *   - two more weight codecs: Q4_1 blocks (the Camelid README's bit-exact
+ *     q4_1 GEMV) and packed int2 with one scale per row (the colibri summary);
+ *   - a host-memory expert tier: the expert set in host RAM, a slot cache of
+ *     experts in HBM (the Camelid README's experts-in-RAM lane with a VRAM
+ *     expert cache; the TurboFieldfare summary's expert slots).
  *
  * Conventions (every entry point):
  *   - Pointers marked "device" are HIP device pointers, "host" are host
  *     pointers.  The caller allocates and owns every buffer and the stream; the
- *     library never allocates, frees or synchronizes.  Work is enqueued on
- *     `stream` (NULL = the null stream) and completes asynchronously.
+ *     library never allocates, frees or synchronizes (one exception, stated
+ *     there: md_moe_cached_forward reads the routing back once per call).
+ *     Work is enqueued on `stream` (NULL = the null stream) and completes
+ *     asynchronously.
  *   - Every argument is validated on the host before anything is enqueued; a
- *     call that returns an error has enqueued nothing and written nothing.
+ *     call that returns an error has enqueued nothing and written nothing
+ *     (md_moe_cached_forward: nothing after the step that failed).
  *     Unsupported shapes return MD_ERR_UNSUPPORTED: there is no fallback.
  *   - Device data pointers must be 16-byte aligned (MD_ERR_ALIGNMENT).
  *   - md_last_error_detail() returns a thread-local message describing the
