@@ -246,9 +246,9 @@ md_status md_add(const float *a, const float *b, float *y, int64_t n, hipStream_
  * TurboFieldfare summary, "memory and expert streaming": the runtime splits
  * the router's choices into cache hits and misses before the experts run).
  * idx, gates: device [T][k] (int32, fp32); a token's k entries must be
- * distinct; entries outside [0, E) are clamped into it.  Needs
- * md_moe_workspace_size(L, T) bytes of workspace.  Layers with a shared
- * expert -> MD_ERR_UNSUPPORTED; other errors as md_moe_layer_forward. */
+ * distinct; entries outside [0, E) are clamped into it.  A shared expert
+ * is added as in md_moe_layer_forward.  Needs md_moe_workspace_size(L, T)
+ * bytes of workspace.  Errors as md_moe_layer_forward. */
 md_status md_moe_experts_forward(const md_moe_layer *L /*host*/, const float *x, int32_t T, const int32_t *idx,
                                  const float *gates, float *y, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
@@ -306,17 +306,23 @@ md_status md_expert_cache_fill(const md_moe_layer *src /*host*/, const md_moe_la
  * (src's W_r / router_bias, device memory), one read-back of the routing
  * (this call synchronizes the stream once), the cache plan, the copies of
  * the misses, then md_moe_experts_forward on the slots with the slot ids.
- * idx_out / gates_out (device, nullable) receive the expert ids and gates.
- * c->slot_idx must hold T*k entries and stay untouched until the next call
- * on the stream (an asynchronous copy reads it).  Workspace:
+ * With a copy_stream (and an event copy_done to join it), the misses load on
+ * it while dst's shared expert (resident) runs on stream, and the routed
+ * experts wait for the copies (the TurboFieldfare summary: misses filled
+ * while the shared branch computes); a null copy_stream puts the copies on
+ * stream.  idx_out / gates_out (device, nullable) receive the expert ids and
+ * gates.  c->slot_idx must hold T*k entries and stay untouched until the
+ * next call on the stream (an asynchronous copy reads it).  Workspace:
  * md_moe_cached_workspace_size.  Errors: as md_moe_layer_forward,
  * md_expert_cache_plan and md_expert_cache_fill; a cache whose E / S differ
- * from src->E / dst->E -> MD_ERR_SHAPE; shared experts -> MD_ERR_UNSUPPORTED. */
+ * from src->E / dst->E -> MD_ERR_SHAPE; a copy_stream without an event ->
+ * MD_ERR_INVALID_ARG. */
 md_status md_moe_cached_workspace_size(const md_moe_layer *src /*host*/, const md_moe_layer *dst /*host*/, int32_t T,
                                        size_t *bytes /*host*/);
 md_status md_moe_cached_forward(const md_moe_layer *src /*host*/, const md_moe_layer *dst /*host*/,
                                 md_expert_cache *c /*host*/, const float *x, int32_t T, float *y, int32_t *idx_out,
-                                float *gates_out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+                                float *gates_out, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipStream_t copy_stream, hipEvent_t copy_done);
 
 /* Measurement aid: reads nbytes of device memory at src once, in address
  * order, with every compute unit busy, and writes nothing unless some lane's

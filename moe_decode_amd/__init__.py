@@ -92,7 +92,7 @@ def lib():
             "md_expert_cache_plan": (i32, [vp, vp, i32, vp, vp, vp, vp]),
             "md_expert_cache_fill": (i32, [vp, vp, vp, vp, i32, vp]),
             "md_moe_cached_workspace_size": (i32, [vp, vp, i32, psz]),
-            "md_moe_cached_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "md_moe_cached_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -394,17 +394,23 @@ class ExpertTier:
     HBM caching them: `host` is a MoELayer whose expert stacks are host
     tensors (router weights on the device); the slots are allocated here."""
 
-    def __init__(self, host, S, device="cuda"):
+    def __init__(self, host, S, device="cuda", shared=None, overlap=True):
         import torch
         self.host = host
         self.S = S
+        # the misses load on a stream of their own while the shared expert runs
+        self.copy_stream = torch.cuda.Stream(device=device) if overlap else None
+        self.copy_done = torch.cuda.Event() if overlap else None
+        if self.copy_done is not None:
+            self.copy_done.record(self.copy_stream)   # torch creates the HIP event at its first record
 
         def slots_like(m, rows):
             q = torch.empty(S * rows * row_bytes(m.type, m.cols), dtype=torch.uint8, device=device)
             sc = None if m.row_scale is None else torch.empty(S * rows, dtype=torch.float32, device=device)
             return DevQMatrix(m.type, m.rows, m.cols, q, sc, S)
         self.slots = MoELayer(host.H, host.F, S, host.k, host.act, slots_like(host.gate, host.F),
-                              slots_like(host.up, host.F), slots_like(host.down, host.H), host.Wr, host.bias)
+                              slots_like(host.up, host.F), slots_like(host.down, host.H), host.Wr, host.bias,
+                              shared if shared is not None else host.shared)
         self.cache = ExpertCache(host.E, S)
 
     def workspace_size(self, T):
@@ -420,7 +426,9 @@ class ExpertTier:
         if y is None:
             y = torch.empty(T, self.host.H, dtype=torch.float32, device=x.device)
         ws, wsb = _workspace(self.workspace_size(T), x.device, workspace)
+        cs = self.copy_stream.cuda_stream if self.copy_stream is not None else None
+        ev = self.copy_done.cuda_event if self.copy_done is not None else None
         _check(lib().md_moe_cached_forward(ctypes.byref(self.host.desc()), ctypes.byref(self.slots.desc()),
                                            ctypes.byref(self.cache.state), _ptr(x), T, _ptr(y), _ptr(idx),
-                                           _ptr(gates), _ptr(ws), wsb, _stream(stream)))
+                                           _ptr(gates), _ptr(ws), wsb, _stream(stream), cs, ev))
         return y

@@ -796,21 +796,61 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
 }
 
 // The experts of a layer for a given routing (idx, gates: device [T][k]):
-// the gate/up, down and combine stages of moe_forward without the router.
+// the stages of moe_forward after the router, in two phases so that a caller
+// can put other work between them: the shared expert (into the workspace),
+// then the routed experts with the combine, which adds the shared output.
 // The routing is first copied into the workspace with every entry clamped
 // into [0, E), so no entry can address outside the expert stacks.
-static md_status experts_forward(const md_moe_layer* L, const float* x, int32_t T, const int32_t* idx_in,
-                                 const float* gates_in, float* y, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
+static md_status experts_check(const md_moe_layer* L, const float* x, int32_t T, const int32_t* idx_in,
+                               const float* gates_in, const float* y, size_t workspace_bytes, const void* workspace) {
   md_status s = check_moe(L, T);
   if (s != MD_OK) return s;
-  if (L->has_shared) return fail(MD_ERR_UNSUPPORTED, "experts forward: layers without a shared expert only");
   if (!x || !y || !idx_in || !gates_in) return fail(MD_ERR_INVALID_ARG, "null x, y, idx or gates");
   if (!aligned16(x) || !aligned16(y) || !aligned16(idx_in) || !aligned16(gates_in))
     return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  return check_ws(const_cast<void*>(workspace), workspace_bytes, moe_ws(L, T).total);
+}
+
+// Phase 1: the shared expert's output for the T tokens (nullptr without one).
+static md_status shared_phase(const md_moe_layer* L, const float* x, int32_t T, char* ws, hipStream_t stream,
+                              float** y_s_out) {
+  *y_s_out = nullptr;
+  if (!L->has_shared) return MD_OK;
   const MoeWs w = moe_ws(L, T);
-  if ((s = check_ws(workspace, workspace_bytes, w.total)) != MD_OK) return s;
-  char* ws = static_cast<char*>(workspace);
+  auto P = [&](size_t off) { return static_cast<void*>(ws + off); };
+  const int H = L->H, sfmt = L->shared.gate.type;
+  float* y_s = static_cast<float*>(P(w.y_s));
+  md_status s;
+  if (use_pairs(L, T)) {
+    const DigBuf sxd = dig_buf_at(ws + w.sxd, sfmt, T, H);
+    const DigBuf shd = dig_buf_at(ws + w.shd, sfmt, T, L->shared.gate.rows);
+    s = run_ffn(&L->shared, x, T, nullptr, sxd, shd, static_cast<float*>(P(w.h_s)), y_s, stream);
+  } else {
+    ChunkAct xs{nullptr, nullptr, nullptr, nullptr};
+    hipError_t e;
+    if (row_type(sfmt)) {
+      e = md::launch_limbs(x, T, H, sfmt, static_cast<int8_t*>(P(w.xs_dig)), static_cast<int*>(P(w.xs_exp)), stream);
+      xs.dig = static_cast<int8_t*>(P(w.xs_dig));
+      xs.expo = static_cast<int*>(P(w.xs_exp));
+    } else {
+      e = md::launch_split_bf16(x, (int64_t)T * H, static_cast<u16*>(P(w.x_hi)), static_cast<u16*>(P(w.x_lo)), stream);
+      xs.hi = static_cast<u16*>(P(w.x_hi));
+      xs.lo = static_cast<u16*>(P(w.x_lo));
+    }
+    if (e != hipSuccess) return hip_fail(e, "shared activation launch");
+    s = run_ffn_mfma(&L->shared, xs, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
+                     static_cast<u16*>(P(w.hs_lo)), static_cast<int8_t*>(P(w.hs_dig)), static_cast<int*>(P(w.hs_exp)),
+                     y_s, stream);
+  }
+  if (s != MD_OK) return s;
+  *y_s_out = y_s;
+  return MD_OK;
+}
+
+// Phase 2: the routed experts; y = their gated sum + y_add (nullable).
+static md_status routed_phase(const md_moe_layer* L, const float* x, int32_t T, const int32_t* idx_in,
+                              const float* gates_in, const float* y_add, float* y, char* ws, hipStream_t stream) {
+  const MoeWs w = moe_ws(L, T);
   auto P = [&](size_t off) { return static_cast<void*>(ws + off); };
   const int H = L->H, F = L->F, E = L->E, k = L->k, fmt = L->type;
   const int64_t gu_bytes = (int64_t)F * md::row_bytes(fmt, H);
@@ -829,7 +869,7 @@ static md_status experts_forward(const md_moe_layer* L, const float* x, int32_t 
                              xd.planes, xd.scales, hd.planes, hd.scales, nullptr, nullptr, stream, idx);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
     e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
-                           gates_in, hd.planes, hd.scales, nullptr, y, stream);
+                           gates_in, hd.planes, hd.scales, y_add, y, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "down launch");
   }
   ChunkAct xa{nullptr, nullptr, nullptr, nullptr};
@@ -872,8 +912,19 @@ static md_status experts_forward(const md_moe_layer* L, const float* x, int32_t 
                               dn_bytes, H, F, L->act, d, n_items, h_hi, h_lo, false, o, nullptr, nullptr, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "expert launch");
-  e = md::launch_combine(o, dout.pos_of_pair, gates_in, T, k, H, nullptr, nullptr, y, stream);
+  e = md::launch_combine(o, dout.pos_of_pair, gates_in, T, k, H, y_add, nullptr, y, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "combine launch");
+}
+
+static md_status experts_forward(const md_moe_layer* L, const float* x, int32_t T, const int32_t* idx_in,
+                                 const float* gates_in, float* y, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  md_status s = experts_check(L, x, T, idx_in, gates_in, y, workspace_bytes, workspace);
+  if (s != MD_OK) return s;
+  char* ws = static_cast<char*>(workspace);
+  float* y_s = nullptr;
+  if ((s = shared_phase(L, x, T, ws, stream, &y_s)) != MD_OK) return s;
+  return routed_phase(L, x, T, idx_in, gates_in, y_s, y, ws, stream);
 }
 
 md_status md_moe_layer_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
@@ -1063,14 +1114,15 @@ md_status md_moe_cached_workspace_size(const md_moe_layer* src, const md_moe_lay
 
 md_status md_moe_cached_forward(const md_moe_layer* src, const md_moe_layer* dst, md_expert_cache* c, const float* x,
                                 int32_t T, float* y, int32_t* idx_out, float* gates_out, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                size_t workspace_bytes, hipStream_t stream, hipStream_t copy_stream,
+                                hipEvent_t copy_done) {
   md_status s = check_tier_pair(src, dst);
   if (s != MD_OK) return s;
   if (!c || !c->slot_idx) return fail(MD_ERR_INVALID_ARG, "null cache or cache scratch");
   if (c->E != src->E || c->S != dst->E) return fail(MD_ERR_SHAPE, "cache of %d experts / %d slots for a %d-expert "
                                                     "layer with %d slots", c->E, c->S, src->E, dst->E);
   if (!src->W_r) return fail(MD_ERR_INVALID_ARG, "null router weights");
-  if (src->has_shared || dst->has_shared) return fail(MD_ERR_UNSUPPORTED, "layers without a shared expert only");
+  if (copy_stream && !copy_done) return fail(MD_ERR_INVALID_ARG, "a copy stream needs an event");
   if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
   if (!aligned16(x) || !aligned16(y) || (idx_out && !aligned16(idx_out)) || (gates_out && !aligned16(gates_out)))
     return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
@@ -1094,10 +1146,17 @@ md_status md_moe_cached_forward(const md_moe_layer* src, const md_moe_layer* dst
   if (e != hipSuccess) return hip_fail(e, "routing read-back");
   int miss_e[kMaxT * kMaxK], miss_s[kMaxT * kMaxK], nm = 0;
   if ((s = md_expert_cache_plan(c, host_idx, n, c->slot_idx, miss_e, miss_s, &nm)) != MD_OK) return s;
-  if ((s = md_expert_cache_fill(src, dst, miss_e, miss_s, nm, stream)) != MD_OK) return s;
+  // the misses load on the copy stream while the shared expert (resident)
+  // runs on the compute stream; the routed experts wait for both
+  if ((s = md_expert_cache_fill(src, dst, miss_e, miss_s, nm, copy_stream ? copy_stream : stream)) != MD_OK) return s;
+  if (copy_stream && (e = hipEventRecord(copy_done, copy_stream)) != hipSuccess) return hip_fail(e, "event record");
   e = hipMemcpyAsync(slots, c->slot_idx, sizeof(int) * n, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "slot ids copy");
-  return experts_forward(dst, x, T, slots, gates, y, ws + w.experts, workspace_bytes - w.experts, stream);
+  char* xws = ws + w.experts;
+  float* y_s = nullptr;
+  if ((s = shared_phase(dst, x, T, xws, stream, &y_s)) != MD_OK) return s;
+  if (copy_stream && (e = hipStreamWaitEvent(stream, copy_done, 0)) != hipSuccess) return hip_fail(e, "event wait");
+  return routed_phase(dst, x, T, slots, gates, y_s, y, xws, stream);
 }
 
 md_status md_hbm_read_probe(const void* src, size_t nbytes, uint32_t key, uint32_t* sink, int32_t workgroups,

@@ -34,8 +34,8 @@ def device_moe(sp, device="cuda"):
 
 
 def host_moe(sp, device="cuda"):
-    """The layer with its expert set in pinned host memory (the router on the
-    GPU): the source of a host-memory expert tier."""
+    """The layer with its routed experts in pinned host memory (the router
+    and any shared expert on the GPU): the source of a host-memory tier."""
     stacks = {}
     for part in ("gate", "up", "down"):
         rows, cols = (sp.H, sp.F) if part == "down" else (sp.F, sp.H)
@@ -45,8 +45,13 @@ def host_moe(sp, device="cuda"):
             return m.data, m.scales
         stacks[part] = upload_stack_host(sp.fmt, rows, cols, sp.E, fetch, device)
     Wr, b = W.moe_router(sp)
+    shared = None
+    sh = W.moe_shared(sp)
+    if sh is not None:  # the shared expert stays resident on the GPU
+        shared = md.FFN(sp.act, upload_matrix(sh["gate"], device), upload_matrix(sh["up"], device),
+                        upload_matrix(sh["down"], device))
     return md.MoELayer(sp.H, sp.F, sp.E, sp.k, sp.act, stacks["gate"], stacks["up"], stacks["down"],
-                       torch.from_numpy(Wr).to(device), None if b is None else torch.from_numpy(b).to(device))
+                       torch.from_numpy(Wr).to(device), None if b is None else torch.from_numpy(b).to(device), shared)
 
 
 def device_dense(sp, name, device="cuda"):

@@ -68,10 +68,10 @@ def test_experts_forward_clamps_the_routing():
     assert torch.equal(y1, y2)
 
 
-def _tier(key, S):
+def _tier(key, S, overlap=True):
     import moe_decode_amd as md
     from synth.device import host_moe
-    return md.ExpertTier(host_moe(W.spec(key)), S)
+    return md.ExpertTier(host_moe(W.spec(key)), S, overlap=overlap)
 
 
 def _slots_hold_their_experts(tier):
@@ -141,3 +141,33 @@ def test_tier_decode_c4_int4():
         torch.cuda.synchronize()
         assert torch.equal(y, y2), i
     _slots_hold_their_experts(tier)
+
+
+@pytest.mark.parametrize("overlap", [True, False])
+def test_tier_with_shared_expert_c3(orc_mt, overlap):
+    """The 128-expert layer with its shared expert: misses load on a stream of
+    their own while the shared expert runs (or on the one stream); outputs
+    within the tolerance of the oracle, and the two orders bit-identical."""
+    import torch
+    from .gpu_common import assert_within, oracle_moe
+    say(f"[tier] c3 S=32 overlap={overlap}")
+    sp = W.spec("c3")
+    tier = _tier("c3", 32, overlap=overlap)
+    rng = np.random.default_rng([3, 903])
+    outs = []
+    for i, T in enumerate((1, 1, 2, 1, 3, 1)):
+        x = rng.standard_normal((T, sp.H)).astype(np.float32)
+        y = tier.forward(torch.from_numpy(x).cuda())
+        torch.cuda.synchronize()
+        y_ref, _, _, S = oracle_moe(orc_mt, sp, x)
+        assert_within(y.cpu().numpy(), y_ref, S, f"c3 tier step {i}")
+        outs.append(y.cpu().numpy())
+    assert tier.cache.misses > 0
+    _slots_hold_their_experts(tier)
+    _c3_outs.setdefault("runs", []).append(outs)
+    if len(_c3_outs["runs"]) == 2:
+        a, b = _c3_outs["runs"]
+        assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+_c3_outs = {}

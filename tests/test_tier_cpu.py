@@ -119,7 +119,11 @@ def test_fill_and_forward_argument_checks():
     assert sz.value > 0
     c = md.ExpertCache(8, 3)                                 # 3 slots, but dst has 4
     assert md.STATUS[L.md_moe_cached_forward(ctypes.byref(src), ctypes.byref(dst), ctypes.byref(c.state), FAKE, 1,
-                                             FAKE, None, None, FAKE, 1 << 30, None)] == "MD_ERR_SHAPE"
+                                             FAKE, None, None, FAKE, 1 << 30, None, None, None)] == "MD_ERR_SHAPE"
+    c4 = md.ExpertCache(8, 4)
+    assert md.STATUS[L.md_moe_cached_forward(ctypes.byref(src), ctypes.byref(dst), ctypes.byref(c4.state), FAKE, 1,
+                                             FAKE, None, None, FAKE, 1 << 30, None, FAKE, None)] == \
+        "MD_ERR_INVALID_ARG"                                # a copy stream without its event
     sh = _layer(4, has_shared=1)
     assert md.STATUS[L.md_moe_experts_forward(ctypes.byref(sh), FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)] in \
         ("MD_ERR_UNSUPPORTED", "MD_ERR_INVALID_ARG")
