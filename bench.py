@@ -478,10 +478,10 @@ def main():
         for key, Ts in (("c4_i8", (1, 4, 128)), ("c4_i2", (1, 4, 128)), ("c3", (1, 16, 128))):
             s2 = W.spec(key)
             l2 = device_moe(s2)
-            for T in Ts:
-                m = run_mode(l2, s2, T, max(10, args.steps // (4 if T > 1 else 1)), 5)
-                modes[f"{key}_T{T}"] = m
-                log(f"[bench] {key} T={T}: {m['ms_per_step'] * 1e3:.1f} us/step")
+            for Tx in Ts:
+                m = run_mode(l2, s2, Tx, max(10, args.steps // (4 if Tx > 1 else 1)), 5)
+                modes[f"{key}_T{Tx}"] = m
+                log(f"[bench] {key} T={Tx}: {m['ms_per_step'] * 1e3:.1f} us/step")
             del l2
             torch.cuda.empty_cache()
 

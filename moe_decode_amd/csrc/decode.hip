@@ -269,6 +269,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(FMT == I2_
   const int npairs = a.RGW * G * kNP;
   const int ngx = a.H / D::NV;
 
+  // The token's activation planes do not depend on the expert: their loads
+  // are in flight while wave 0 selects it (int4 layer 38.0 -> 36.2 us per
+  // token).  Not for packed int2, whose twelve planes held across the top-k
+  // made its step 1.5 us slower.
+  constexpr bool kPre = FMT != I2_ROW;
+  const int ngh = a.F / D::NV;
+  GuTile u{nullptr, nullptr, nullptr, nullptr, a.F, a.H, a.act, a.KS, a.RGW, a.xd + (int64_t)tok * ngx * D::NPL,
+           a.xsc + (int64_t)tok * ngx, a.hd + (int64_t)blockIdx.y * ngh * D::NPL, a.hsc + (int64_t)blockIdx.y * ngh};
+  ActDig<FMT, 1> xa;
+  if constexpr (kPre) gu_act<FMT, L>(u, xa);
+
   int e = a.idx_in ? a.idx_in[tok * a.k + slot] : 0;
   if (a.part) {
     if (wave == 0) {
@@ -290,18 +301,18 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(FMT == I2_
     e = s_sel[slot];
   }
 
-  const int ngh = a.F / D::NV;
-  GuTile u{a.gq + (int64_t)e * a.mat_bytes, a.uq + (int64_t)e * a.mat_bytes,
-           Fmt<FMT>::ROW ? a.gs + (int64_t)e * a.F : nullptr, Fmt<FMT>::ROW ? a.us + (int64_t)e * a.F : nullptr,
-           a.F, a.H, a.act, a.KS, a.RGW, a.xd + (int64_t)tok * ngx * D::NPL, a.xsc + (int64_t)tok * ngx,
-           a.hd + (int64_t)blockIdx.y * ngh * D::NPL, a.hsc + (int64_t)blockIdx.y * ngh};
+  u.Gm = a.gq + (int64_t)e * a.mat_bytes;
+  u.Um = a.uq + (int64_t)e * a.mat_bytes;
+  u.gs = Fmt<FMT>::ROW ? a.gs + (int64_t)e * a.F : nullptr;
+  u.us = Fmt<FMT>::ROW ? a.us + (int64_t)e * a.F : nullptr;
   if constexpr (kLoop) {
     // more row tiles than resident workgroups: each loops over its tiles of
     // this slot, so the top-k runs once per workgroup
     const int ntiles = (a.F + npairs - 1) / npairs;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) gu_tile<FMT, L, kNP>(u, tile * npairs, lds, ys);
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
+      gu_tile<FMT, L, kNP>(u, tile * npairs, lds, ys, kPre ? &xa : nullptr);
   } else {
-    gu_tile<FMT, L, kNP>(u, blockIdx.x * npairs, lds, ys);
+    gu_tile<FMT, L, kNP>(u, blockIdx.x * npairs, lds, ys, kPre ? &xa : nullptr);
   }
 }
 

@@ -293,8 +293,18 @@ struct GuTile {
   float* hsc;
 };
 
+// The activation planes a lane of gu_tile multiplies: chunk ks * L + t of the
+// token (expert-independent, so a caller may load them before it knows the
+// expert and pass them in as pre).
+template <int FMT, int L>
+MD_DEV void gu_act(const GuTile& a, ActDig<FMT, 1>& xa) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = wave % a.KS, t = lane % L;
+  if (wave / a.KS < a.RGW) load_act<FMT, L, 1>(xa, a.xd, a.xsc, ks * L + t);
+}
+
 template <int FMT, int L, int kNP, bool kCoh = false, int kWin = MD_GU_WINDOW>
-MD_DEV void gu_tile(const GuTile& a, int f0, float* lds, uint32_t* ys) {
+MD_DEV void gu_tile(const GuTile& a, int f0, float* lds, uint32_t* ys, const ActDig<FMT, 1>* pre = nullptr) {
   using D = Dig<FMT>;
   constexpr int G = 64 / L;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -315,7 +325,8 @@ MD_DEV void gu_tile(const GuTile& a, int f0, float* lds, uint32_t* ys) {
   if (rg < a.RGW) {
     const int c0 = ks * L + t;  // this lane's chunk (one chunk per lane per slice)
     ActDig<FMT, 1> xa;
-    load_act<FMT, L, 1>(xa, a.xd, a.xsc, c0);
+    if (pre) xa = *pre;
+    else load_act<FMT, L, 1>(xa, a.xd, a.xsc, c0);
     const int fb = f0 + (rg * G + g) * kNP;
     const int64_t rb = row_bytes(FMT, a.H);
     float pg[kNP], pu[kNP];
