@@ -388,13 +388,14 @@ MD_DEV void gu_tile(const GuTile& a, int f0, float* lds, uint32_t* ys, const Act
 // same launch.
 template <int FMT, int L, int CPL, int NRW, bool kCoh = false>
 MD_DEV void dn_rows(const uint8_t* Dm, const float* ds, int H, int F, const u32x4* hd, const float* hsc, int i0,
-                    float* out) {
+                    float* out, const ActDig<FMT, CPL>* pre = nullptr) {
   constexpr int G = 64 / L, NR = NRW / G;
   static_assert(NRW % G == 0 && NR <= L, "rows per wave");
   const int lane = threadIdx.x & 63;
   const int g = lane / L, t = lane % L;
   ActDig<FMT, CPL> ha;
-  load_act<FMT, L, CPL, kCoh>(ha, hd, hsc, t);
+  if (pre) ha = *pre;
+  else load_act<FMT, L, CPL, kCoh>(ha, hd, hsc, t);
   const int ib = i0 + g * NR;
   const int64_t rb = row_bytes(FMT, F);
   float part[NR];
