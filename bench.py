@@ -475,7 +475,8 @@ def main():
             m = run_dense(key, name, batch, max(20, args.steps), 10)
             modes[f"{key}_{name}_b{batch}"] = m
             log(f"[bench] {key} {name} batch {batch}: {m['ms_per_call'] * 1e3:.1f} us ({m['weight_GBps']:.0f} GB/s)")
-        for key, Ts in (("c4_i8", (1, 4, 128)), ("c4_i2", (1, 4, 128)), ("c3", (1, 16, 128))):
+        for key, Ts in (("c4_i8", (1, 4, 128)), ("c4_i2", (1, 4, 128)), ("c4_q41", (1, 4, 128)),
+                        ("c3", (1, 16, 128))):
             s2 = W.spec(key)
             l2 = device_moe(s2)
             for Tx in Ts:

@@ -98,9 +98,8 @@ typedef enum md_status {
  *   MD_I8_ROW, MD_I4_ROW, MD_I2_ROW: identical to the canonical layout.
  * Every row therefore starts a run of 16-byte quant chunks that a wavefront
  * streams with coalesced 16-byte loads, scales kept out of the way.
- * MD_Q4_1 and MD_I2_ROW are taken by md_row_bytes, md_prepare_layout and
- * md_qgemv (+ its workspace size); the FFN and MoE entry points return
- * MD_ERR_UNSUPPORTED for them. */
+ * Every type is taken by every entry point: md_qgemv, the FFN and MoE layers
+ * (one-token kernels, grouped GEMMs) and the expert tier. */
 typedef enum md_qtype {
   MD_Q8_0 = 1, MD_Q4_0 = 2, MD_I8_ROW = 3, MD_I4_ROW = 4, MD_Q4_1 = 5, MD_I2_ROW = 6
 } md_qtype;

@@ -38,8 +38,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_type(int32_t t) { return t >= MD_Q8_0 && t <= MD_I2_ROW; }
 bool row_type(int32_t t) { return t == MD_I8_ROW || t == MD_I4_ROW || t == MD_I2_ROW; }
-// the formats the FFN and MoE kernels take (Q4_1: md_qgemv only)
-bool layer_type(int32_t t) { return (t >= MD_Q8_0 && t <= MD_I4_ROW) || t == MD_I2_ROW; }
 
 constexpr int kMaxCols = 16384;
 constexpr int kMaxRows = 65536;
@@ -85,8 +83,6 @@ md_status check_ffn(const md_ffn* f, int32_t H) {
   if ((s = check_qmatrix("ffn.down", &f->down)) != MD_OK) return s;
   if (f->gate.type != f->up.type || f->gate.type != f->down.type)
     return fail(MD_ERR_UNSUPPORTED, "ffn: gate/up/down must share one type");
-  if (!layer_type(f->gate.type))
-    return fail(MD_ERR_UNSUPPORTED, "ffn: type %d runs in md_qgemv only", f->gate.type);
   const int F = f->gate.rows;
   if (f->gate.cols != H || f->up.cols != H || f->up.rows != F || f->down.rows != H || f->down.cols != F)
     return fail(MD_ERR_SHAPE, "ffn: gate/up must be F x H and down H x F (H=%d)", H);
@@ -214,7 +210,6 @@ md_status check_moe(const md_moe_layer* L, int32_t T) {
   if (L->E > kMaxE || L->k > kMaxK) return fail(MD_ERR_UNSUPPORTED, "E <= %d and k <= %d are supported", kMaxE, kMaxK);
   if (L->act != MD_ACT_GELU_TANH && L->act != MD_ACT_SILU) return fail(MD_ERR_INVALID_ARG, "unknown act %d", L->act);
   if (!valid_type(L->type)) return fail(MD_ERR_INVALID_ARG, "unknown expert type %d", L->type);
-  if (!layer_type(L->type)) return fail(MD_ERR_UNSUPPORTED, "expert type %d runs in md_qgemv only", L->type);
   if (!L->gate_q || !L->up_q || !L->down_q || !L->W_r) return fail(MD_ERR_INVALID_ARG, "null expert or router weights");
   if (!aligned16(L->gate_q) || !aligned16(L->up_q) || !aligned16(L->down_q) || !aligned16(L->W_r) ||
       (L->router_bias && !aligned16(L->router_bias)))

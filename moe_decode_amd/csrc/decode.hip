@@ -67,6 +67,7 @@ MD_DEV void dig_rows(const DigJob& j, uint32_t* ys, int b, int nb) {
     switch (j.fmt) {
       case Q8_0: dig_block<Q8_0>(v, n, ys, j.planes + g0 * Dig<Q8_0>::NPL, j.scales + g0); break;
       case Q4_0: dig_block<Q4_0>(v, n, ys, j.planes + g0 * Dig<Q4_0>::NPL, j.scales + g0); break;
+      case Q4_1: dig_block<Q4_1>(v, n, ys, j.planes + g0 * Dig<Q4_1>::NPL, j.scales + g0); break;
       case I8_ROW: dig_block<I8_ROW>(v, n, ys, j.planes + g0 * Dig<I8_ROW>::NPL, j.scales + g0); break;
       case I2_ROW: dig_block<I2_ROW>(v, n, ys, j.planes + g0 * Dig<I2_ROW>::NPL, j.scales + g0); break;
       default: dig_block<I4_ROW>(v, n, ys, j.planes + g0 * Dig<I4_ROW>::NPL, j.scales + g0); break;
@@ -570,7 +571,7 @@ hipError_t launch_gateup_t1(int fmt, const uint8_t* gq, const uint8_t* uq, const
 #define MD_GUL(F_) MD_GU(F_, 64, 8) MD_GU(F_, 32, 8) MD_GU(F_, 16, 8) MD_GU(F_, 8, 8) \
                    MD_GU(F_, 64, 4) MD_GU(F_, 32, 4) MD_GU(F_, 16, 4) MD_GU(F_, 8, 4) \
                    MD_GU(F_, 64, 2) MD_GU(F_, 32, 2) MD_GU(F_, 16, 2) MD_GU(F_, 8, 2)
-  MD_GUL(Q8_0) MD_GUL(Q4_0) MD_GUL(I8_ROW) MD_GUL(I4_ROW) MD_GUL(I2_ROW)
+  MD_GUL(Q8_0) MD_GUL(Q4_0) MD_GUL(I8_ROW) MD_GUL(I4_ROW) MD_GUL(I2_ROW) MD_GUL(Q4_1)
 #undef MD_GUL
 #undef MD_GU
   return hipErrorInvalidConfiguration;
@@ -589,7 +590,7 @@ hipError_t launch_down_t1(int fmt, const uint8_t* dq, const float* ds, int64_t m
     hipLaunchKernelGGL((k_down_t1<F_, L_, C_>), grid, block, 0, st, a); return hipGetLastError(); }
 #define MD_DNL(F_, L_) MD_DN(F_, L_, 1) MD_DN(F_, L_, 2) MD_DN(F_, L_, 3)
 #define MD_DNF(F_) MD_DNL(F_, 64) MD_DNL(F_, 32) MD_DNL(F_, 16) MD_DNL(F_, 8)
-  MD_DNF(Q8_0) MD_DNF(Q4_0) MD_DNF(I8_ROW) MD_DNF(I4_ROW) MD_DNF(I2_ROW)
+  MD_DNF(Q8_0) MD_DNF(Q4_0) MD_DNF(I8_ROW) MD_DNF(I4_ROW) MD_DNF(I2_ROW) MD_DNF(Q4_1)
 #undef MD_DNF
 #undef MD_DNL
 #undef MD_DN

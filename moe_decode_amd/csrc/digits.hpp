@@ -33,6 +33,9 @@ template <> struct Dig<Q4_0> {
   // word m, nibble i <- value: low nibble of byte b is weight 4m+b, high is 16+4m+b
   static constexpr int pos(int, int m, int i) { return (i & 1) ? 16 + 4 * m + (i >> 1) : 4 * m + (i >> 1); }
 };
+// Q4_1: the Q4_0 nibble order; its codes are unsigned, entered as n - 8 like
+// Q4_0's, with (8d + m) times the group's activation sum added per block.
+template <> struct Dig<Q4_1> : Dig<Q4_0> {};
 template <> struct Dig<I4_ROW> {
   static constexpr int NV = 32, NPL = 6, SB = 22, SH = 4, PER = 8;
   static constexpr uint32_t BIAS = 0x00888888u, FLIP = 0x88888888u;
@@ -156,7 +159,7 @@ MD_DEV float dig_chunk(u32x4 w, const u32x4* d, float sc, DigAcc<FMT>& r) {
     r.hi = (int)hi;
     return fmaf((float)dhi, sc * 16384.0f, (float)dlo * (sc * 0.25f));
   }
-  if constexpr (FMT == Q4_0) w ^= u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};  // n - 8
+  if constexpr (FMT == Q4_0 || FMT == Q4_1) w ^= u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};  // n - 8
 #pragma unroll
   for (int j = 0; j < D::NPL; ++j) {
 #pragma unroll
@@ -198,6 +201,33 @@ MD_DEV float dig_block_scale(const uint8_t* row, int K, int c) {
   } else {
     return 1.0f;
   }
+}
+
+// Q4_1: block c's scale d and minimum m, one 4-byte read.
+MD_DEV void dig_block_dm_q4_1(const uint8_t* row, int K, int c, float& d, float& m) {
+  const uint32_t dm = *reinterpret_cast<const uint32_t*>(row + (K / 32) * 16 + 4 * c);
+  d = h2f((uint16_t)(dm & 0xFFFFu));
+  m = h2f((uint16_t)(dm >> 16));
+}
+
+// Sum of a 4-bit group's values as the planes hold them, times sc: each
+// plane's digits summed by one dot against all-ones nibbles, then combined
+// in base 16 (|sum X| <= 32 * 2^22, exact in int32).
+template <int FMT>
+MD_DEV float dig_group_sum(const u32x4* d, float sc) {
+  static_assert(Dig<FMT>::SH == 4 && Dig<FMT>::NV == 32, "4-bit groups of 32");
+  int s[Dig<FMT>::NPL];
+#pragma unroll
+  for (int j = 0; j < Dig<FMT>::NPL; ++j) {
+    int a = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a = __builtin_amdgcn_sdot8((int)d[j][m], 0x11111111, a, false);
+    s[j] = a;
+  }
+  int X = s[Dig<FMT>::NPL - 1];
+#pragma unroll
+  for (int j = Dig<FMT>::NPL - 2; j >= 0; --j) X = 16 * X + s[j];
+  return (float)X * sc;
 }
 
 }  // namespace md

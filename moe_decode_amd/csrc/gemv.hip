@@ -398,6 +398,7 @@ hipError_t launch_gateup(int fmt, const GemvCfg& c, const uint8_t* gq, const uin
     case I8_ROW: return gateup_f<I8_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
     case I4_ROW: return gateup_f<I4_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
     case I2_ROW: return gateup_f<I2_ROW>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
+    case Q4_1: return gateup_f<Q4_1>(c, gq, uq, gs, us, mat_bytes, F, H, act, d, x, h, st);
   }
   return hipErrorInvalidValue;
 }
@@ -424,6 +425,7 @@ hipError_t launch_down(int fmt, const GemvCfg& c, const uint8_t* dq, const float
     case I8_ROW: return down_f<I8_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
     case I4_ROW: return down_f<I4_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
     case I2_ROW: return down_f<I2_ROW>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
+    case Q4_1: return down_f<Q4_1>(c, dq, ds, mat_bytes, H, F, d, h, o, st);
   }
   return hipErrorInvalidValue;
 }

@@ -244,8 +244,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
       if constexpr (TL::BLK) {
         if (tid < BR) {
           if constexpr (FMT == Q4_1) {
-            for (int h = 0; h < TL::SCW / 8; ++h)
-              *reinterpret_cast<u32x4*>(&s_sc[buf][tid * TL::SCW + 8 * h]) = rs[set][h];
+            // (d, m) pairs step-major, [step][row][2]: a lane's four rows of
+            // a step are one 16-byte read
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+              *reinterpret_cast<uint32_t*>(&s_sc[buf][2 * (s2 * BR + tid)]) = rs[set][s2 >> 2][s2 & 3];
           } else {
             // block scales step-major, [step][row]: the four consecutive rows
             // of a lane's MFMA outputs read their step's scales as one 8-byte load
@@ -302,12 +305,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
             z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, z, 0, 0, 0);
             if (has_lo) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, z, 0, 0, 0);
             if constexpr (FMT == Q4_1) {
+              const u32x4 dm = *reinterpret_cast<const u32x4*>(&s_sc[buf][2 * (s * BR + wr + 16 * rt + 4 * q)]);
 #pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int row = wr + 16 * rt + 4 * q + v;
-                acc[rt][v] = fmaf(h2f(s_sc[buf][row * 16 + 2 * s]), z[v],
-                                  fmaf(h2f(s_sc[buf][row * 16 + 2 * s + 1]), zs[v], acc[rt][v]));
-              }
+              for (int v = 0; v < 4; ++v)
+                acc[rt][v] = fmaf(h2f((uint16_t)(dm[v] & 0xFFFFu)), z[v],
+                                  fmaf(h2f((uint16_t)(dm[v] >> 16)), zs[v], acc[rt][v]));
             } else {
               const uint2 sc4 = *reinterpret_cast<const uint2*>(&s_sc[buf][s * BR + wr + 16 * rt + 4 * q]);
               const unsigned sw[2] = {sc4.x, sc4.y};
@@ -450,7 +452,7 @@ hipError_t launch_moe_mfma(int fmt, bool gateup, const uint8_t* wq, const uint8_
     if (gateup) hipLaunchKernelGGL((k_moe_mfma<F_, 1, RT_, true>), grid, dim3(256), 0, st, a); \
     else hipLaunchKernelGGL((k_moe_mfma<F_, 0, RT_, true>), grid, dim3(256), 0, st, a); \
     return hipGetLastError(); }
-  MD_MF(Q8_0, 1) MD_MF(Q4_0, 2)
+  MD_MF(Q8_0, 1) MD_MF(Q4_0, 2) MD_MF(Q4_1, 1)
 #undef MD_MF
   return hipErrorInvalidValue;
 }

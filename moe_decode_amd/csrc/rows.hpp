@@ -70,6 +70,7 @@ template <int FMT, int CPL>
 struct RowBuf {
   u32x4 w[CPL];
   float s[CPL];
+  float m[FMT == Q4_1 ? CPL : 1];  // Q4_1: 8d + m of each block
 };
 
 template <int FMT, int L, int CPL>
@@ -77,14 +78,25 @@ MD_DEV void load_row(RowBuf<FMT, CPL>& b, const uint8_t* row, int K, int c0) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i) b.w[i] = ld_stream(row + 16 * (int64_t)(c0 + L * i));
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) b.s[i] = dig_block_scale<FMT>(row, K, c0 + L * i);
+  for (int i = 0; i < CPL; ++i) {
+    if constexpr (FMT == Q4_1) {
+      float d, m;
+      dig_block_dm_q4_1(row, K, c0 + L * i, d, m);
+      b.s[i] = d;
+      b.m[i] = fmaf(8.0f, d, m);
+    } else {
+      b.s[i] = dig_block_scale<FMT>(row, K, c0 + L * i);
+    }
+  }
 }
 
-// Activation digit planes of the CPL chunks a lane owns.
+// Activation digit planes of the CPL chunks a lane owns (Q4_1: with each
+// group's activation sum).
 template <int FMT, int CPL>
 struct ActDig {
   u32x4 d[CPL][Dig<FMT>::NPL];
   float sc[CPL];
+  float xs[FMT == Q4_1 ? CPL : 1];
 };
 
 // kCoh: the planes were written by another workgroup of the same launch
@@ -109,6 +121,7 @@ MD_DEV void load_act(ActDig<FMT, CPL>& x, const u32x4* planes, const float* scal
       x.sc[i] = __hip_atomic_load(scales + c0 + L * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
       x.sc[i] = scales[c0 + L * i];
+    if constexpr (FMT == Q4_1) x.xs[i] = dig_group_sum<FMT>(x.d[i], x.sc[i]);
   }
 }
 
@@ -120,7 +133,10 @@ MD_DEV float row_dot(const RowBuf<FMT, CPL>& b, const ActDig<FMT, CPL>& x, DigAc
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const float v = kRun ? dig_chunk<FMT>(b.w[i], x.d[i], x.sc[i], r) : dig_chunk<FMT>(b.w[i], x.d[i], x.sc[i]);
-    acc = Fmt<FMT>::ROW ? acc + v : fmaf(b.s[i], v, acc);
+    if constexpr (FMT == Q4_1)  // d * sum (n - 8) X + (8d + m) * sum X
+      acc = fmaf(b.s[i], v, fmaf(b.m[i], x.xs[i], acc));
+    else
+      acc = Fmt<FMT>::ROW ? acc + v : fmaf(b.s[i], v, acc);
   }
   return acc;
 }

@@ -26,6 +26,8 @@ random, not trained):
 ``c4_i8``  the same layer with int8 per-row weights.
 ``c4_i2``  the same layer with packed int2 per-row weights (the colibri
            summary's third expert format); its own router seed (variant 2).
+``c4_q41`` the same layer with Q4_1 block experts (d ~ the Q4_0 range, block
+           minimum m = -d * U[6, 10]); its own router seed (variant 3).
 ``q41``    dense Q4_1 GEMVs at the ``c2`` shapes and activations (bf16), batch
            1 and 8; block minimum m = -d * U[6, 10] (rounded to fp16).
 ``i2``     dense packed-int2 per-row GEMVs at the ``c4`` expert shapes
@@ -130,6 +132,9 @@ SPECS: Dict[str, object] = {
     # the 256-expert layer once more with packed int2 per-row experts
     "c4_i2": MoESpec("c4_i2", 4, H=6144, F=2048, E=256, k=8, act="gelu_tanh", fmt="i2_row",
                      d_range=ROW_S, router_std=0.05, bias_std=None, tokens=(1, 4, 128), variant=2),
+    # and with Q4_1 block experts (23.6 MB per expert)
+    "c4_q41": MoESpec("c4_q41", 4, H=6144, F=2048, E=256, k=8, act="gelu_tanh", fmt="q4_1",
+                      d_range=Q4_D, router_std=0.05, bias_std=None, tokens=(1, 4, 128), variant=3),
     # the two further codecs, on dense GEMVs: Q4_1 at the Q4_0 workload's
     # shapes, packed int2 per-row at the 256-expert layer's expert shapes
     "q41": DenseSpec("q41", 5, "q4_1", Q4_D,

@@ -126,7 +126,6 @@ def test_moe_errors():
         (dict(down_q=FAKE_ODD), 1, "MD_ERR_ALIGNMENT"),
         (dict(type=md.I8_ROW), 1, "MD_ERR_INVALID_ARG"),
         (dict(has_shared=1), 1, "MD_ERR_INVALID_ARG"),
-        (dict(type=md.Q4_1), 1, "MD_ERR_UNSUPPORTED"),           # md_qgemv only
         (dict(type=md.I2_ROW), 1, "MD_ERR_INVALID_ARG"),          # per-row type without scales
         (dict(type=7), 1, "MD_ERR_INVALID_ARG"),
         ({}, 0, "MD_ERR_SHAPE"),
@@ -139,6 +138,9 @@ def test_moe_errors():
             want, (kw, T)
     i2 = _layer(type=md.I2_ROW, gate_scale=FAKE, up_scale=FAKE, down_scale=FAKE)   # packed int2 experts
     assert L.md_moe_workspace_size(ctypes.byref(i2), 4, ctypes.byref(sz)) == 0 and sz.value > 0
+    q41 = _layer(type=md.Q4_1)                                                      # Q4_1 experts
+    for T in (1, 9, 128):
+        assert L.md_moe_workspace_size(ctypes.byref(q41), T, ctypes.byref(sz)) == 0 and sz.value > 0
     d = _layer()
     assert _status(L.md_moe_layer_forward(ctypes.byref(d), FAKE, 1, FAKE, None, None, FAKE, 16, None)) == \
         "MD_ERR_WORKSPACE"
@@ -158,9 +160,15 @@ def test_ffn_and_layout_errors():
     assert _status(L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz))) == "MD_ERR_SHAPE"
     f.down = _qm(type_=md.Q4_0, rows=256, cols=512)
     assert _status(L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz))) == "MD_ERR_UNSUPPORTED"
-    f = md.FFNDesc(0, _qm(type_=md.Q4_1, rows=512, cols=256), _qm(type_=md.Q4_1, rows=512, cols=256),
-                   _qm(type_=md.Q4_1, rows=256, cols=512))
-    assert _status(L.md_ffn_workspace_size(ctypes.byref(f), 3, ctypes.byref(sz))) == "MD_ERR_UNSUPPORTED"
+    # Q4_1 takes the Q4_0 digit planes: the same workspace at every token count
+    for T in (1, 3, 9, 128):
+        ws = []
+        for t in (md.Q4_0, md.Q4_1):
+            f = md.FFNDesc(0, _qm(type_=t, rows=512, cols=256), _qm(type_=t, rows=512, cols=256),
+                           _qm(type_=t, rows=256, cols=512))
+            assert L.md_ffn_workspace_size(ctypes.byref(f), T, ctypes.byref(sz)) == 0
+            ws.append(sz.value)
+        assert ws[0] == ws[1] > 0, (T, ws)
     assert _status(L.md_prepare_layout(md.Q8_0, 4, 256, 1, FAKE, FAKE + 64, None)) == "MD_ERR_INVALID_ARG"
     assert _status(L.md_prepare_layout(md.Q8_0, 4, 256, 1, FAKE, FAKE_ODD, None)) == "MD_ERR_ALIGNMENT"
     assert _status(L.md_prepare_layout(md.Q8_0, 4, 100, 1, FAKE, FAKE + 4096, None)) == "MD_ERR_UNSUPPORTED"

@@ -102,7 +102,9 @@ def _moe_gpu(key, x):
                                    # 16 tokens, the large ones group by expert above 8
                                    ("c0", 16), ("c3", 12), ("c3", 16), ("c4_i4", 12),
                                    # packed int2 experts: one token, a batch, a verify batch
-                                   ("c4_i2", 1), ("c4_i2", 4), ("c4_i2", 12)])
+                                   ("c4_i2", 1), ("c4_i2", 4), ("c4_i2", 12),
+                                   # Q4_1 block experts
+                                   ("c4_q41", 1), ("c4_q41", 4), ("c4_q41", 12)])
 def test_moe_layer_matches_oracle(orc_mt, key, T):
     sp = W.spec(key)
     x = W.moe_x(sp, T)
@@ -115,7 +117,7 @@ def test_moe_layer_matches_oracle(orc_mt, key, T):
     say(f"[moe] {key} T={T} max err/S {ratio:.2e}")
 
 
-@pytest.mark.parametrize("key", ["c4_i4", "c4_i8", "c4_i2"])
+@pytest.mark.parametrize("key", ["c4_i4", "c4_i8", "c4_i2", "c4_q41"])
 def test_moe_prefill_chunk_sampled(orc_mt, key):
     """128-token chunk at full size: routing of every token checked, outputs
     of a sample of tokens checked (tokens are independent in the layer)."""
@@ -287,6 +289,13 @@ _RAGGED = {
     "i2_h16384": W.MoESpec("i2_h16384", 48, 16384, 512, 16, 4, "silu", "i2_row", (1e-3, 1e-2), 0.05, None, (1,)),
     "q8_e16_sh_i2": W.MoESpec("q8_e16_sh_i2", 49, 1536, 512, 16, 2, "gelu_tanh", "q8_0", (1e-3, 1e-2), 0.05, None,
                               (1,), shared_F=1536, shared_fmt="i2_row", shared_d_range=(1e-3, 1e-2)),
+    # Q4_1 experts (w = d n + m): a biased router with k = 3, a Q4_1 shared
+    # expert beside Q4_1 experts, and one beside Q8_0 experts
+    "q41_e40_k3": W.MoESpec("q41_e40_k3", 50, 1280, 768, 40, 3, "silu", "q4_1", (1e-3, 2e-2), 0.05, 0.5, (1,)),
+    "q41_e24_k2_sh": W.MoESpec("q41_e24_k2_sh", 51, 1536, 512, 24, 2, "gelu_tanh", "q4_1", (1e-3, 2e-2), 0.05,
+                               None, (1,), shared_F=768, shared_fmt="q4_1", shared_d_range=(1e-3, 2e-2)),
+    "q8_e16_sh_q41": W.MoESpec("q8_e16_sh_q41", 52, 1536, 512, 16, 2, "gelu_tanh", "q8_0", (1e-3, 1e-2), 0.05,
+                               None, (1,), shared_F=1536, shared_fmt="q4_1", shared_d_range=(1e-3, 2e-2)),
 }
 _ragged_layers = {}
 
@@ -312,3 +321,10 @@ def test_moe_ragged_shapes(orc_mt, name, T):
     assert np.max(np.abs(gates.cpu().numpy() - g_ref)) <= 1e-6
     ratio = assert_within(y.cpu().numpy(), y_ref, S, f"{name} T={T}")
     say(f"[moe ragged] {name} T={T} max err/S {ratio:.2e}")
+
+
+@pytest.mark.parametrize("name", ["q41_e40_k3", "q41_e24_k2_sh"])
+def test_moe_q4_1_chunk(orc_mt, name):
+    """A 128-token chunk of Q4_1 layers (grouped GEMMs over several 16-token
+    tiles per expert), against the oracle."""
+    test_moe_ragged_shapes(orc_mt, name, 128)
