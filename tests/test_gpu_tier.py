@@ -39,7 +39,8 @@ def _forward(layer, x):
     return y, idx, gates
 
 
-@pytest.mark.parametrize("key,T", [("c0", 1), ("c0", 3), ("c0", 33), ("c4_i4", 1), ("c4_i2", 4)])
+@pytest.mark.parametrize("key,T", [("c0", 1), ("c0", 3), ("c0", 33), ("c4_i4", 1), ("c4_i2", 4),
+                                   ("c4_q41", 1), ("c4_q41", 33)])
 def test_experts_forward_equals_layer(key, T):
     import moe_decode_amd as md
     import torch
