@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libmoe_decode.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["gemv.hip", "decode.hip", "fused.hip", "route.hip", "prefill.hip", "abi.cpp"]
+SOURCES = ["gemv.hip", "decode.hip", "route.hip", "prefill.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

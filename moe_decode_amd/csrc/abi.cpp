@@ -114,7 +114,6 @@ struct MoeWs {
   size_t x_dig, x_exp, h_dig, h_exp, hs_dig, hs_exp;  // int8 digit planes (per-row formats)
   size_t xs_dig, xs_exp;  // x digits in the shared expert's order
   size_t xd, sxd, hd, shd;  // digit planes of x and h for the one-token kernels (routed, shared formats)
-  size_t fo, fctr;          // fused kernel: per-pair down outputs, counters
   size_t rcopy;             // the residual's copy where y, which it may be, is written before it is added
 };
 
@@ -131,17 +130,6 @@ int pair_limit(const md_moe_layer* L) {
 bool use_pairs(const md_moe_layer* L, int T) {
   return T <= pair_limit(L) && md::t1_supported(L->type, L->H, L->F) &&
          (!L->has_shared || md::t1_supported(L->shared.gate.type, L->H, L->shared.gate.rows));
-}
-
-// Few tokens on shapes the fused persistent kernel covers, when MD_FUSED=1 is
-// set in the environment at call time (the separate one-token kernels are the
-// default: they are faster on the shapes measured so far).  The workspace
-// size does not depend on the choice.
-bool use_fused(const md_moe_layer* L, int T) {
-  const char* v = getenv("MD_FUSED");
-  if (!v || v[0] != '1' || T > 8) return false;
-  return md::fused_supported(L->type, L->H, L->F, L->has_shared ? L->shared.gate.type : 0,
-                             L->has_shared ? L->shared.gate.rows : 0, L->has_shared != 0);
 }
 
 MoeWs moe_ws(const md_moe_layer* L, int T) {
@@ -170,8 +158,6 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
       w.sxd = take(dig_buf_bytes(L->shared.gate.type, T, H));
       w.shd = take(dig_buf_bytes(L->shared.gate.type, T, L->shared.gate.rows));
     }
-    w.fo = take(sizeof(float) * (size_t)T * (k + 1) * H);
-    w.fctr = take(sizeof(int) * (size_t)md::fused_counter_words(T, k, H));
     w.rcopy = take(sizeof(float) * (size_t)T * H);
   } else {
     w.items = take(sizeof(int4) * (size_t)md::max_tiles(T, k, max_active(T, E, k)));
@@ -447,7 +433,7 @@ md_status md_moe_route_topk(const float* x, int32_t T, int32_t H, const float* W
   if ((s = check_ws(workspace, workspace_bytes, need)) != MD_OK) return s;
   const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(workspace);
-  hipError_t e = md::launch_router(x, T, H, W_r, E, rp, part, md::DigJob{}, md::DigJob{}, md::ZeroJob{}, stream);
+  hipError_t e = md::launch_router(x, T, H, W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   e = md::launch_select(part, rp, bias, T, E, k, logits, idx, gates, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "select launch");
@@ -566,7 +552,6 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       shd = dig_buf_at(ws + w.shd, sfmt, T, L->shared.gate.rows);
       js = dig_job(x, T, H, sfmt, sxd);
     }
-    const bool fused = use_fused(L, T);
     // the paths that add the residual in a launch of its own after y is
     // written keep a copy of it when it is y itself
     const float* res_late = residual;
@@ -577,67 +562,9 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       res_late = c;
       return true;
     };
-    md::ZeroJob zj{};
-    if (fused) zj = md::ZeroJob{static_cast<int*>(P(w.fctr)), md::fused_counter_words(T, k, H)};
     if (!mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
-    e = md::launch_router(x, T, H, L->W_r, E, rp, part, dig_job(x, T, H, fmt, xd), js, zj, stream);
+    e = md::launch_router(x, T, H, L->W_r, E, rp, part, dig_job(x, T, H, fmt, xd), js, stream);
     if (e != hipSuccess) return hip_fail(e, "router launch");
-    if (fused) {
-      // gate/up, down and the combine (and the shared expert) in one kernel
-      if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0) || !mark(MD_STAGE_SHARED, ev1) ||
-          !mark(MD_STAGE_SELECT, ev0) || !mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0))
-        return hip_fail(e, "event record");
-      md::FusedLaunch fl{};
-      fl.fmt = fmt;
-      fl.gq = static_cast<const uint8_t*>(L->gate_q);
-      fl.uq = static_cast<const uint8_t*>(L->up_q);
-      fl.dq = static_cast<const uint8_t*>(L->down_q);
-      fl.gs = row_type(fmt) ? L->gate_scale : nullptr;
-      fl.us = row_type(fmt) ? L->up_scale : nullptr;
-      fl.ds = row_type(fmt) ? L->down_scale : nullptr;
-      fl.gu_bytes = gu_bytes;
-      fl.dn_bytes = dn_bytes;
-      fl.F = F;
-      fl.act = L->act;
-      fl.xd = xd.planes;
-      fl.xsc = xd.scales;
-      fl.hd = hd.planes;
-      fl.hsc = hd.scales;
-      if (L->has_shared) {
-        const md_ffn& sf = L->shared;
-        fl.sfmt = sf.gate.type;
-        fl.sgq = static_cast<const uint8_t*>(sf.gate.q);
-        fl.suq = static_cast<const uint8_t*>(sf.up.q);
-        fl.sdq = static_cast<const uint8_t*>(sf.down.q);
-        fl.sgs = row_type(sf.gate.type) ? sf.gate.row_scale : nullptr;
-        fl.sus = row_type(sf.gate.type) ? sf.up.row_scale : nullptr;
-        fl.sds = row_type(sf.gate.type) ? sf.down.row_scale : nullptr;
-        fl.Fs = sf.gate.rows;
-        fl.sact = sf.act;
-        fl.sxd = sxd.planes;
-        fl.sxsc = sxd.scales;
-        fl.shd = shd.planes;
-        fl.shsc = shd.scales;
-      }
-      fl.H = H; fl.E = E; fl.k = k; fl.T = T;
-      fl.part = part; fl.S = rp.S; fl.bias = L->router_bias;
-      fl.o = static_cast<float*>(P(w.fo));
-      fl.y = y;
-      fl.idx_out = idx;
-      fl.gates_out = gates;
-      fl.ctr = static_cast<int*>(P(w.fctr));
-      if (residual && !keep_residual()) return hip_fail(hipGetLastError(), "residual copy");
-      e = md::launch_moe_fused(fl, stream);
-      if (e != hipSuccess) return hip_fail(e, "fused launch");
-      if (residual) {
-        e = md::launch_add(y, res_late, y, (int64_t)T * H, stream);
-        if (e != hipSuccess) return hip_fail(e, "residual launch");
-      }
-      if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0) || !mark(MD_STAGE_DOWN, ev1) ||
-          !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
-        return hip_fail(e, "event record");
-      return ok();
-    }
     if (L->has_shared && md::rs_supported(fmt, H, F, L->shared.gate.type, L->shared.gate.rows, k, T)) {
       // the shared expert inside the routed launches
       if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0) || !mark(MD_STAGE_SHARED, ev1) ||
@@ -739,7 +666,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
   const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(P(w.part));
-  e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, md::ZeroJob{}, stream);
+  e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");
 

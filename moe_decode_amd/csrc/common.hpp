@@ -8,9 +8,9 @@
 //   I8_ROW 16 int8 weights (scale per row)
 //   I4_ROW 32 two's-complement nibbles, low nibble of byte b = weight 2b
 //   Q4_1   one block: 32 unsigned nibbles in the Q4_0 order; scale d and
-//          minimum m of the block (w = d n + m; dense GEMV only)
+//          minimum m of the block (w = d n + m)
 //   I2_ROW 64 two's-complement bit pairs, bits 2i..2i+1 of byte b = weight
-//          4b+i (scale per row; dense GEMV only)
+//          4b+i (scale per row)
 // Decoding happens in VGPRs.  int8 goes through the sign-extending byte
 // convert.  A 4-bit code is made a two's-complement nibble (Q4_0: n XOR 8 is
 // n - 8) and moved into the high half of a byte with a 0xF0F0F0F0 mask, so each

@@ -131,19 +131,17 @@ MD_DEV double wave_sum_f64_dpp(double v) {
 // S partials in order, then the bias, and rounds once to fp32.  A lane's
 // W_r values (at most kRV float4) are loaded once, before any product, and
 // each token's activations likewise.  Workgroups past E*S run the digit jobs
-// and the zero job beside the router work.
+// beside the router work.
 constexpr int kRV = 8;
 __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr, int E, int S,
-                                                     double* __restrict__ part, DigJob j0, DigJob j1, ZeroJob z) {
+                                                     double* __restrict__ part, DigJob j0, DigJob j1) {
   __shared__ double red[4][4];
   __shared__ uint32_t ys[256];
   const int nr = E * S;
   if ((int)blockIdx.x >= nr) {
     // the activations' digit planes for the expert kernels (independent of the routing)
     const int b = blockIdx.x - nr, nb = gridDim.x - nr;
-    if (b == 0)
-      for (int i = threadIdx.x; i < z.n; i += blockDim.x) z.p[i] = 0;
     dig_rows(j0, ys, b, nb);
     dig_rows(j1, ys, b, nb);
     return;
@@ -220,10 +218,9 @@ int router_splits(int H, int E) {
 }
 
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
-                              const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st) {
-  int nd = dig_blocks(j0) > dig_blocks(j1) ? dig_blocks(j0) : dig_blocks(j1);
-  if (nd < 1 && z.n > 0) nd = 1;
-  hipLaunchKernelGGL(k_router_part, dim3(E * S + nd), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1, z);
+                              const DigJob& j0, const DigJob& j1, hipStream_t st) {
+  const int nd = dig_blocks(j0) > dig_blocks(j1) ? dig_blocks(j0) : dig_blocks(j1);
+  hipLaunchKernelGGL(k_router_part, dim3(E * S + nd), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1);
   return hipGetLastError();
 }
 

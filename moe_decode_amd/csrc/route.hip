@@ -121,9 +121,9 @@ RouterPlan router_plan(int T, int H, int E, bool pairs) {
 }
 
 hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, const RouterPlan& p, double* part,
-                         const DigJob& j0, const DigJob& j1, const ZeroJob& z, hipStream_t st) {
-  if (!p.gemm) return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, z, st);
-  if (j0.x || j1.x || z.n) return hipErrorInvalidValue;
+                         const DigJob& j0, const DigJob& j1, hipStream_t st) {
+  if (!p.gemm) return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, st);
+  if (j0.x || j1.x) return hipErrorInvalidValue;
   const dim3 grid((E + kRG - 1) / kRG, (T + kRG - 1) / kRG, p.S);
   hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, st, x, T, H, Wr, E, H / p.S, part);
   return hipGetLastError();

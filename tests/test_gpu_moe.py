@@ -175,22 +175,19 @@ def test_single_expert_gate_one_is_its_ffn():
 
 
 @pytest.mark.parametrize("key,T", [("c0", 1), ("c3", 1), ("c3", 8), ("c4_i4", 1), ("c4_i4", 4), ("c4_i8", 1)])
-def test_moe_fused_kernel_matches_oracle(orc_mt, key, T, monkeypatch):
-    """The few-token layer through the fused persistent kernel (switched on
-    with MD_FUSED=1) against the oracle, and against the separate kernels'
-    routing."""
+def test_moe_few_tokens_repeatable(orc_mt, key, T):
+    """The few-token layer against the oracle, called twice: the second call
+    (same buffers, same inputs) gives the same bits, indices and gates."""
     sp = W.spec(key)
     x = W.moe_x(sp, T)
-    say(f"[moe fused] {key} T={T}")
+    say(f"[moe repeat] {key} T={T}")
     y, idx, gates = _moe_gpu(key, x)
-    monkeypatch.setenv("MD_FUSED", "1")
-    yf, idf, gf = _moe_gpu(key, x)
+    y2, id2, g2 = _moe_gpu(key, x)
     y_ref, i_ref, g_ref, S = oracle_moe(orc_mt, sp, x)
-    assert np.array_equal(idx, i_ref) and np.array_equal(idf, i_ref)
-    assert np.array_equal(gates, gf)
+    assert np.array_equal(idx, i_ref) and np.array_equal(id2, i_ref)
+    assert np.array_equal(gates, g2) and np.array_equal(y, y2)
     assert np.max(np.abs(gates - g_ref)) <= 1e-6
-    assert_within(y, y_ref, S, f"{key} T={T} separate")
-    assert_within(yf, y_ref, S, f"{key} T={T} fused")
+    assert_within(y, y_ref, S, f"{key} T={T}")
 
 
 @pytest.mark.parametrize("key", ["c4_i4", "c4_i8", "c3"])

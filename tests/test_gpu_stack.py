@@ -143,14 +143,13 @@ def test_stack_graph_replays_match_eager(T):
     say(f"[stack] graph of {len(layers)} layers, T={T}: 4 replays equal the eager run")
 
 
-@pytest.mark.parametrize("key,T,fused", [("c0", 1, False), ("c0", 2, True), ("c3", 1, False), ("c3", 33, False),
-                                         ("c4_i4", 12, False), ("q4_sh", 3, False)])
-def test_residual_forward_equals_forward_then_add(key, T, fused, monkeypatch):
-    """y = residual + layer(x) from the fused entry point equals the layer
+@pytest.mark.parametrize("key,T", [("c0", 1), ("c0", 2), ("c3", 1), ("c3", 33), ("c4_i4", 12), ("q4_sh", 3)])
+def test_residual_forward_equals_forward_then_add(key, T):
+    """y = residual + layer(x) from the residual entry point equals the layer
     followed by md_add, bit for bit, on every path (one-token kernels without
-    and with a shared expert, the merged routed + shared launches, the fused
-    kernel, the grouped GEMMs with and without a shared expert), with the
-    residual a separate buffer and with the residual being y itself."""
+    and with a shared expert, the merged routed + shared launches, the grouped
+    GEMMs with and without a shared expert), with the residual a separate
+    buffer and with the residual being y itself."""
     import moe_decode_amd as md
     import torch
     from .gpu_common import moe_layer
@@ -162,8 +161,6 @@ def test_residual_forward_equals_forward_then_add(key, T, fused, monkeypatch):
     else:
         sp = W.spec(key)
         layer = moe_layer(key)
-    if fused:
-        monkeypatch.setenv("MD_FUSED", "1")
     x = torch.from_numpy(W.moe_x(sp, T)).cuda()
     r = torch.from_numpy(np.random.default_rng([7, T]).standard_normal((T, sp.H)).astype(np.float32)).cuda()
     y0 = md.moe_layer_forward(layer, x)
