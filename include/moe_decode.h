@@ -44,6 +44,40 @@
  * most 16384; rows 1..65536; E <= 256; 1 <= k <= 8; T <= 128 tokens per
  * layer call (longer prompts are split by the caller into chunks of at most
  * 128 tokens); batch <= 8 for md_qgemv.
+ *
+ * Accuracy contract.  Weights are decoded exactly (scale times code) and
+ * every contraction y = sum_c w_c x_c is accumulated in fp32 or exactly in
+ * integers; the router is accumulated in fp64 and rounded once.  The tolerance
+ * the source pages' problem statement sets is
+ *     |y - y_exact| <= 1e-4 * S + 1e-6,   S = sum_c |w_c x_c|,
+ * and per path the library guarantees:
+ *   - md_qgemv (every batch and format), and the FFN / MoE layers' chunks on
+ *     block formats (Q8_0, Q4_0, Q4_1: bf16 matrix cores on the exact codes
+ *     against activations split into two bf16 halves): the tolerance for
+ *     every finite input.
+ *   - FFN / MoE layers on the one-token kernels (up to 8 tokens, 16 on small
+ *     layers; every format): the activations a 16-byte weight chunk
+ *     multiplies -- a group g of 32 consecutive values for Q4_0 / Q4_1 /
+ *     packed int4, 16 for Q8_0 / int8, 64 for packed int2 -- are rounded to
+ *     integers of 2^-22 of the group's largest magnitude M_g before exact
+ *     integer dot products.  Per contraction (gate, up, down, shared expert)
+ *         |y - y_exact| <= 2^-22 * A + 2^-19 * S,
+ *         A = sum_g M_g * sum_{c in g} |w_c|,
+ *     which gives the tolerance whenever A <= 400 * S: a group's largest
+ *     activation may exceed the typical magnitude of the activations that
+ *     its weights multiply by up to about 400x.  Inputs outside that
+ *     precondition (a group holding a value ~1000x the others, with the
+ *     weights concentrated on the small ones) can exceed 1e-4 * S; the
+ *     seeded workloads sit at A / S <= 15.
+ *   - FFN / MoE layers' chunks on the per-row formats (int8, packed int4 /
+ *     int2 with one scale per row: int8 matrix cores): each activation row
+ *     (a token's x, a pair's h) is rounded to integers of 2^-30 of the row's
+ *     largest magnitude M; per contraction
+ *         |y - y_exact| <= 2^-30 * M * sum_c |w_c| + 2^-19 * S,
+ *     which gives the tolerance whenever M * sum_c |w_c| <= 1e5 * S (the
+ *     seeded workloads: <= 80).
+ *   A layer's output additionally carries the effect of its gate/up
+ *   contractions' error on h, as any fp32 evaluation does.
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H
