@@ -231,6 +231,25 @@ md_status md_moe_layer_forward(const md_moe_layer *L /*host*/, const float *x, i
                                int32_t *idx_out, float *gates_out,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* md_moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the scratch taken from a
+ * 64 MiB array built into the library instead of a caller's workspace.
+ * Every GPU the library runs on holds one such array from the library's
+ * first use on it until the process ends; its address is looked up once per
+ * device, on the first call with that device current.  This call allocates
+ * and frees nothing and calls no allocating routine.  All calls on one GPU
+ * share its array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller; the array keeps the
+ * last call's contents, and nothing in it needs to start cleared.
+ * Errors: as md_moe_layer_forward; a call whose scratch (the size
+ * md_moe_workspace_size reports) exceeds 64 MiB -> MD_ERR_UNSUPPORTED, with
+ * nothing enqueued (every layer and token count of the seeded workloads fits:
+ * the largest, 128 tokens of a 256-expert layer of hidden size 6144, needs
+ * about 62 MiB). */
+md_status md_moe_layer_forward_noalloc(const md_moe_layer *L /*host*/, const float *x, int32_t T, float *y,
+                                       int32_t *idx_out, float *gates_out, hipStream_t stream);
+
 /* Measurement variant of md_moe_layer_forward: identical work and results;
  * additionally records `start` on `stream` just before the launches of stage
  * `stage` and `stop` just after them (HIP events created by the caller), so

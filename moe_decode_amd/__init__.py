@@ -25,7 +25,8 @@ EXPORTS = ("md_abi_version", "md_status_string", "md_last_error_detail", "md_row
            "md_ffn_workspace_size", "md_ffn_forward", "md_moe_workspace_size", "md_moe_layer_forward",
            "md_moe_layer_forward_timed", "md_moe_layer_forward_residual", "md_add",
            "md_hbm_read_probe", "md_moe_experts_forward", "md_expert_cache_reset", "md_expert_cache_plan",
-           "md_expert_cache_fill", "md_moe_cached_workspace_size", "md_moe_cached_forward")
+           "md_expert_cache_fill", "md_moe_cached_workspace_size", "md_moe_cached_forward",
+           "md_moe_layer_forward_noalloc")
 STAGES = {"shared": 0, "router": 1, "select": 2, "gateup": 3, "down": 4, "combine": 5}
 
 
@@ -93,6 +94,7 @@ def lib():
             "md_expert_cache_fill": (i32, [vp, vp, vp, vp, i32, vp]),
             "md_moe_cached_workspace_size": (i32, [vp, vp, i32, psz]),
             "md_moe_cached_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp, vp, vp]),
+            "md_moe_layer_forward_noalloc": (i32, [vp, vp, i32, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -286,6 +288,15 @@ def moe_layer_forward(layer, x, y=None, idx=None, gates=None, workspace=None, st
     else:
         _check(lib().md_moe_layer_forward_residual(ctypes.byref(d), _ptr(x), T, _ptr(residual), _ptr(y), _ptr(idx),
                                                    _ptr(gates), _ptr(ws), wsb, _stream(stream)))
+    return y
+
+
+def moe_layer_forward_noalloc(layer, x, y, idx=None, gates=None, stream=None):
+    """y = layer(x) with the library's built-in scratch (no workspace; the
+    caller passes the output buffers).  Calls on one GPU must not overlap."""
+    d = layer.desc()
+    _check(lib().md_moe_layer_forward_noalloc(ctypes.byref(d), _ptr(x), x.shape[0], _ptr(y), _ptr(idx), _ptr(gates),
+                                              _stream(stream)))
     return y
 
 

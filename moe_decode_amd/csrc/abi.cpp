@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "moe_decode.h"
 #include "common.hpp"
@@ -852,6 +853,64 @@ static md_status experts_forward(const md_moe_layer* L, const float* x, int32_t 
 md_status md_moe_layer_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
                                float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+// ---- the layer forward that allocates nothing -------------------------------
+//
+// Scratch of md_moe_layer_forward_noalloc: an array in the library's code
+// object, so every GPU the library runs on holds one copy of it (at its own
+// address) until the process ends.  Host code reaches a device's copy only
+// through the address hipGetSymbolAddress returns on that device (the array's
+// name on the host is a stand-in, not a device address).  Nothing in it needs
+// to start at zero: every kernel of the layer writes what a later one reads.
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (looked up once per device,
+// with that device current).
+md_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MD_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MD_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MD_OK;
+}
+}  // namespace
+
+extern "C" {
+
+md_status md_moe_layer_forward_noalloc(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
+                                       float* gates_out, hipStream_t stream) {
+  md_status s = check_moe(L, T);
+  if (s != MD_OK) return s;
+  if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
+  if (!aligned16(x) || !aligned16(y) || (idx_out && !aligned16(idx_out)) || (gates_out && !aligned16(gates_out)))
+    return fail(MD_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  const size_t need = moe_ws(L, T).total;
+  if (need > kScratchBytes)
+    return fail(MD_ERR_UNSUPPORTED,
+                "this layer call needs %zu bytes of scratch, more than the %zu bytes built in "
+                "(md_moe_layer_forward takes a workspace of any size)", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != MD_OK) return s;
+  return moe_forward(L, x, T, y, idx_out, gates_out, ws, kScratchBytes, stream, -1, nullptr, nullptr);
 }
 
 md_status md_moe_layer_forward_timed(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,

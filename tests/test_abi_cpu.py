@@ -148,6 +148,28 @@ def test_moe_errors():
         "MD_ERR_ALIGNMENT"
 
 
+def test_noalloc_errors_before_any_device_call():
+    """The no-allocation layer call validates like md_moe_layer_forward and
+    refuses a call whose scratch would exceed its 64 MiB before it looks up
+    the device (so these return their codes without a GPU)."""
+    L = md.lib()
+    sz = ctypes.c_size_t(0)
+    for kw, T, want in [(dict(k=9), 1, "MD_ERR_SHAPE"), ({}, 129, "MD_ERR_UNSUPPORTED"),
+                        (dict(gate_q=None), 1, "MD_ERR_INVALID_ARG")]:
+        d = _layer(**kw)
+        assert _status(L.md_moe_layer_forward_noalloc(ctypes.byref(d), FAKE, T, FAKE, None, None, None)) == want
+    d = _layer()
+    assert _status(L.md_moe_layer_forward_noalloc(ctypes.byref(d), None, 1, FAKE, None, None, None)) == \
+        "MD_ERR_INVALID_ARG"
+    assert _status(L.md_moe_layer_forward_noalloc(ctypes.byref(d), FAKE, 1, FAKE_ODD, None, None, None)) == \
+        "MD_ERR_ALIGNMENT"
+    big = _layer(H=16384, F=16384, E=256, k=8)
+    assert L.md_moe_workspace_size(ctypes.byref(big), 128, ctypes.byref(sz)) == 0 and sz.value > 64 << 20
+    assert _status(L.md_moe_layer_forward_noalloc(ctypes.byref(big), FAKE, 128, FAKE, None, None, None)) == \
+        "MD_ERR_UNSUPPORTED"
+    assert b"64" in L.md_last_error_detail() or b"67108864" in L.md_last_error_detail()
+
+
 def test_ffn_and_layout_errors():
     L = md.lib()
     sz = ctypes.c_size_t(0)
