@@ -272,6 +272,21 @@ md_status md_moe_layer_forward_timed(const md_moe_layer *L /*host*/, const float
                                      void *workspace, size_t workspace_bytes, hipStream_t stream,
                                      int32_t stage, hipEvent_t start, hipEvent_t stop);
 
+/* Measurement aid: enqueues only the launches of stage `stage` (md_stage) of
+ * md_moe_layer_forward with the same arguments, which read the intermediate
+ * results that an earlier such call left in `workspace` (and in idx_out /
+ * gates_out); the stage's outputs are rewritten with the same values.
+ * Relaunching one stage back to back over several workspaces, each left by a
+ * different token's call, times that stage's kernels on their real inputs
+ * with nothing else in between (HIP events around the whole run give the
+ * kernels' average duration, without the dispatch latency that events around
+ * one launch add).  The workspace must hold what the earlier call with the
+ * same layer, x, T and outputs wrote, untouched since.  Errors: as
+ * md_moe_layer_forward; a stage outside 0..5 -> MD_ERR_INVALID_ARG. */
+md_status md_moe_layer_stage_relaunch(const md_moe_layer *L /*host*/, const float *x, int32_t T, float *y,
+                                      int32_t *idx_out, float *gates_out, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream, int32_t stage);
+
 /* md_moe_layer_forward with a residual: y = residual + layer(x), residual an
  * fp32 [T][H] device buffer (it may be x or y itself).  The residual is added
  * in the layer's last kernel (the down projection or the combine, after the

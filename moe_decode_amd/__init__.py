@@ -26,7 +26,7 @@ EXPORTS = ("md_abi_version", "md_status_string", "md_last_error_detail", "md_row
            "md_moe_layer_forward_timed", "md_moe_layer_forward_residual", "md_add",
            "md_hbm_read_probe", "md_moe_experts_forward", "md_expert_cache_reset", "md_expert_cache_plan",
            "md_expert_cache_fill", "md_moe_cached_workspace_size", "md_moe_cached_forward",
-           "md_moe_layer_forward_noalloc")
+           "md_moe_layer_forward_noalloc", "md_moe_layer_stage_relaunch")
 STAGES = {"shared": 0, "router": 1, "select": 2, "gateup": 3, "down": 4, "combine": 5}
 
 
@@ -95,6 +95,7 @@ def lib():
             "md_moe_cached_workspace_size": (i32, [vp, vp, i32, psz]),
             "md_moe_cached_forward": (i32, [vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp, vp, vp]),
             "md_moe_layer_forward_noalloc": (i32, [vp, vp, i32, vp, vp, vp, vp]),
+            "md_moe_layer_stage_relaunch": (i32, [vp, vp, i32, vp, vp, vp, vp, sz, vp, i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -289,6 +290,16 @@ def moe_layer_forward(layer, x, y=None, idx=None, gates=None, workspace=None, st
         _check(lib().md_moe_layer_forward_residual(ctypes.byref(d), _ptr(x), T, _ptr(residual), _ptr(y), _ptr(idx),
                                                    _ptr(gates), _ptr(ws), wsb, _stream(stream)))
     return y
+
+
+def moe_layer_stage_relaunch(layer, x, stage, y, workspace, idx=None, gates=None, stream=None):
+    """Re-enqueue one stage ("shared", "router", "select", "gateup", "down",
+    "combine") of an earlier moe_layer_forward made with the same x, y, idx,
+    gates and workspace (a measurement aid)."""
+    d = layer.desc()
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib().md_moe_layer_stage_relaunch(ctypes.byref(d), _ptr(x), x.shape[0], _ptr(y), _ptr(idx), _ptr(gates),
+                                             _ptr(workspace), wsb, _stream(stream), STAGES.get(stage, stage)))
 
 
 def moe_layer_forward_noalloc(layer, x, y, idx=None, gates=None, stream=None):

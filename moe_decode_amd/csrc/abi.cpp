@@ -506,7 +506,8 @@ md_status md_moe_workspace_size(const md_moe_layer* L, int32_t T, size_t* bytes)
 // residual: nullable [T][H], added to y (it may be y itself).
 static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
                              float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                             int32_t stage, hipEvent_t ev0, hipEvent_t ev1, const float* residual = nullptr) {
+                             int32_t stage, hipEvent_t ev0, hipEvent_t ev1, const float* residual = nullptr,
+                             int32_t only = -1) {
   md_status s = check_moe(L, T);
   if (s != MD_OK) return s;
   if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
@@ -529,6 +530,9 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     e = hipEventRecord(ev, stream);
     return e == hipSuccess;
   };
+  // only >= 0: enqueue the launches of that stage alone (they read what an
+  // earlier full call left in the workspace)
+  auto want = [&](int st) { return only < 0 || only == st; };
 
   const int64_t gu_bytes = (int64_t)F * md::row_bytes(fmt, H);
   const int64_t dn_bytes = (int64_t)H * md::row_bytes(fmt, F);
@@ -564,8 +568,10 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       return true;
     };
     if (!mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
-    e = md::launch_router(x, T, H, L->W_r, E, rp, part, dig_job(x, T, H, fmt, xd), js, stream);
-    if (e != hipSuccess) return hip_fail(e, "router launch");
+    if (want(MD_STAGE_ROUTER)) {
+      e = md::launch_router(x, T, H, L->W_r, E, rp, part, dig_job(x, T, H, fmt, xd), js, stream);
+      if (e != hipSuccess) return hip_fail(e, "router launch");
+    }
     if (L->has_shared && md::rs_supported(fmt, H, F, L->shared.gate.type, L->shared.gate.rows, k, T)) {
       // the shared expert inside the routed launches
       if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0) || !mark(MD_STAGE_SHARED, ev1) ||
@@ -595,33 +601,40 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       rl.Fs = sf.gate.rows; rl.sact = sf.act;
       rl.sxd = sxd.planes; rl.sxsc = sxd.scales; rl.shd = shd.planes; rl.shsc = shd.scales;
       rl.idx = idx; rl.gates = gates; rl.y = y; rl.residual = residual;
-      e = md::launch_moe_rs(rl, stream);
-      if (e != hipSuccess) return hip_fail(e, "routed+shared launch");
+      rl.parts = (want(MD_STAGE_GATEUP) ? 1 : 0) | (want(MD_STAGE_DOWN) ? 2 : 0);
+      if (rl.parts) {
+        e = md::launch_moe_rs(rl, stream);
+        if (e != hipSuccess) return hip_fail(e, "routed+shared launch");
+      }
       if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0) || !mark(MD_STAGE_DOWN, ev1) ||
           !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
         return hip_fail(e, "event record");
       return ok();
     }
     if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
-    if (L->has_shared) {
+    if (L->has_shared && want(MD_STAGE_SHARED)) {
       s = run_ffn(&L->shared, x, T, &sxd, sxd, shd, static_cast<float*>(P(w.h_s)), y_s, stream);
       if (s != MD_OK) return s;
     }
     if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_SELECT, ev0) || !mark(MD_STAGE_SELECT, ev1) ||
         !mark(MD_STAGE_GATEUP, ev0))
       return hip_fail(e, "event record");
-    e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
-                             L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, part, rp.S, L->router_bias,
-                             xd.planes, xd.scales, hd.planes, hd.scales, idx, gates, stream);
-    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (want(MD_STAGE_GATEUP)) {
+      e = md::launch_gateup_t1(fmt, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                               L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, E, k, T, part, rp.S,
+                               L->router_bias, xd.planes, xd.scales, hd.planes, hd.scales, idx, gates, stream);
+      if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    }
     if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
-    if (y_s && residual && !keep_residual()) return hip_fail(hipGetLastError(), "residual copy");
-    e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
-                           gates, hd.planes, hd.scales, y_s ? y_s : residual, y, stream);
-    if (e != hipSuccess) return hip_fail(e, "down launch");
-    if (y_s && residual) {  // the addend slot held the shared output
-      e = md::launch_add(y, res_late, y, (int64_t)T * H, stream);
-      if (e != hipSuccess) return hip_fail(e, "residual launch");
+    if (want(MD_STAGE_DOWN)) {
+      if (y_s && residual && !keep_residual()) return hip_fail(hipGetLastError(), "residual copy");
+      e = md::launch_down_t1(fmt, static_cast<const uint8_t*>(L->down_q), L->down_scale, dn_bytes, H, F, k, T, idx,
+                             gates, hd.planes, hd.scales, y_s ? y_s : residual, y, stream);
+      if (e != hipSuccess) return hip_fail(e, "down launch");
+      if (y_s && residual) {  // the addend slot held the shared output
+        e = md::launch_add(y, res_late, y, (int64_t)T * H, stream);
+        if (e != hipSuccess) return hip_fail(e, "residual launch");
+      }
     }
     if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0) || !mark(MD_STAGE_COMBINE, ev1))
       return hip_fail(e, "event record");
@@ -632,24 +645,30 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   ChunkAct xa{nullptr, nullptr, nullptr, nullptr};
   if (!mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
   {
-    // the activation forms the chunk path's kernels need
+    // the activation forms the chunk path's kernels need (enqueued with the
+    // shared expert's stage; pointers set up for every stage)
     const bool need_pair = !row_type(fmt) || (L->has_shared && !row_type(L->shared.gate.type));
     const bool need_dig = row_type(fmt);
     if (need_pair) {
-      e = md::launch_split_bf16(x, (int64_t)T * H, static_cast<u16*>(P(w.x_hi)), static_cast<u16*>(P(w.x_lo)), stream);
-      if (e != hipSuccess) return hip_fail(e, "split launch");
       xa.hi = static_cast<u16*>(P(w.x_hi));
       xa.lo = static_cast<u16*>(P(w.x_lo));
+      if (want(MD_STAGE_SHARED)) {
+        e = md::launch_split_bf16(x, (int64_t)T * H, static_cast<u16*>(P(w.x_hi)), static_cast<u16*>(P(w.x_lo)),
+                                  stream);
+        if (e != hipSuccess) return hip_fail(e, "split launch");
+      }
     }
     if (need_dig) {
-      e = md::launch_limbs(x, T, H, fmt, static_cast<int8_t*>(P(w.x_dig)), static_cast<int*>(P(w.x_exp)),
-                           stream);
-      if (e != hipSuccess) return hip_fail(e, "digit launch");
       xa.dig = static_cast<int8_t*>(P(w.x_dig));
       xa.expo = static_cast<int*>(P(w.x_exp));
+      if (want(MD_STAGE_SHARED)) {
+        e = md::launch_limbs(x, T, H, fmt, static_cast<int8_t*>(P(w.x_dig)), static_cast<int*>(P(w.x_exp)),
+                             stream);
+        if (e != hipSuccess) return hip_fail(e, "digit launch");
+      }
     }
   }
-  if (L->has_shared) {
+  if (L->has_shared && want(MD_STAGE_SHARED)) {
     ChunkAct xs = xa;
     const int sfmt = L->shared.gate.type;
     if (row_type(sfmt)) {  // x digits in the shared expert's own column order
@@ -667,8 +686,10 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
   const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(P(w.part));
-  e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
-  if (e != hipSuccess) return hip_fail(e, "router launch");
+  if (want(MD_STAGE_ROUTER)) {
+    e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+  }
   if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");
 
   // a chunk of tokens: group the (token, slot) pairs by expert, then one
@@ -677,10 +698,12 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   md::DispOut dout{static_cast<int*>(P(w.n_active)), static_cast<int*>(P(w.active_e)),
                    static_cast<int*>(P(w.active_off)), static_cast<int*>(P(w.pairs)), static_cast<int*>(P(w.pos)),
                    static_cast<int4*>(P(w.items)), n_items};
-  e = md::launch_select(part, rp, L->router_bias, T, E, k, logits, idx, gates, stream);
-  if (e != hipSuccess) return hip_fail(e, "select launch");
-  e = md::launch_dispatch(idx, T, E, k, dout, stream);
-  if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+  if (want(MD_STAGE_SELECT)) {
+    e = md::launch_select(part, rp, L->router_bias, T, E, k, logits, idx, gates, stream);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    e = md::launch_dispatch(idx, T, E, k, dout, stream);
+    if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+  }
   if (!mark(MD_STAGE_SELECT, ev1) || !mark(MD_STAGE_GATEUP, ev0)) return hip_fail(e, "event record");
 
   md::Disp d{dout.n_active, dout.active_e, dout.active_off, dout.pairs, k, T, dout.items};
@@ -689,31 +712,41 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   if (row_type(fmt)) {
     int8_t* h_dig = static_cast<int8_t*>(P(w.h_dig));
     int* h_exp = static_cast<int*>(P(w.h_exp));
-    e = md::launch_moe_mfma_i8(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
-                               L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, A, xa.dig, xa.expo, true, h,
-                               stream);
-    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (want(MD_STAGE_GATEUP)) {
+      e = md::launch_moe_mfma_i8(fmt, true, static_cast<const uint8_t*>(L->gate_q),
+                                 static_cast<const uint8_t*>(L->up_q), L->gate_scale, L->up_scale, gu_bytes, F, H,
+                                 L->act, d, A, xa.dig, xa.expo, true, h, stream);
+      if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    }
     if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
-    e = md::launch_limbs(h, T * k, F, fmt, h_dig, h_exp, stream);
-    if (e != hipSuccess) return hip_fail(e, "digit launch");
-    e = md::launch_moe_mfma_i8(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
-                               dn_bytes, H, F, L->act, d, A, h_dig, h_exp, false, o, stream);
-    if (e != hipSuccess) return hip_fail(e, "down launch");
+    if (want(MD_STAGE_DOWN)) {
+      e = md::launch_limbs(h, T * k, F, fmt, h_dig, h_exp, stream);
+      if (e != hipSuccess) return hip_fail(e, "digit launch");
+      e = md::launch_moe_mfma_i8(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
+                                 dn_bytes, H, F, L->act, d, A, h_dig, h_exp, false, o, stream);
+      if (e != hipSuccess) return hip_fail(e, "down launch");
+    }
   } else {
     u16* h_hi = static_cast<u16*>(P(w.h_hi));
     u16* h_lo = static_cast<u16*>(P(w.h_lo));
-    e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
-                            L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, A, xa.hi, xa.lo, true, h, h_hi,
-                            h_lo, stream);
-    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    if (want(MD_STAGE_GATEUP)) {
+      e = md::launch_moe_mfma(fmt, true, static_cast<const uint8_t*>(L->gate_q), static_cast<const uint8_t*>(L->up_q),
+                              L->gate_scale, L->up_scale, gu_bytes, F, H, L->act, d, A, xa.hi, xa.lo, true, h, h_hi,
+                              h_lo, stream);
+      if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+    }
     if (!mark(MD_STAGE_GATEUP, ev1) || !mark(MD_STAGE_DOWN, ev0)) return hip_fail(e, "event record");
-    e = md::launch_moe_mfma(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
-                            dn_bytes, H, F, L->act, d, A, h_hi, h_lo, false, o, nullptr, nullptr, stream);
-    if (e != hipSuccess) return hip_fail(e, "down launch");
+    if (want(MD_STAGE_DOWN)) {
+      e = md::launch_moe_mfma(fmt, false, static_cast<const uint8_t*>(L->down_q), nullptr, L->down_scale, nullptr,
+                              dn_bytes, H, F, L->act, d, A, h_hi, h_lo, false, o, nullptr, nullptr, stream);
+      if (e != hipSuccess) return hip_fail(e, "down launch");
+    }
   }
   if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0)) return hip_fail(e, "event record");
-  e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, residual, y, stream);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (want(MD_STAGE_COMBINE)) {
+    e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, residual, y, stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
   if (!mark(MD_STAGE_COMBINE, ev1)) return hip_fail(e, "event record");
   return ok();
 }
@@ -918,6 +951,14 @@ md_status md_moe_layer_forward_timed(const md_moe_layer* L, const float* x, int3
                                      int32_t stage, hipEvent_t start, hipEvent_t stop) {
   if (stage < 0) return fail(MD_ERR_INVALID_ARG, "stage %d", stage);
   return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, stage, start, stop);
+}
+
+md_status md_moe_layer_stage_relaunch(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
+                                      float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                      int32_t stage) {
+  if (stage < MD_STAGE_SHARED || stage > MD_STAGE_COMBINE) return fail(MD_ERR_INVALID_ARG, "stage %d", stage);
+  return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr,
+                     nullptr, stage);
 }
 
 md_status md_moe_layer_forward_residual(const md_moe_layer* L, const float* x, int32_t T, const float* residual,

@@ -635,16 +635,21 @@ hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st) {
   const int ks = g.r.KS > g.s.KS ? g.r.KS : g.s.KS;
   const size_t lds = sizeof(float) * (mx + (ks > 1 ? 2 * ks * mx : 0));
   const int nblk = L.T * L.k * rtiles + L.T * stiles;
-  hipLaunchKernelGGL((k_gateup_rs<Q4_0, 64, 8, Q8_0, 64, 8>), dim3(nblk), dim3(64 * g.r.KS * g.r.RGW), lds, st, a, sh,
-                     rtiles, L.T);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  DownT1 d{L.dq, L.ds, L.dn_bytes, L.H, L.F, L.k, L.idx, L.gates, static_cast<const u32x4*>(L.hd), L.hsc, L.residual,
-           L.y};
-  SharedDN sd{L.sdq, L.sds, L.Fs, static_cast<const u32x4*>(L.shd), L.shsc};
-  hipLaunchKernelGGL((k_down_rs<Q4_0, 8, 3, Q8_0, 64, 2>), dim3((L.H + kNRW - 1) / kNRW, L.T), dim3(64 * (L.k + 1)), 0,
-                     st, d, sd);
-  return hipGetLastError();
+  if (L.parts & 1) {
+    hipLaunchKernelGGL((k_gateup_rs<Q4_0, 64, 8, Q8_0, 64, 8>), dim3(nblk), dim3(64 * g.r.KS * g.r.RGW), lds, st, a,
+                       sh, rtiles, L.T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (L.parts & 2) {
+    DownT1 d{L.dq, L.ds, L.dn_bytes, L.H, L.F, L.k, L.idx, L.gates, static_cast<const u32x4*>(L.hd), L.hsc,
+             L.residual, L.y};
+    SharedDN sd{L.sdq, L.sds, L.Fs, static_cast<const u32x4*>(L.shd), L.shsc};
+    hipLaunchKernelGGL((k_down_rs<Q4_0, 8, 3, Q8_0, 64, 2>), dim3((L.H + kNRW - 1) / kNRW, L.T), dim3(64 * (L.k + 1)),
+                       0, st, d, sd);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace md

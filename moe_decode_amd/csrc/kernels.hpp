@@ -144,6 +144,7 @@ struct RsLaunch {
   float* gates;
   float* y;
   const float* residual;                    // added to y, or nullptr
+  int parts = 3;                            // 1: the gate/up launch, 2: the down launch, 3: both
 };
 bool rs_supported(int fmt, int H, int F, int sfmt, int Fs, int k, int T);
 hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st);

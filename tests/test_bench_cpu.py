@@ -46,3 +46,31 @@ def test_traffic_follows_the_source_hash(tmp_path, monkeypatch):
 def test_committed_summary_names_a_hash_and_a_figure():
     text = open(os.path.join(ROOT, "profiles", "k_gateup_t1_c4_i4_T1_pmc.md")).read()
     assert "traffic_bytes_per_launch:" in text and "source_sha256:" in text
+
+
+def test_mfma_stats_by_hand():
+    """Every token of a 128-token chunk chooses experts 0..7: 8 experts of
+    128 tokens = 64 tiles of 16; useful ops 2 * (2F * H) per (token, slot)
+    pair; issued = 16 positions * 64 tiles * 4 digit passes = 4x useful."""
+    import numpy as np
+    from synth import workloads as W
+    sp = W.spec("c4_i4")
+    idx = np.tile(np.arange(8, dtype=np.int32), (128, 1))[None]
+    st = bench.mfma_stats(sp, idx, 1.0, "int8")
+    useful = 2.0 * 2 * 2048 * 6144 * 1024
+    assert st["tiles_per_call"] == 64
+    assert abs(st["useful_TOPS"] - useful / 1e-3 / 1e12) < 1e-9
+    assert abs(st["issued_TOPS"] / st["useful_TOPS"] - 4.0) < 1e-12
+    assert st["peak_TOPS"] == 5000.0
+    b = bench.mfma_stats(sp, idx, 1.0, "bf16")
+    assert abs(b["issued_TOPS"] / b["useful_TOPS"] - 2.0) < 1e-12 and b["peak_TOPS"] == 2500.0
+    # one token per expert: a tile of 16 for each pair, 16x the useful work per pass
+    idx1 = np.arange(128 * 8, dtype=np.int32).reshape(1, 128, 8) % 256
+    s1 = bench.mfma_stats(sp, idx1, 1.0, "int8")
+    assert s1["tiles_per_call"] == 256
+
+
+def test_records_are_plain():
+    h = bench.host_record()
+    assert h["logical_cpus"] == os.cpu_count()
+    assert bench.source_hash() == bench.source_hash() and len(bench.source_hash()) == 64
