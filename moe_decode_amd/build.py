@@ -1,6 +1,8 @@
 """Build libmoe_decode.so in-tree with hipcc for gfx950.
 
-    python -m moe_decode_amd.build
+    python -m moe_decode_amd.build              # the library
+    python -m moe_decode_amd.build --sanitize   # libmoe_decode_san.so: host code
+                                                # with ASan + UBSan (CPU tests only)
 """
 import os
 import subprocess
@@ -11,7 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libmoe_decode.so")
+OUT_SAN = os.path.join(HERE, "libmoe_decode_san.so")
 BUILD = os.path.join(HERE, "_build")
+BUILD_SAN = os.path.join(HERE, "_build_san")
 
 SOURCES = ["gemv.hip", "decode.hip", "route.hip", "prefill.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,12 +27,17 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-pass-failed",
     "-I", os.path.join(ROOT, "include"),
 ]
+# host-side sanitizers only (the device code is built as usual)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+SAN_LINK = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"]
 
 
-def _compile(src, build_dir=BUILD, defines=()):
+def _compile(src, build_dir=BUILD, defines=(), extra=()):
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + FLAGS + [f"-D{d}" for d in defines] + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + list(extra) + [f"-D{d}" for d in defines] + lang + ["-c", os.path.join(CSRC, src), "-o",
+                                                                               obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -36,20 +45,25 @@ def _compile(src, build_dir=BUILD, defines=()):
     return obj, warn
 
 
-def build(verbose=False, out=OUT, build_dir=BUILD, defines=()):
+def build(verbose=False, out=None, build_dir=None, defines=(), sanitize=False):
     """Compile every source and link the shared library (out); `defines` are
-    extra -D settings of the kernels' compile-time parameters."""
+    extra -D settings of the kernels' compile-time parameters; sanitize: host
+    code with AddressSanitizer + UndefinedBehaviorSanitizer (a process that
+    loads it must preload the clang ASan runtime)."""
+    out = out or (OUT_SAN if sanitize else OUT)
+    build_dir = build_dir or (BUILD_SAN if sanitize else BUILD)
+    extra = SAN_FLAGS if sanitize else []
     os.makedirs(build_dir, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+        results = list(ex.map(lambda s: _compile(s, build_dir, defines, extra), srcs))
     objs = [o for o, _ in results]
     if verbose:
         for (_, w), s in zip(results, srcs):
             if w:
                 print(f"--- {s}\n{w}")
     tmp = out + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + (SAN_LINK if sanitize else []) + ["-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
@@ -58,4 +72,4 @@ def build(verbose=False, out=OUT, build_dir=BUILD, defines=()):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -14,8 +14,12 @@ import subprocess
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB = os.path.join(HERE, "liboracle.so")
+# MD_SANITIZE=1: the AddressSanitizer + UndefinedBehaviorSanitizer build
+# (build(sanitize=True); the process must preload the clang ASan runtime)
+SANITIZE = os.environ.get("MD_SANITIZE") == "1"
+LIB = os.path.join(HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 SRC = os.path.join(HERE, "oracle.c")
+CLANG = "/opt/rocm/llvm/bin/clang"
 
 FMT = {"q8_0": 1, "q4_0": 2, "i8_row": 3, "i4_row": 4, "q4_1": 5, "i2_row": 6}
 ACT = {"gelu_tanh": 0, "silu": 1}
@@ -23,16 +27,24 @@ XT = {"f32": 0, "bf16": 1}
 ERR = {0: "ok", 1: "invalid argument", 2: "non-finite logit", 3: "selected expert not supplied"}
 
 
-def build(force=True):
-    """Compile the oracle with gcc: plain C, no fast-math, no FMA contraction."""
-    if not force and os.path.exists(LIB):
-        return LIB
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-o", tmp, SRC, "-lm"]
+def build(force=True, sanitize=False):
+    """Compile the oracle with gcc: plain C, no fast-math, no FMA contraction.
+    sanitize: a single-threaded AddressSanitizer + UndefinedBehaviorSanitizer
+    build with clang (liboracle_san.so; any undefined behaviour aborts)."""
+    lib = os.path.join(HERE, "liboracle_san.so" if sanitize else "liboracle.so")
+    if not force and os.path.exists(lib):
+        return lib
+    tmp = lib + ".tmp"
+    if sanitize:
+        cmd = [CLANG, "-O1", "-g", "-std=gnu11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+               "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-shared-libsan", "-Wall", "-Wno-unknown-pragmas", "-o", tmp, SRC, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-o", tmp, SRC, "-lm"]
     subprocess.run(cmd, check=True, cwd=HERE)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 class _QMat(ctypes.Structure):

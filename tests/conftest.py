@@ -9,6 +9,12 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    # MD_SANITIZE=1: the CPU tests against the sanitizer builds of the oracle
+    # and of the library's host code (oracle.build(sanitize=True),
+    # python -m moe_decode_amd.build --sanitize; the clang ASan runtime preloaded)
+    if os.environ.get("MD_SANITIZE") == "1":
+        import moe_decode_amd as md
+        md.LIBPATH = os.path.join(ROOT, "moe_decode_amd", "libmoe_decode_san.so")
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: large CPU work (full-size oracle runs)")
 
