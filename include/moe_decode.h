@@ -381,10 +381,15 @@ md_status md_expert_cache_fill(const md_moe_layer *src /*host*/, const md_moe_la
  * stream.  idx_out / gates_out (device, nullable) receive the expert ids and
  * gates.  c->slot_idx must hold T*k entries and stay untouched until the
  * next call on the stream (an asynchronous copy reads it).  Workspace:
- * md_moe_cached_workspace_size.  Errors: as md_moe_layer_forward,
- * md_expert_cache_plan and md_expert_cache_fill; a cache whose E / S differ
- * from src->E / dst->E -> MD_ERR_SHAPE; a copy_stream without an event ->
- * MD_ERR_INVALID_ARG. */
+ * md_moe_cached_workspace_size.  A cache (and its slots) must be used from
+ * one compute stream: the call's one synchronisation orders the copies into
+ * the slots after the previous calls' reads of them only on that stream.
+ * Errors: as md_moe_layer_forward, md_expert_cache_plan and
+ * md_expert_cache_fill; a cache whose E / S differ from src->E / dst->E ->
+ * MD_ERR_SHAPE; a copy_stream without an event -> MD_ERR_INVALID_ARG.  An
+ * error after the plan (a copy or a launch that fails) marks the slots the
+ * plan gave to missed experts empty, so their contents are never taken for
+ * those experts (nor for the experts they held before). */
 md_status md_moe_cached_workspace_size(const md_moe_layer *src /*host*/, const md_moe_layer *dst /*host*/, int32_t T,
                                        size_t *bytes /*host*/);
 md_status md_moe_cached_forward(const md_moe_layer *src /*host*/, const md_moe_layer *dst /*host*/,

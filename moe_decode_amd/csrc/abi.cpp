@@ -1170,15 +1170,31 @@ md_status md_moe_cached_forward(const md_moe_layer* src, const md_moe_layer* dst
   if ((s = md_expert_cache_plan(c, host_idx, n, c->slot_idx, miss_e, miss_s, &nm)) != MD_OK) return s;
   // the misses load on the copy stream while the shared expert (resident)
   // runs on the compute stream; the routed experts wait for both
-  if ((s = md_expert_cache_fill(src, dst, miss_e, miss_s, nm, copy_stream ? copy_stream : stream)) != MD_OK) return s;
-  if (copy_stream && (e = hipEventRecord(copy_done, copy_stream)) != hipSuccess) return hip_fail(e, "event record");
-  e = hipMemcpyAsync(slots, c->slot_idx, sizeof(int) * n, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "slot ids copy");
-  char* xws = ws + w.experts;
-  float* y_s = nullptr;
-  if ((s = shared_phase(dst, x, T, xws, stream, &y_s)) != MD_OK) return s;
-  if (copy_stream && (e = hipStreamWaitEvent(stream, copy_done, 0)) != hipSuccess) return hip_fail(e, "event wait");
-  return routed_phase(dst, x, T, slots, gates, y_s, y, xws, stream);
+  auto rest = [&]() -> md_status {
+    md_status r = md_expert_cache_fill(src, dst, miss_e, miss_s, nm, copy_stream ? copy_stream : stream);
+    if (r != MD_OK) return r;
+    if (copy_stream && (e = hipEventRecord(copy_done, copy_stream)) != hipSuccess) return hip_fail(e, "event record");
+    e = hipMemcpyAsync(slots, c->slot_idx, sizeof(int) * n, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "slot ids copy");
+    char* xws = ws + w.experts;
+    float* y_s = nullptr;
+    if ((r = shared_phase(dst, x, T, xws, stream, &y_s)) != MD_OK) return r;
+    if (copy_stream && (e = hipStreamWaitEvent(stream, copy_done, 0)) != hipSuccess) return hip_fail(e, "event wait");
+    return routed_phase(dst, x, T, slots, gates, y_s, y, xws, stream);
+  };
+  s = rest();
+  if (s != MD_OK) {
+    // the plan already gave the missed experts their slots, whose copies may
+    // not have run or may have run in part: the slots are marked empty, so
+    // no later call takes what they hold for a resident expert
+    for (int i = 0; i < nm; ++i) {
+      c->slot_of_expert[miss_e[i]] = -1;
+      c->expert_in_slot[miss_s[i]] = -1;
+      c->uses[miss_s[i]] = 0;
+      c->last_use[miss_s[i]] = 0;
+    }
+  }
+  return s;
 }
 
 md_status md_hbm_read_probe(const void* src, size_t nbytes, uint32_t key, uint32_t* sink, int32_t workgroups,
