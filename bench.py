@@ -179,8 +179,8 @@ def kernel_time(layers, sp, T, stage, n_inputs, reps=3):
     """Average duration of one stage's kernels on real inputs: n_inputs
     forwards (each on its own seeded input, layer copy i mod len(layers) and
     workspace) leave their intermediate results behind; then the stage alone
-    is relaunched over all of them back to back, `reps` times, between two HIP
-    events on the kernels' stream.  Consecutive launches work on different
+    is relaunched over all of them back to back (captured in a HIP graph,
+    replayed `reps` times between two HIP events on the kernels' stream).  Consecutive launches work on different
     tokens (different experts), so their weight bytes come from HBM."""
     import numpy as np
     import torch
@@ -204,13 +204,25 @@ def kernel_time(layers, sp, T, stage, n_inputs, reps=3):
 
     run()
     torch.cuda.synchronize()
+    # the relaunches captured in one HIP graph: a kernel shorter than the
+    # host's time per call would otherwise wait for its own submission
+    g = torch.cuda.CUDAGraph()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            run()
+    torch.cuda.current_stream().wait_stream(s_)
+    g.replay()
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(reps):
-        run()
+        g.replay()
     t1.record()
     torch.cuda.synchronize()
+    del g
     ms = t0.elapsed_time(t1) / (reps * n_inputs)
     idx_np = idx.cpu().numpy()
     del wss
@@ -473,6 +485,56 @@ def hbm_probe(nbytes=4 << 30, reps=5):
     return {"bytes": nbytes, "reps": reps, "GBps": best["GBps"], "workgroups": best["workgroups"], "sweep": sweep}
 
 
+def chain_floor(sizes, reps=16, pool_bytes=4 << 30):
+    """Time of a chain of plain streaming reads of the given byte counts, back
+    to back (the library's read probe; each read from a fresh region of a
+    4 GiB buffer of random bytes, so nothing comes from the caches), captured
+    in a HIP graph and replayed: what a chain of kernels that each stream
+    those bytes takes at this GPU's attainable read rate, launch gaps
+    included, when nothing overlaps."""
+    import torch
+    import moe_decode_amd as md
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    src = torch.randint(0, 256, (pool_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    per_chain = sum((n + 255) // 256 * 256 for n in sizes)
+    chains = max(1, pool_bytes // per_chain)
+
+    def run():
+        off = 0
+        for c in range(reps):
+            if (c % chains) == 0:
+                off = 0
+            for n in sizes:
+                n16 = (n + 15) // 16 * 16
+                md.hbm_read_probe(src[off:off + n16], sink, workgroups=max(64, min(8192, n16 // 32768 + 1)))
+                off += (n16 + 255) // 256 * 256
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            run()
+    torch.cuda.current_stream().wait_stream(s_)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del g, src
+    torch.cuda.empty_cache()
+    return {"bytes": list(sizes), "us_per_chain": ms * 1e3, "GBps": sum(sizes) / (ms / 1e3) / 1e9,
+            "timing": f"{reps} chains of back-to-back read-probe launches in one HIP graph"}
+
+
 def environment():
     import torch
     pr = torch.cuda.get_device_properties(0)
@@ -620,7 +682,7 @@ def decode_roofline(layers, sp, T, r):
         "traffic": traffic_record(kernel, f"{sp.key}_T{T}"),
         "bytes_per_launch": gb, "avg_launch_ms": kt["ms_per_launch"],
         "timing": f"{kt['launches']} back-to-back relaunches of the stage over {kt['inputs']} tokens' workspaces "
-                  f"between two HIP events",
+                  f"(HIP graph replays) between two HIP events",
         "event_launch_ms": r["stage_ms_avg"],
         "event_launch_GBps": r["stage_GBps"],
         "down_avg_launch_ms": kd["ms_per_launch"],
@@ -657,7 +719,7 @@ def prefill_leg(layers, sp, steps, warmup, cpu, sample_tokens, T=128):
             "traffic": traffic_record(kernel, f"{sp.key}_T{T}"),
             "bytes_per_launch": gb, "avg_launch_ms": kt["ms_per_launch"],
             "timing": f"{kt['launches']} back-to-back relaunches of the stage over {kt['inputs']} chunks' "
-                      f"workspaces between two HIP events",
+                      f"workspaces (HIP graph replays) between two HIP events",
             "event_launch_ms": r["stage_ms_avg"],
             "mfma": mfma_stats(sp, kt["idx"], kt["ms_per_launch"], dtype),
         },
@@ -788,6 +850,13 @@ def main():
     if roof:
         roof["hbm_read_probe_GBps"] = probe["GBps"]
         roof["frac_of_probe"] = roof["achieved"] / probe["GBps"]
+        # the layer's three launches (router, gate/up, down) as plain reads of their weight bytes
+        gu = roof["bytes_per_launch"]
+        floor = chain_floor([sp.router_bytes(), int(gu), int(r["weight_bytes_per_step"] - gu - sp.router_bytes())])
+        roof["chain_floor"] = floor
+        roof["step_over_chain_floor"] = r["ms_per_step"] * 1e3 / floor["us_per_chain"]
+        log(f"[bench] chain of plain reads of the same bytes: {floor['us_per_chain']:.1f} us "
+            f"(step {r['ms_per_step'] * 1e3:.1f} us)")
     smi_after = smi_snapshot()
 
     inputs[f"{sp.key}_x_T{T}"] = r["inputs_sha256"]

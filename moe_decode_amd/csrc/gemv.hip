@@ -319,11 +319,26 @@ __global__ __launch_bounds__(kBlock) void k_combine(const float* __restrict__ o,
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= (int64_t)T * H4) return;
   const int t = (int)(i / H4), c = (int)(i % H4);
+  // the positions and gates of the token's k <= 8 slots first, then all their
+  // rows' loads in flight together, summed in slot order
+  int pj[8];
+  float gj[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pj[j] = j < k ? pos_of_pair[t * k + j] : 0;
+    gj[j] = j < k ? gates[t * k + j] : 0.f;
+  }
+  float4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v[j] = j < k ? reinterpret_cast<const float4*>(o + (int64_t)pj[j] * H)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const float gj = gates[t * k + j];
-    const float4 v = reinterpret_cast<const float4*>(o + (int64_t)pos_of_pair[t * k + j] * H)[c];
-    a.x = fmaf(gj, v.x, a.x); a.y = fmaf(gj, v.y, a.y); a.z = fmaf(gj, v.z, a.z); a.w = fmaf(gj, v.w, a.w);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k) {
+      a.x = fmaf(gj[j], v[j].x, a.x); a.y = fmaf(gj[j], v[j].y, a.y);
+      a.z = fmaf(gj[j], v[j].z, a.z); a.w = fmaf(gj[j], v[j].w, a.w);
+    }
   }
   if (ys) {
     const float4 v = reinterpret_cast<const float4*>(ys + (int64_t)t * H)[c];

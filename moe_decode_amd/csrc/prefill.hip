@@ -477,43 +477,65 @@ constexpr int kLST = kKT + 16;    // LDS stride of a digit plane row (bank sprea
 // packed-int4 word's low and high nibbles are laid out as bytes); perm 2
 // (packed int2): within every 16 columns, column 4b + i goes to 4i + b (bit
 // pair i of the 4 bytes of a weight word forms one byte lane each).
-__global__ __launch_bounds__(256) void k_limbs(const float* __restrict__ a, int K, int perm,
-                                               int8_t* __restrict__ digits, int* __restrict__ expo) {
-  __shared__ float red[4];
+// One workgroup per row, one thread per 16 columns (K / 16 of them, the
+// workgroup rounded up to whole waves, at most 16): 16-byte loads of the
+// values, the row maximum by lane exchanges and LDS, and each digit plane's
+// 16 bytes stored at once.
+__global__ __launch_bounds__(1024) void k_limbs(const float* __restrict__ a, int K, int perm,
+                                                int8_t* __restrict__ digits, int* __restrict__ expo) {
+  __shared__ float red[16];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* row = a + (int64_t)r * K;
+  const int nw = (int)(blockDim.x >> 6);
+  const bool mine = 16 * tid < K;  // threads past the row's groups hold zeros and store nothing
+  const float* row = a + (int64_t)r * K + 16 * tid;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 q = mine ? reinterpret_cast<const float4*>(row)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+  }
   float m = 0.f;
-  for (int c = tid; c < K; c += 256) m = fmaxf(m, fabsf(row[c]));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if (lane == 0) red[wave] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  m = 0.f;
+  for (int w = 0; w < nw; ++w) m = fmaxf(m, red[w]);
   int E = 0;
   if (m > 0.f) frexpf(m, &E);  // m = f * 2^E, f in [0.5, 1): |a| < 2^E
   if (tid == 0) expo[r] = E;
-  int8_t* out = digits + (int64_t)r * 4 * K;
-  for (int c = tid; c < K; c += 256) {
-    const int X = (int)rintf(ldexpf(row[c], 30 - E));
-    const unsigned Y = (unsigned)X + 0x00808080u;
-    int p = c;
-    if (perm == 1) {
-      const int w = c & 7;
-      p = (c & ~7) + ((w & 1) ? 4 + (w >> 1) : (w >> 1));
-    } else if (perm == 2) {
-      const int w = c & 15;
-      p = (c & ~15) + 4 * (w & 3) + (w >> 2);
+  if (!mine) return;
+  // Y = X + bias: bytes 0-2 are digits 0-2 plus 128, byte 3 the top digit
+  uint32_t y[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = (uint32_t)(int)rintf(ldexpf(v[i], 30 - E)) + 0x00808080u;
+  // position p of the group holds column src(p)
+  auto src = [&](int p) {
+    if (perm == 1) { const int h = p & 7, b = p & 8; return b + (h < 4 ? 2 * h : 2 * (h - 4) + 1); }
+    if (perm == 2) return 4 * (p & 3) + (p >> 2);
+    return p;
+  };
+  int8_t* out = digits + (int64_t)r * 4 * K + 16 * tid;
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const uint32_t byte = l < 3 ? (((y[src(p)] >> (8 * l)) & 0xFFu) ^ 0x80u) : ((y[src(p)] >> 24) & 0xFFu);
+      w[p >> 2] |= byte << (8 * (p & 3));
     }
-    out[p] = (int8_t)((Y & 0xFFu) ^ 0x80u);
-    out[K + p] = (int8_t)(((Y >> 8) & 0xFFu) ^ 0x80u);
-    out[2 * K + p] = (int8_t)(((Y >> 16) & 0xFFu) ^ 0x80u);
-    out[3 * K + p] = (int8_t)(Y >> 24);
+    *reinterpret_cast<uint4*>(out + (int64_t)l * K) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 hipError_t launch_limbs(const float* a, int R, int K, int fmt, int8_t* digits, int* expo, hipStream_t st) {
   const int perm = fmt == I4_ROW ? 1 : fmt == I2_ROW ? 2 : 0;
-  hipLaunchKernelGGL(k_limbs, dim3(R), dim3(256), 0, st, a, K, perm, digits, expo);
+  // K is a multiple of 256 and at most 16384: K / 16 threads in whole waves
+  if (K % 256 || K > 16384 || R < 1) return hipErrorInvalidValue;
+  const int threads = (K / 16 + 63) / 64 * 64;
+  hipLaunchKernelGGL(k_limbs, dim3(R), dim3(threads), 0, st, a, K, perm, digits, expo);
   return hipGetLastError();
 }
 
