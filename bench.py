@@ -689,6 +689,41 @@ def decode_roofline(layers, sp, T, r):
     }
 
 
+def decode_leg(layers, sp, steps, warmup):
+    """One-token decode of a layer given as identical copies used in turn:
+    tokens/s, weight GB/s, each of its three launches (router; gate/up with
+    the shared expert's gate/up when it rides in that launch; down with the
+    combine) timed by back-to-back relaunches against the bytes it streams,
+    and the chain of plain reads of those bytes as the floor of a chain of
+    three launches."""
+    import numpy as np
+    r = run_mode(layers, sp, 1, steps, warmup)
+    n_ex = float(np.mean([len(np.unique(i)) for i in r["idx"]]))
+    from synth.formats import matrix_bytes
+    gu_routed = n_ex * 2 * matrix_bytes(sp.fmt, sp.F, sp.H)
+    dn_routed = n_ex * matrix_bytes(sp.fmt, sp.H, sp.F)
+    sh_gu = sh_dn = 0
+    if sp.shared_F:
+        sh_gu = 2 * matrix_bytes(sp.shared_fmt, sp.shared_F, sp.H)
+        sh_dn = matrix_bytes(sp.shared_fmt, sp.H, sp.shared_F)
+    stages = {"router": sp.router_bytes(), "gateup": gu_routed + sh_gu, "down": dn_routed + sh_dn}
+    out = {"workload": f"{sp.key}: MoE layer decode, 1 token per step, {sp.E} experts top-{sp.k}, hidden {sp.H}, "
+                       f"expert FFN {sp.F}, {sp.fmt} experts"
+                       + (f", {sp.shared_fmt} shared expert (FFN {sp.shared_F})" if sp.shared_F else "")
+                       + f", {len(layers)} copies of the layer in HBM used in turn",
+           "steps": steps, "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
+           "weight_bytes_per_step": r["weight_bytes_per_step"], "weight_GBps": r["weight_GBps"],
+           "weight_frac_of_8TBps": r["weight_GBps"] / HBM_PEAK_GBS, "launches": {}}
+    for st, nbytes in stages.items():
+        k = kernel_time(layers, sp, 1, st, n_inputs=32)
+        out["launches"][st] = {"us": k["ms_per_launch"] * 1e3, "bytes": nbytes,
+                               "GBps": nbytes / k["ms_per_launch"] / 1e6}
+    floor = chain_floor([int(v) for v in stages.values()])
+    out["chain_floor"] = floor
+    out["step_over_chain_floor"] = r["ms_per_step"] * 1e3 / floor["us_per_chain"]
+    return out
+
+
 def prefill_leg(layers, sp, steps, warmup, cpu, sample_tokens, T=128):
     """A T-token chunk of a layer: tokens/s and weight GB/s over `steps`
     chunks, the roofline of the grouped gate/up GEMM with its matrix-core
@@ -739,7 +774,7 @@ def main():
     ap.add_argument("--workload", default="c4_i4")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per step (1 = decode; up to 128 = a prefill chunk)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true", help="leave out the 128-token prefill leg")
+    ap.add_argument("--no-prefill", action="store_true", help="leave out the 128-token prefill legs and the c3 layer's decode leg")
     ap.add_argument("--modes", action="store_true", help="also time the other layer shapes")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--stack", type=int, default=0,
@@ -784,6 +819,7 @@ def main():
             f"({roof['achieved']:.0f} GB/s), down {roof['down_avg_launch_ms'] * 1e3:.2f} us")
 
     prefill = {}
+    decode_c3 = None
     inputs = {sp.key: hashes}
     if not args.no_prefill and T == 1:
         steps_p = max(10, args.steps // 10)
@@ -797,6 +833,10 @@ def main():
         inputs["c3"] = h3
         prefill["c3_T128"] = prefill_leg(copies, s3, 2 * steps_p, 3, not args.no_cpu_baseline, 32)
         log(f"[bench] c3 T=128: {prefill['c3_T128']['ms_per_step'] * 1e3:.0f} us/chunk")
+        decode_c3 = decode_leg(copies, s3, args.steps, args.warmup)
+        log(f"[bench] c3 T=1: {decode_c3['ms_per_step'] * 1e3:.1f} us/step, launches "
+            + ", ".join(f"{k} {v['us']:.1f} us" for k, v in decode_c3["launches"].items())
+            + f"; chain of plain reads {decode_c3['chain_floor']['us_per_chain']:.1f} us")
         del copies
         torch.cuda.empty_cache()
         layer = None
@@ -887,6 +927,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "prefill": prefill or None,
+        "decode_c3": decode_c3,
         "timing": {
             "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
             "graph_ms_per_step": r["graph_ms_per_step"],

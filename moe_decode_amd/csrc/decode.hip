@@ -390,8 +390,14 @@ struct SharedGU {
 
 // Blocks [0, T*k*rtiles): routed pair bid / rtiles, row tile bid % rtiles;
 // then T*ntiles shared blocks (token, row tile).
+#ifndef MD_RS_NP
+#define MD_RS_NP 4
+#endif
+constexpr int kRsNP = MD_RS_NP;                 // row pairs per lane group
+constexpr int kRsThreads = 256 * (8 / kRsNP);   // the same rows per workgroup
+
 template <int FMT, int L, int kNP, int SFMT, int SL, int SNP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gateup_rs(GateUpT1 a,
+__global__ __launch_bounds__(kRsThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gateup_rs(GateUpT1 a,
                                                                                              SharedGU sh,
                                                                                              int rtiles, int T) {
   extern __shared__ float lds[];
@@ -447,10 +453,17 @@ struct SharedDN {
   const float* hsc;
 };
 
-// Block = k + 1 waves: wave j < k streams kNRW rows of token t's slot j
-// expert, wave k the same rows of the shared expert (t = blockIdx.y).
+#ifndef MD_RS_SDW
+#define MD_RS_SDW 4
+#endif
+constexpr int kSDW = MD_RS_SDW;   // waves that share the shared expert's down rows
+
+// Block = k + kSDW waves: wave j < k streams kNRW rows of token t's slot j
+// expert, waves k.. the same rows of the shared expert, kNRW / kSDW rows each
+// (t = blockIdx.y).
 template <int FMT, int L, int CPL, int SFMT, int SL, int SCPL>
-__global__ __launch_bounds__(576) void k_down_rs(DownT1 a, SharedDN sh) {
+__global__ __launch_bounds__(64 * (8 + kSDW)) void k_down_rs(DownT1 a, SharedDN sh) {
+  static_assert(kNRW % kSDW == 0, "shared down rows per wave");
   __shared__ float red[9][kNRW];
   const int j = threadIdx.x >> 6;
   const int tok = blockIdx.y;
@@ -464,8 +477,10 @@ __global__ __launch_bounds__(576) void k_down_rs(DownT1 a, SharedDN sh) {
   } else {
     using D = Dig<SFMT>;
     const int ngh = sh.F / D::NV;
-    dn_rows<SFMT, SL, SCPL, kNRW>(sh.dq, sh.ds, a.H, sh.F, sh.hd + (int64_t)tok * ngh * D::NPL,
-                                  sh.hsc + (int64_t)tok * ngh, blockIdx.x * kNRW, red[a.k]);
+    constexpr int NR = kNRW / kSDW;
+    const int q = j - a.k;
+    dn_rows<SFMT, SL, SCPL, NR>(sh.dq, sh.ds, a.H, sh.F, sh.hd + (int64_t)tok * ngh * D::NPL,
+                                sh.hsc + (int64_t)tok * ngh, blockIdx.x * kNRW + q * NR, red[a.k] + q * NR);
   }
   __syncthreads();
   if (threadIdx.x < kNRW) {
@@ -604,16 +619,19 @@ struct RsGeom {
   int Ld, CPLd, Lsd, CPLsd;
 };
 static bool rs_geom(int fmt, int H, int F, int sfmt, int Fs, int k, int T, RsGeom& g) {
-  if (k + 1 > 9) return false;
+  if (k > 8) return false;
   if (!gu_geom(fmt, F, H, T * k, g.r) || !gu_geom(sfmt, Fs, H, T, g.s)) return false;
+  // the same rows per workgroup on more waves, fewer row pairs each
+  for (GuGeom* q : {&g.r, &g.s})
+    if (q->NP == 8 && kRsNP < 8) { q->RGW *= 8 / kRsNP; q->NP = kRsNP; }
   if (g.r.KS * g.r.RGW != g.s.KS * g.s.RGW) return false;   // one workgroup size
-  if (g.r.KS * g.r.RGW > 4) return false;                   // at most 256 threads (the kernel's bound)
+  if (64 * g.r.KS * g.r.RGW > kRsThreads) return false;     // the kernel's bound
   const int ncd = nchunks(fmt, F), ncs = nchunks(sfmt, Fs);
   g.Ld = pow2_div(ncd);
   g.Lsd = pow2_div(ncs);
   g.CPLd = ncd / g.Ld;
   g.CPLsd = ncs / g.Lsd;
-  return fmt == Q4_0 && sfmt == Q8_0 && g.r.L == 64 && g.r.NP == 8 && g.s.L == 64 && g.s.NP == 8 && g.Ld == 8 &&
+  return fmt == Q4_0 && sfmt == Q8_0 && g.r.L == 64 && g.r.NP == kRsNP && g.s.L == 64 && g.s.NP == kRsNP && g.Ld == 8 &&
          g.CPLd == 3 && g.Lsd == 64 && g.CPLsd == 2;
 }
 
@@ -636,7 +654,7 @@ hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st) {
   const size_t lds = sizeof(float) * (mx + (ks > 1 ? 2 * ks * mx : 0));
   const int nblk = L.T * L.k * rtiles + L.T * stiles;
   if (L.parts & 1) {
-    hipLaunchKernelGGL((k_gateup_rs<Q4_0, 64, 8, Q8_0, 64, 8>), dim3(nblk), dim3(64 * g.r.KS * g.r.RGW), lds, st, a,
+    hipLaunchKernelGGL((k_gateup_rs<Q4_0, 64, kRsNP, Q8_0, 64, kRsNP>), dim3(nblk), dim3(64 * g.r.KS * g.r.RGW), lds, st, a,
                        sh, rtiles, L.T);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -645,7 +663,7 @@ hipError_t launch_moe_rs(const RsLaunch& L, hipStream_t st) {
     DownT1 d{L.dq, L.ds, L.dn_bytes, L.H, L.F, L.k, L.idx, L.gates, static_cast<const u32x4*>(L.hd), L.hsc,
              L.residual, L.y};
     SharedDN sd{L.sdq, L.sds, L.Fs, static_cast<const u32x4*>(L.shd), L.shsc};
-    hipLaunchKernelGGL((k_down_rs<Q4_0, 8, 3, Q8_0, 64, 2>), dim3((L.H + kNRW - 1) / kNRW, L.T), dim3(64 * (L.k + 1)),
+    hipLaunchKernelGGL((k_down_rs<Q4_0, 8, 3, Q8_0, 64, 2>), dim3((L.H + kNRW - 1) / kNRW, L.T), dim3(64 * (L.k + kSDW)),
                        0, st, d, sd);
     return hipGetLastError();
   }
