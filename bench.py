@@ -13,7 +13,10 @@ chunks of that layer and of the 128-expert layer with a shared expert (four
 copies of that layer in HBM, used in turn, so its 354 MB of weights are not
 served from the Infinity Cache), each with tokens/s, weight GB/s, the
 roofline of its dominant kernel with the matrix cores' utilisation, and the
-oracle timed on a sample of the same chunk.
+oracle timed on a sample of the same chunk; and "decode_c3": the one-token
+decode of the shared-expert layer (the same four copies), with each of its
+three launches timed against the bytes it streams and the chain of plain
+reads of those bytes.
 
 Each roofline's kernel time is measured live: a number of forwards, each on
 its own inputs and workspace, then that stage alone relaunched over all of
@@ -171,7 +174,7 @@ def run_mode(layers, sp, T, steps, warmup, stage="gateup", graph=False):
         "step_ms_p10_p50_p90": [float(v) for v in np.percentile(step_ms, [10, 50, 90])],
         "host_us_per_call": host_s / steps * 1e6,
         "graph_ms_per_step": graph_ms,
-        "idx": idx_np,
+        "idx": idx_np[:min(max(steps, warmup), pool)],   # the pool entries the calls wrote
     }
 
 
@@ -697,7 +700,7 @@ def decode_leg(layers, sp, steps, warmup):
     and the chain of plain reads of those bytes as the floor of a chain of
     three launches."""
     import numpy as np
-    r = run_mode(layers, sp, 1, steps, warmup)
+    r = run_mode(layers, sp, 1, steps, warmup, graph=True)
     n_ex = float(np.mean([len(np.unique(i)) for i in r["idx"]]))
     from synth.formats import matrix_bytes
     gu_routed = n_ex * 2 * matrix_bytes(sp.fmt, sp.F, sp.H)
@@ -712,6 +715,11 @@ def decode_leg(layers, sp, steps, warmup):
                        + (f", {sp.shared_fmt} shared expert (FFN {sp.shared_F})" if sp.shared_F else "")
                        + f", {len(layers)} copies of the layer in HBM used in turn",
            "steps": steps, "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
+           # the same steps captured in one HIP graph and replayed: the GPU's
+           # time per step without the host's time per call (which is close
+           # to this layer's short kernel chain)
+           "graph_ms_per_step": r["graph_ms_per_step"],
+           "host_us_per_call": r["host_us_per_call"],
            "weight_bytes_per_step": r["weight_bytes_per_step"], "weight_GBps": r["weight_GBps"],
            "weight_frac_of_8TBps": r["weight_GBps"] / HBM_PEAK_GBS, "launches": {}}
     for st, nbytes in stages.items():
@@ -834,7 +842,8 @@ def main():
         prefill["c3_T128"] = prefill_leg(copies, s3, 2 * steps_p, 3, not args.no_cpu_baseline, 32)
         log(f"[bench] c3 T=128: {prefill['c3_T128']['ms_per_step'] * 1e3:.0f} us/chunk")
         decode_c3 = decode_leg(copies, s3, args.steps, args.warmup)
-        log(f"[bench] c3 T=1: {decode_c3['ms_per_step'] * 1e3:.1f} us/step, launches "
+        log(f"[bench] c3 T=1: {decode_c3['ms_per_step'] * 1e3:.1f} us/step "
+            f"({decode_c3['graph_ms_per_step'] * 1e3:.1f} as HIP-graph replays), launches "
             + ", ".join(f"{k} {v['us']:.1f} us" for k, v in decode_c3["launches"].items())
             + f"; chain of plain reads {decode_c3['chain_floor']['us_per_chain']:.1f} us")
         del copies
