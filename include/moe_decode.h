@@ -223,9 +223,15 @@ md_status md_ffn_forward(const md_ffn *f /*host*/, const float *x, int32_t T, fl
  * layer runs as router, gate/up and down kernels (a shared expert runs inside
  * the routed launches where its shapes are covered, else as its own two
  * launches first).  Longer chunks group the pairs by expert and read each
- * selected expert once per 16-token tile of the tokens that chose it.
- * There is one code path per shape: nothing in the environment selects
- * another. */
+ * selected expert once per 16-token tile of the tokens that chose it; their
+ * shared expert, which needs only x, runs on a second stream of the
+ * library's own (one per device, default priority, created at the device's
+ * first such call) beside the routing kernels and joins `stream` before the
+ * combine, so the call's work still starts after, and ends before, the
+ * work around it on `stream` (a graph captured from `stream` takes the side
+ * stream's launches in as a branch).  The results are those of the same
+ * kernels on `stream` alone, bit for bit.  There is one code path per shape:
+ * nothing in the environment selects another. */
 md_status md_moe_workspace_size(const md_moe_layer *L /*host*/, int32_t T, size_t *bytes /*host*/);
 md_status md_moe_layer_forward(const md_moe_layer *L /*host*/, const float *x, int32_t T, float *y,
                                int32_t *idx_out, float *gates_out,
@@ -242,6 +248,7 @@ md_status md_moe_layer_forward(const md_moe_layer *L /*host*/, const float *x, i
  * share its array: calls that overlap on one GPU (other streams, other host
  * threads) race and must be serialized by the caller; the array keeps the
  * last call's contents, and nothing in it needs to start cleared.
+ * Everything runs on `stream` (no side stream).
  * Errors: as md_moe_layer_forward; a call whose scratch (the size
  * md_moe_workspace_size reports) exceeds 64 MiB -> MD_ERR_UNSUPPORTED, with
  * nothing enqueued (every layer and token count of the seeded workloads fits:
@@ -250,8 +257,9 @@ md_status md_moe_layer_forward(const md_moe_layer *L /*host*/, const float *x, i
 md_status md_moe_layer_forward_noalloc(const md_moe_layer *L /*host*/, const float *x, int32_t T, float *y,
                                        int32_t *idx_out, float *gates_out, hipStream_t stream);
 
-/* Measurement variant of md_moe_layer_forward: identical work and results;
- * additionally records `start` on `stream` just before the launches of stage
+/* Measurement variant of md_moe_layer_forward: identical work and results,
+ * every launch on `stream` (no side stream); additionally records `start` on
+ * `stream` just before the launches of stage
  * `stage` and `stop` just after them (HIP events created by the caller), so
  * the elapsed time between the two events is that stage's time on the
  * stream.  A stage the call does not run (the shared expert of a layer

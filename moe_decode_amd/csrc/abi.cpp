@@ -504,10 +504,53 @@ md_status md_moe_workspace_size(const md_moe_layer* L, int32_t T, size_t* bytes)
 }
 
 // residual: nullable [T][H], added to y (it may be y itself).
+// A second stream per device for a chunk's shared expert: it needs only x,
+// so it runs beside the routing kernels (which occupy a small part of the
+// GPU) and joins the caller's stream before the combine.  Created at a
+// device's first such call, default priority; each fork (event recorded on
+// the caller's stream, waited on by the side stream) and each join (the
+// reverse) is made under one lock, so concurrent calls cannot interleave them.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+static std::mutex g_side_mu;
+static SideStream g_side[64];
+
+static SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+      if (a) (void)hipEventDestroy(a);
+      (void)hipStreamDestroy(st);
+      return nullptr;
+    }
+    ss.s = st;
+    ss.fork = a;
+    ss.join = b;
+  }
+  return &ss;
+}
+
+// `from` waits for everything enqueued on `to_wait_on` so far.
+static hipError_t stream_after(SideStream* ss, hipEvent_t ev, hipStream_t to_wait_on, hipStream_t from) {
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  hipError_t e = hipEventRecord(ev, to_wait_on);
+  if (e == hipSuccess) e = hipStreamWaitEvent(from, ev, 0);
+  return e;
+}
+
 static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
                              float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream,
                              int32_t stage, hipEvent_t ev0, hipEvent_t ev1, const float* residual = nullptr,
-                             int32_t only = -1) {
+                             int32_t only = -1, bool allow_side = false) {
   md_status s = check_moe(L, T);
   if (s != MD_OK) return s;
   if (!x || !y) return fail(MD_ERR_INVALID_ARG, "null x or y");
@@ -668,19 +711,41 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       }
     }
   }
+  // a plain call runs the shared expert on the side stream; every exit after
+  // the fork joins it back into the caller's stream
+  SideStream* side = nullptr;
+  struct Join {
+    SideStream* ss = nullptr;
+    hipStream_t caller = nullptr;
+    hipError_t now() {
+      if (!ss) return hipSuccess;
+      SideStream* t = ss;
+      ss = nullptr;
+      return stream_after(t, t->join, t->s, caller);
+    }
+    ~Join() { (void)now(); }
+  } join;
   if (L->has_shared && want(MD_STAGE_SHARED)) {
+    hipStream_t sst = stream;
+    if (allow_side && stage < 0 && only < 0 && (side = side_stream()) != nullptr) {
+      e = stream_after(side, side->fork, stream, side->s);
+      if (e != hipSuccess) return hip_fail(e, "side stream fork");
+      join.ss = side;
+      join.caller = stream;
+      sst = side->s;
+    }
     ChunkAct xs = xa;
     const int sfmt = L->shared.gate.type;
     if (row_type(sfmt)) {  // x digits in the shared expert's own column order
       e = md::launch_limbs(x, T, H, sfmt, static_cast<int8_t*>(P(w.xs_dig)),
-                           static_cast<int*>(P(w.xs_exp)), stream);
+                           static_cast<int*>(P(w.xs_exp)), sst);
       if (e != hipSuccess) return hip_fail(e, "digit launch");
       xs.dig = static_cast<int8_t*>(P(w.xs_dig));
       xs.expo = static_cast<int*>(P(w.xs_exp));
     }
     s = run_ffn_mfma(&L->shared, xs, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
                      static_cast<u16*>(P(w.hs_lo)), static_cast<int8_t*>(P(w.hs_dig)), static_cast<int*>(P(w.hs_exp)),
-                     y_s, stream);
+                     y_s, sst);
     if (s != MD_OK) return s;
   }
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
@@ -743,6 +808,7 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     }
   }
   if (!mark(MD_STAGE_DOWN, ev1) || !mark(MD_STAGE_COMBINE, ev0)) return hip_fail(e, "event record");
+  if ((e = join.now()) != hipSuccess) return hip_fail(e, "side stream join");
   if (want(MD_STAGE_COMBINE)) {
     e = md::launch_combine(o, dout.pos_of_pair, gates, T, k, H, y_s, residual, y, stream);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
@@ -885,7 +951,8 @@ static md_status experts_forward(const md_moe_layer* L, const float* x, int32_t 
 
 md_status md_moe_layer_forward(const md_moe_layer* L, const float* x, int32_t T, float* y, int32_t* idx_out,
                                float* gates_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr);
+  return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr,
+                     nullptr, -1, true);
 }
 
 }  // extern "C"
@@ -967,7 +1034,7 @@ md_status md_moe_layer_forward_residual(const md_moe_layer* L, const float* x, i
   if (!residual) return fail(MD_ERR_INVALID_ARG, "residual is null");
   if (!aligned16(residual)) return fail(MD_ERR_ALIGNMENT, "residual not 16-byte aligned");
   return moe_forward(L, x, T, y, idx_out, gates_out, workspace, workspace_bytes, stream, -1, nullptr, nullptr,
-                     residual);
+                     residual, -1, true);
 }
 
 md_status md_add(const float* a, const float* b, float* y, int64_t n, hipStream_t stream) {
