@@ -584,11 +584,23 @@ def host_record():
 
 
 def git_sha():
+    """The checkout's commit, or (where the tree travelled without its
+    history) the one the library was built from, as its build recorded it."""
     import subprocess
     try:
         r = subprocess.run(["git", "rev-parse", "HEAD"], cwd=ROOT, capture_output=True, text=True, timeout=10)
-        return r.stdout.strip() or None
+        if r.stdout.strip():
+            return r.stdout.strip()
     except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open(os.path.join(ROOT, "moe_decode_amd", "build_info.json")) as f:
+            info = json.load(f)
+        sha = info.get("git_sha")
+        if sha and info.get("sources_differ_from_commit"):
+            sha += " (library built from sources differing from it)"
+        return sha
+    except (OSError, ValueError):
         return None
 
 

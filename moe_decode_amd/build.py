@@ -68,7 +68,35 @@ def build(verbose=False, out=None, build_dir=None, defines=(), sanitize=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, out)
+    if not sanitize and out == OUT:
+        _write_build_info(srcs)
     return out
+
+
+BUILD_INFO = os.path.join(HERE, "build_info.json")
+
+
+def _write_build_info(srcs):
+    """The commit and source hash the library was built from, beside it (the
+    library travels without the repository's history)."""
+    import hashlib
+    import json
+    sha = None
+    try:
+        r = subprocess.run(["git", "rev-parse", "HEAD"], cwd=os.path.dirname(HERE), capture_output=True, text=True,
+                           timeout=10)
+        sha = r.stdout.strip() or None
+        d = subprocess.run(["git", "status", "--porcelain", "--", "moe_decode_amd/csrc", "include"],
+                           cwd=os.path.dirname(HERE), capture_output=True, text=True, timeout=10)
+        dirty = bool(d.stdout.strip())
+    except (OSError, subprocess.SubprocessError):
+        dirty = None
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        h.update(name.encode())
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    with open(BUILD_INFO, "w") as f:
+        json.dump({"git_sha": sha, "sources_differ_from_commit": dirty, "csrc_sha256": h.hexdigest()}, f)
 
 
 if __name__ == "__main__":
