@@ -101,3 +101,42 @@ def test_residual_form_on_the_side_stream():
     md.add(r, y_ref, out=out)
     torch.cuda.synchronize()
     assert torch.equal(y, out)
+
+
+def test_graph_capture_takes_the_side_stream_in():
+    """A chunk forward captured in a HIP graph from a torch stream (the side
+    stream joins the capture through the fork event and leaves it through
+    the join), replayed three times with eager forwards of other inputs in
+    between: every replay gives the eager result for its input, bit for bit."""
+    import moe_decode_amd as md
+    import torch
+    T = 128
+    say(f"[side] c3 graph capture T={T}")
+    sp = W.spec("c3")
+    layer = moe_layer("c3")
+    x = torch.from_numpy(W.moe_x(sp, T)).cuda()
+    x_other = torch.tanh(x * 3.0)
+    ws = torch.empty(md.moe_workspace_size(layer, T), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws)
+    y = torch.empty(T, sp.H, device="cuda")
+    idx = torch.empty(T, sp.k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, sp.k, device="cuda")
+    y_ref = torch.empty_like(y)
+    md.moe_layer_forward(layer, x, y=y_ref, workspace=ws_e)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            md.moe_layer_forward(layer, x, y=y, idx=idx, gates=gates, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    y_other = torch.empty_like(y)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        md.moe_layer_forward(layer, x_other, y=y_other, workspace=ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}"
+    del g
