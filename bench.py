@@ -471,7 +471,7 @@ def hbm_probe(nbytes=4 << 30, reps=5):
     src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen)
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     sweep = []
-    for wg in (1024, 2048, 4096, 8192, 16384):
+    for wg in (2048, 8192, 32768, 65536, 131072):
         md.hbm_read_probe(src, sink, workgroups=wg)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
@@ -504,14 +504,51 @@ def chain_floor(sizes, reps=16, pool_bytes=4 << 30):
     per_chain = sum((n + 255) // 256 * 256 for n in sizes)
     chains = max(1, pool_bytes // per_chain)
 
+    # each read's grid: the fastest of one, two or four 32 KB tiles per
+    # workgroup, each timed alone (graph replays over fresh regions)
+    def timed(nbytes, wg, n=16):
+        nb = (nbytes + 15) // 16 * 16
+        stride = (nb + 255) // 256 * 256
+        k = max(1, min(n, pool_bytes // stride))
+
+        def go():
+            for i in range(n):
+                o = (i % k) * stride
+                md.hbm_read_probe(src[o:o + nb], sink, workgroups=wg)
+        go()
+        torch.cuda.synchronize()
+        gg = torch.cuda.CUDAGraph()
+        ss = torch.cuda.Stream()
+        ss.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(ss):
+            with torch.cuda.graph(gg, stream=ss):
+                go()
+        torch.cuda.current_stream().wait_stream(ss)
+        gg.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        gg.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del gg
+        return a.elapsed_time(b) / n
+
+    grids = []
+    for n in sizes:
+        tiles = max(1, -(-n // 32768))
+        cand = sorted({tiles, max(1, -(-tiles // 2)), max(1, -(-tiles // 4))})
+        grids.append(min(cand, key=lambda wg: timed(n, wg)))
+
     def run():
         off = 0
         for c in range(reps):
             if (c % chains) == 0:
                 off = 0
-            for n in sizes:
+            for n, wg in zip(sizes, grids):
                 n16 = (n + 15) // 16 * 16
-                md.hbm_read_probe(src[off:off + n16], sink, workgroups=max(64, min(8192, n16 // 32768 + 1)))
+                md.hbm_read_probe(src[off:off + n16], sink, workgroups=wg)
                 off += (n16 + 255) // 256 * 256
 
     run()
@@ -534,7 +571,7 @@ def chain_floor(sizes, reps=16, pool_bytes=4 << 30):
     ms = t0.elapsed_time(t1) / reps
     del g, src
     torch.cuda.empty_cache()
-    return {"bytes": list(sizes), "us_per_chain": ms * 1e3, "GBps": sum(sizes) / (ms / 1e3) / 1e9,
+    return {"bytes": list(sizes), "workgroups": grids, "us_per_chain": ms * 1e3, "GBps": sum(sizes) / (ms / 1e3) / 1e9,
             "timing": f"{reps} chains of back-to-back read-probe launches in one HIP graph"}
 
 

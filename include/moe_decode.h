@@ -411,7 +411,10 @@ md_status md_moe_cached_forward(const md_moe_layer *src /*host*/, const md_moe_l
  * sink[0]; for zeroed memory any nonzero key keeps sink untouched).  Timed over a buffer far larger than the caches it gives the HBM
  * read bandwidth this device attains, the practical ceiling of the weight
  * streams above (the Camelid README, "Gemma 4": GPU-resident decode runs at
- * the memory-bandwidth wall).  workgroups: 0 picks the default (2048).
+ * the memory-bandwidth wall).  workgroups: the grid (0 picks 2048; at most
+ * one workgroup per 32 KB tile is launched); each workgroup takes its tiles
+ * in groups of up to four consecutive ones, every load of a group in flight
+ * before any is used.
  * Errors: null pointer -> MD_ERR_INVALID_ARG; nbytes 0 or not a multiple of
  * 16 -> MD_ERR_SHAPE; src not 16-byte aligned -> MD_ERR_ALIGNMENT;
  * workgroups < 0 or > 2^20 -> MD_ERR_INVALID_ARG. */

@@ -476,27 +476,31 @@ hipError_t launch_add(const float* a, const float* b, float* y, int64_t n, hipSt
 }
 
 // The attainable HBM read bandwidth, the practical ceiling of every weight
-// stream here: each workgroup reads tiles of kBlock x kProbeU 16-byte chunks,
-// all kProbeU loads of a lane issued before any is used, tiles taken in
-// address order across the grid.  Indexes past the end are clamped (the last
-// chunk is read again) so no load waits on a branch.  A lane stores the xor
-// of the words it read only when that equals `key`, which the caller picks so
-// that it does not happen for the data; the loads cannot be dropped.
+// stream here: each workgroup reads groups of U tiles of kBlock x kProbeU
+// 16-byte chunks (the kernels' streaming loads), groups taken in address order
+// across the grid, all U x kProbeU loads of a lane in flight before any is
+// used (U = the tiles per workgroup the grid implies, 1 to 4).  Indexes past
+// the end are clamped (the last chunk is read again) so no load sits under a
+// branch.  A lane stores the xor of the words it read only when that equals
+// `key`, which the caller picks so that it does not happen for the data; the
+// loads cannot be dropped.
 constexpr int kProbeU = 8;
 
+template <int U>
 __global__ __launch_bounds__(kBlock) void k_read_probe(const uint4* __restrict__ src, int64_t n16, uint32_t key,
                                                        uint32_t* sink) {
-  constexpr int64_t tile = (int64_t)kBlock * kProbeU;
+  constexpr int64_t group = (int64_t)U * kBlock * kProbeU;
+  const uint8_t* base8 = reinterpret_cast<const uint8_t*>(src);
   uint32_t acc = 0;
-  for (int64_t base = (int64_t)blockIdx.x * tile; base < n16; base += (int64_t)gridDim.x * tile) {
-    uint4 v[kProbeU];
+  for (int64_t base = (int64_t)blockIdx.x * group; base < n16; base += (int64_t)gridDim.x * group) {
+    u32x4 v[U * kProbeU];
 #pragma unroll
-    for (int j = 0; j < kProbeU; ++j) {
+    for (int j = 0; j < U * kProbeU; ++j) {
       const int64_t i = base + j * kBlock + threadIdx.x;
-      v[j] = src[i < n16 ? i : n16 - 1];
+      v[j] = ld_stream(base8 + 16 * (i < n16 ? i : n16 - 1));
     }
 #pragma unroll
-    for (int j = 0; j < kProbeU; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    for (int j = 0; j < U * kProbeU; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
   }
   if (acc == key) sink[0] = acc;
 }
@@ -505,8 +509,16 @@ hipError_t launch_read_probe(const void* src, int64_t n16, uint32_t key, uint32_
                              hipStream_t st) {
   const int64_t tiles = (n16 + (int64_t)kBlock * kProbeU - 1) / ((int64_t)kBlock * kProbeU);
   const int g = (int)std::min<int64_t>(grid, tiles);
-  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)g), dim3(kBlock), 0, st, static_cast<const uint4*>(src), n16,
-                     key, sink);
+  const int64_t per = (tiles + g - 1) / g;  // tiles per workgroup
+  const uint4* s4 = static_cast<const uint4*>(src);
+  if (per >= 4) {
+    hipLaunchKernelGGL(k_read_probe<4>, dim3((unsigned)std::min<int64_t>(g, (tiles + 3) / 4)), dim3(kBlock), 0, st,
+                       s4, n16, key, sink);
+  } else if (per >= 2) {
+    hipLaunchKernelGGL(k_read_probe<2>, dim3((unsigned)((tiles + 1) / 2)), dim3(kBlock), 0, st, s4, n16, key, sink);
+  } else {
+    hipLaunchKernelGGL(k_read_probe<1>, dim3((unsigned)tiles), dim3(kBlock), 0, st, s4, n16, key, sink);
+  }
   return hipGetLastError();
 }
 
