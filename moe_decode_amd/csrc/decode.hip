@@ -206,9 +206,11 @@ __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x
 }
 
 #ifndef MD_ROUTER_BLOCKS
-#define MD_ROUTER_BLOCKS 256
+#define MD_ROUTER_BLOCKS 128
 #endif
 // K-slices per expert: the fewest that give at least MD_ROUTER_BLOCKS blocks
+// (128-expert layer: one slice instead of two, so each gate/up workgroup's
+// top-k reads half the partials: router 3.58 -> 3.44 us, gate/up 8.75 -> 8.62)
 int router_splits(int H, int E) {
   const int units = H / 256;  // K-slices stay multiples of 256
   int S = 1;
