@@ -76,7 +76,7 @@ MD_DEV void dig_rows(const DigJob& j, uint32_t* ys, int b, int nb) {
 }
 
 // Workgroups that one pass of dig_rows needs for a job (0 without a job).
-static int dig_blocks(const DigJob& j) {
+__host__ __device__ static int dig_blocks(const DigJob& j) {
   if (!j.x) return 0;
   const int nv = dig_nv(j.fmt);
   const int64_t G = (int64_t)j.R * j.K / nv;
@@ -140,10 +140,13 @@ __global__ __launch_bounds__(256) void k_router_part(const float* __restrict__ x
   __shared__ uint32_t ys[256];
   const int nr = E * S;
   if ((int)blockIdx.x >= nr) {
-    // the activations' digit planes for the expert kernels (independent of the routing)
-    const int b = blockIdx.x - nr, nb = gridDim.x - nr;
-    dig_rows(j0, ys, b, nb);
-    dig_rows(j1, ys, b, nb);
+    // the activations' digit planes for the expert kernels (independent of
+    // the routing): the first dig_blocks(j0) workgroups take the first job,
+    // the rest the second, so each makes one pass (two passes in one
+    // workgroup were the launch's longest path on the shared-expert layer)
+    const int b = blockIdx.x - nr, n0 = dig_blocks(j0), n1 = gridDim.x - nr - n0;
+    if (b < n0) dig_rows(j0, ys, b, n0);
+    else dig_rows(j1, ys, b - n0, n1);
     return;
   }
   const int e = blockIdx.x / S, sl = blockIdx.x % S;
@@ -221,7 +224,7 @@ int router_splits(int H, int E) {
 
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
                               const DigJob& j0, const DigJob& j1, hipStream_t st) {
-  const int nd = dig_blocks(j0) > dig_blocks(j1) ? dig_blocks(j0) : dig_blocks(j1);
+  const int nd = dig_blocks(j0) + dig_blocks(j1);
   hipLaunchKernelGGL(k_router_part, dim3(E * S + nd), dim3(256), 0, st, x, T, H, Wr, E, S, part, j0, j1);
   return hipGetLastError();
 }
