@@ -15,30 +15,36 @@ namespace md {
 
 // -------------------------------------------------------------- router
 
-// Chunk router: logits partials of many tokens as a register-tiled fp64 GEMM.
-// Block (ex, ty, s) covers experts 64*ex.., tokens 64*ty.. and K-slice s; a
-// thread owns 4 experts x 4 tokens (experts tx + 16i, tokens tyy + 16j).  W_r
-// and x tiles are staged as fp32 in LDS (transposed, padded) and widened
-// to fp64 at use; each product of two fp32 values is exact in fp64, and the
-// K-slice's terms are accumulated in ascending k with fp64 FMAs.
+// Chunk router: logits partials of many tokens as a GEMM on the fp64 matrix
+// cores (v_mfma_f64_16x16x4_f64).  Block (ex, ty, s) covers experts 64*ex..,
+// tokens 64*ty.. and K-slice s; each wave owns 2 x 2 tiles of 16 experts x 16
+// tokens.  W_r and x tiles are staged as fp32 in LDS (transposed, padded),
+// each operand widened to fp64 as it is read (exact), and each product of two
+// fp32 values is exact in fp64; the K-slice's terms accumulate in fp64.
 constexpr int kRG = 64;   // experts / tokens per block tile
 constexpr int kRKC = 32;  // K per LDS stage
 
-__global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x, int T, int H,
+// Per 4-wide K step a lane widens one W_r and one x element per tile row /
+// column from the LDS stage.  Operand layout of the 16x16x4 fp64 MFMA
+// (checked on the device): A[i][k] and B[k][j] at lane 16 k + i (j), result
+// D[4 v + lane / 16][lane % 16] in element v.  The next stage's tiles are
+// fetched into registers while a stage is used.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_router_mfma(const float* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr, int E, int Ks,
                                                      double* __restrict__ part) {
   __shared__ float sw[kRKC][kRG + 1];
   __shared__ float sx[kRKC][kRG + 1];
-  const int tid = threadIdx.x, tx = tid & 15, tyy = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e0 = blockIdx.x * kRG, t0 = blockIdx.y * kRG, sl = blockIdx.z;
   const int kbeg = sl * Ks;
-  double acc[4][4];
+  const int li = lane & 15, kq = lane >> 4;
+  const int er0 = 2 * (wave & 1), tc0 = 2 * (wave >> 1);  // this wave's first tile row / column
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-
-  // the next stage's tiles are fetched into registers while this one is used
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   float4 pw[2], px[2];
   auto fetch = [&](int kc) {
 #pragma unroll
@@ -62,30 +68,32 @@ __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x
     }
     __syncthreads();
     if (kc + kRKC < kbeg + Ks) fetch(kc + kRKC);
-#pragma unroll 4
-    for (int kk = 0; kk < kRKC; ++kk) {
-      double wd[4], xd[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wd[i] = (double)sw[kk][tx + 16 * i];
+    for (int k4 = 0; k4 < kRKC; k4 += 4) {
+      double av[2], bv[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xd[j] = (double)sx[kk][tyy + 16 * j];
+      for (int a = 0; a < 2; ++a) av[a] = (double)sw[k4 + kq][16 * (er0 + a) + li];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int b = 0; b < 2; ++b) bv[b] = (double)sx[k4 + kq][16 * (tc0 + b) + li];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(wd[i], xd[j], acc[i][j]);
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + tyy + 16 * j;
-    if (t >= T) continue;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + tx + 16 * i;
-      if (e < E) part[((int64_t)sl * T + t) * E + e] = acc[i][j];
+    for (int b = 0; b < 2; ++b) {
+      const int t = t0 + 16 * (tc0 + b) + li;
+      if (t >= T) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int e = e0 + 16 * (er0 + a) + 4 * v + kq;
+        if (e < E) part[((int64_t)sl * T + t) * E + e] = acc[a][b][v];
+      }
     }
-  }
 }
 
 #ifndef MD_ROUTER_GEMM_BLOCKS
@@ -125,7 +133,7 @@ hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, c
   if (!p.gemm) return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, st);
   if (j0.x || j1.x) return hipErrorInvalidValue;
   const dim3 grid((E + kRG - 1) / kRG, (T + kRG - 1) / kRG, p.S);
-  hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, st, x, T, H, Wr, E, H / p.S, part);
+  hipLaunchKernelGGL(k_router_mfma, grid, dim3(256), 0, st, x, T, H, Wr, E, H / p.S, part);
   return hipGetLastError();
 }
 
