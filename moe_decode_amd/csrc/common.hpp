@@ -73,6 +73,22 @@ MD_DEV u32x4 ld_stream(const uint8_t* p) {
 #endif
 }
 
+// Raw buffer resource over the n bytes at p (descriptor word 3 of the gfx9
+// family: dword data, range-checked).  A read at an offset past n returns
+// zeros and touches no memory; kPast is past the end of every resource here
+// (all are under 2 GiB, so offset + kPast never wraps).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+MD_DEV rsrc_t make_res(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+constexpr uint32_t kPast = 0x80000000u;
+MD_DEV uint32_t past(bool ok, uint32_t off) { return ok ? off : kPast; }
+constexpr int kAuxStream = MD_NT_LOADS ? 2 : 0;  // nontemporal hint for streamed weights
+template <int AUX = 0>
+MD_DEV u32x4 buf_load(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+}
+
 MD_DEV float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
 // Scale that multiplies chunk c of a row (block formats, including the 1/16

@@ -150,6 +150,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
   using TL = Tile<FMT>;
   constexpr int BR = 64 * RT;
   constexpr int WCH = BR * TL::WB / 16, WPT = WCH / 256;
+  // gate/up: a thread's pieces i < WPT/2 lie in the gate rows, the rest in the up rows
+  static_assert(!GU || WPT % 2 == 0, "gate and up rows split the pieces evenly");
   __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BR * TL::WSTR];
   __shared__ __attribute__((aligned(16))) uint16_t s_sc[2][BR * TL::SCW];
   __shared__ __attribute__((aligned(16))) u16 s_hi[2][kTok * kAST];
@@ -180,14 +182,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
   // block rows: gate/up stage -> BR/2 gate + BR/2 up rows of f0..
   const int r0 = GU ? blockIdx.x * (BR / 2) : blockIdx.x * BR;
 
-  auto row_ptr = [&](int r) -> const uint8_t* {  // r: block row 0..BR-1
-    if (GU) {
-      const int f = min(r0 + (r % (BR / 2)), a.M - 1);
-      const uint8_t* base = (r < BR / 2 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes;
-      return base + (int64_t)f * rb;
-    }
-    return a.wq + (int64_t)er.e * a.mat_bytes + (int64_t)min(r0 + r, a.M - 1) * rb;
-  };
   auto pos_token = [&](int pos) { return a.d.n_active == nullptr ? pos : a.d.pairs[pos] / a.d.k; };
 
   {
@@ -196,43 +190,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
     const int nt = min(kTok, er.p1 - t0);
     // this thread's activation rows for staging: token slot jj = tid / 16, piece pp = tid % 16
     const int jj = tid >> 4, pp = tid & 15;
-    const u16* ahi = nullptr;
-    const u16* alo = nullptr;
+    constexpr bool has_lo = LO;
+    // Tiles are read through buffer resources: an offset past a resource's
+    // end reads zeros without a memory access, so the lanes with nothing to
+    // load (empty token slots, lanes past the scale rows) and the tiles past
+    // the last one issue the same loads as the others.  With no branch around
+    // a load, the compiled loop waits only for the older of the two tiles in
+    // flight (where the paths of a conditional load meet it waits for all).
+    const uint8_t* wg = a.wq + (int64_t)er.e * a.mat_bytes;
+    const uint8_t* wu = GU ? a.wq2 + (int64_t)er.e * a.mat_bytes : wg;
+    const int mat_len = (int)((int64_t)a.M * rb);
+    const rsrc_t res_g = make_res(wg, mat_len), res_u = make_res(wu, mat_len);
+    const int a_rows = a.act_by_token ? a.d.T : a.d.T * a.d.k;
+    const int a_len = (int)((int64_t)a_rows * a.K * 2);
+    const rsrc_t res_ah = make_res(a.a_hi, a_len), res_al = make_res(has_lo ? a.a_lo : a.a_hi, a_len);
+    uint32_t woff[WPT];  // this thread's weight pieces, tile 0 of the matrix
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
+      const int f = min(r0 + (GU ? r % (BR / 2) : r), a.M - 1);
+      woff[i] = (uint32_t)((int64_t)f * rb) + 16u * piece;
+    }
+    // block scales, BR rows x SCW fp16 words per tile, spread over all 256
+    // threads: SPT bytes each, TPR threads per row (gate/up: the gate rows'
+    // scales fall to threads 0..127, waves 0 and 1)
+    constexpr int SPT = BR * TL::SCW * 2 / 256, TPR = TL::SCW * 2 / SPT;
+    static_assert(!TL::BLK || ((SPT == 4 || SPT == 8) && TPR * BR == 256), "scale pieces");
+    const int sc_row = tid / TPR, sc_part = tid % TPR;
+    const bool up_wave = GU && __builtin_amdgcn_readfirstlane(tid) >= 128;
+    const rsrc_t res_s = up_wave ? res_u : res_g;
+    const uint32_t soff = (uint32_t)((int64_t)min(r0 + (GU ? sc_row % (BR / 2) : sc_row), a.M - 1) * rb) +
+                          (uint32_t)(FMT == Q8_0 ? a.K : (a.K / 32) * 16) + (uint32_t)(SPT * sc_part);
+    uint32_t aoff = 0;  // this thread's activation piece (token slot jj)
     if (jj < nt) {
       const int row = a.act_by_token ? pos_token(t0 + jj) : t0 + jj;
-      ahi = a.a_hi + (int64_t)row * a.K;
-      alo = a.a_lo ? a.a_lo + (int64_t)row * a.K : nullptr;
+      aoff = (uint32_t)((int64_t)row * a.K * 2) + 32u * pp;
     }
-    constexpr bool has_lo = LO;
+    const bool a_lane = jj < nt;
     // two register sets: tile kt+1 waits in one while tile kt+2 is in flight
     u32x4 rw[2][WPT];
-    u32x4 rs[2][TL::SCW / 8] = {};
+    uint32_t rs[2][2] = {};
     uint4 rh[2][2], rl[2][2];
     auto gload = [&](int ktl, int set) {
       const int kt = kt_begin + ktl;
+      const bool tile = ktl < nkt;
 #pragma unroll
-      for (int i = 0; i < WPT; ++i) {
-        const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
-        rw[set][i] = ld_stream(row_ptr(r) + (int64_t)kt * TL::WB + 16 * piece);
-      }
+      for (int i = 0; i < WPT; ++i)
+        rw[set][i] = buf_load<kAuxStream>(GU && i >= WPT / 2 ? res_u : res_g,
+                                          past(tile, woff[i] + (uint32_t)kt * TL::WB));
       if constexpr (TL::BLK) {
-        if (tid < BR) {
-          const int scoff = FMT == Q8_0 ? a.K : (a.K / 32) * 16;
-#pragma unroll
-          for (int h = 0; h < TL::SCW / 8; ++h)
-            rs[set][h] = *reinterpret_cast<const u32x4*>(row_ptr(tid) + scoff + 2 * TL::SCW * kt + 16 * h);
+        const uint32_t o = past(tile, soff + (uint32_t)(2 * TL::SCW * kt));
+        if constexpr (SPT == 8) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(res_s, o, 0, 0);
+          rs[set][0] = v[0];
+          rs[set][1] = v[1];
+        } else {
+          rs[set][0] = __builtin_amdgcn_raw_buffer_load_b32(res_s, o, 0, 0);
         }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        if (ahi) {
-          rh[set][i] = *reinterpret_cast<const uint4*>(ahi + kt * kKT + 16 * pp + 8 * i);
-          rl[set][i] = alo ? *reinterpret_cast<const uint4*>(alo + kt * kKT + 16 * pp + 8 * i)
-                           : make_uint4(0u, 0u, 0u, 0u);
-        } else {
-          rh[set][i] = make_uint4(0u, 0u, 0u, 0u);
-          rl[set][i] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        const uint32_t o = past(tile && a_lane, aoff + (uint32_t)kt * (2 * kKT) + 16u * i);
+        rh[set][i] = __builtin_bit_cast(uint4, buf_load(res_ah, o));
+        rl[set][i] = has_lo ? __builtin_bit_cast(uint4, buf_load(res_al, o)) : make_uint4(0u, 0u, 0u, 0u);
       }
     };
     auto lstore = [&](int buf, int set) {
@@ -242,21 +262,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
         *reinterpret_cast<u32x4*>(&s_w[buf][r * TL::WSTR + 16 * piece]) = rw[set][i];
       }
       if constexpr (TL::BLK) {
-        if (tid < BR) {
-          if constexpr (FMT == Q4_1) {
-            // (d, m) pairs step-major, [step][row][2]: a lane's four rows of
-            // a step are one 16-byte read
+        if constexpr (FMT == Q4_1) {
+          // (d, m) pairs step-major, [step][row][2]: a lane's four rows of a
+          // step are one 16-byte read; this thread holds steps 2 sc_part, +1
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2)
-              *reinterpret_cast<uint32_t*>(&s_sc[buf][2 * (s2 * BR + tid)]) = rs[set][s2 >> 2][s2 & 3];
-          } else {
-            // block scales step-major, [step][row]: the four consecutive rows
-            // of a lane's MFMA outputs read their step's scales as one 8-byte load
-            const u32x4 w = rs[set][0];
+          for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<uint32_t*>(&s_sc[buf][2 * ((2 * sc_part + j) * BR + sc_row)]) = rs[set][j];
+        } else {
+          // block scales step-major, [step][row]: the four consecutive rows
+          // of a lane's MFMA outputs read their step's scales as one 8-byte
+          // load; this thread holds SPT / 2 consecutive steps
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2)
-              s_sc[buf][s2 * BR + tid] = (uint16_t)(w[s2 >> 1] >> (16 * (s2 & 1)));
-          }
+          for (int j = 0; j < SPT / 2; ++j)
+            s_sc[buf][((SPT / 2) * sc_part + j) * BR + sc_row] = (uint16_t)(rs[set][j >> 1] >> (16 * (j & 1)));
         }
       }
       if constexpr (FMT == Q4_0 || FMT == Q4_1) {
@@ -324,22 +342,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_BF_WAVES
         }
       }
     };
-    // iteration kt: LDS buffer kt&1 holds tile kt, register set (kt+1)&1
-    // holds tile kt+1, tile kt+2 is loaded into set kt&1
+    // Loop top: LDS buffer 0 holds tile kt, register set 1 tile kt+1.  The
+    // loop runs while tile kt+2 exists, so its LDS stores are unconditional
+    // (a store skipped on some path would leave that path's loads pending
+    // at the loop top, and the compiled loop would wait for them there); the
+    // last one or two tiles are computed after it.
     gload(0, 0);
-    if (nkt > 1) gload(1, 1);
+    gload(1, 1);
     lstore(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < nkt; kt += 2) {
-      if (kt + 2 < nkt) gload(kt + 2, 0);
+    int kt = 0;
+    for (; kt + 2 < nkt; kt += 2) {
+      gload(kt + 2, 0);
       compute(0);
-      if (kt + 1 < nkt) lstore(1, 1);
+      lstore(1, 1);
       __syncthreads();
-      if (kt + 1 >= nkt) break;
-      if (kt + 3 < nkt) gload(kt + 3, 1);
+      gload(kt + 3, 1);
       compute(1);
-      if (kt + 2 < nkt) lstore(0, 0);
+      lstore(0, 0);
       __syncthreads();
+    }
+    compute(0);
+    if (kt + 1 < nkt) {
+      lstore(1, 1);
+      __syncthreads();
+      compute(1);
     }
 
     // 4-bit codes entered as 16 * value (Q4_1: its block sums as 16 * sum):
@@ -625,36 +652,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
   const int rb_first = blockIdx.x * a.R;
   const int nrb = min(a.R, nrb_all - rb_first);
   const int NT = nrb * nkt;
-  auto row_ptr = [&](int rbi, int r) -> const uint8_t* {
-    const int r0 = (rb_first + rbi) * RPB;
-    if (GU) {
-      const int f = min(r0 + (r % (BR / 2)), a.M - 1);
-      return (r < BR / 2 ? a.wq : a.wq2) + (int64_t)er.e * a.mat_bytes + (int64_t)f * rb;
-    }
-    return a.wq + (int64_t)er.e * a.mat_bytes + (int64_t)min(r0 + r, a.M - 1) * rb;
-  };
   auto act_row = [&](int jj) {
     const int pos = t0 + jj;
     return a.act_by_token ? (a.d.n_active == nullptr ? pos : a.d.pairs[pos] / a.d.k) : pos;
   };
   // staging: thread (jj, pp) moves bytes [16 pp, 16 pp + 16) of each digit plane of token slot jj
   const int jj = tid >> 4, pp = tid & 15;
-  const int8_t* dsrc = jj < nt ? a.digits + (int64_t)act_row(jj) * 4 * a.K : nullptr;
   if (tid < kTok) s_e[tid] = tid < nt ? a.expo[act_row(tid)] : 0;
+  // Tiles are read through buffer resources (offsets past a resource's end
+  // read zeros without a memory access), so empty token slots and the tiles
+  // past the last issue the same loads as the rest: no branch around a load,
+  // and the compiled loop waits only for the older of the two tiles in flight.
+  const int mat_len = (int)((int64_t)a.M * rb);
+  const rsrc_t res_g = make_res(a.wq + (int64_t)er.e * a.mat_bytes, mat_len);
+  const rsrc_t res_u = make_res((GU ? a.wq2 : a.wq) + (int64_t)er.e * a.mat_bytes, mat_len);
+  const int a_rows = a.act_by_token ? a.d.T : a.d.T * a.d.k;
+  const rsrc_t res_d = make_res(a.digits, (int)((int64_t)a_rows * 4 * a.K));
+  const bool d_lane = jj < nt;
+  const uint32_t doff = d_lane ? (uint32_t)((int64_t)act_row(jj) * 4 * a.K) + 16u * pp : 0u;
 
   u32x4 rw[2][WPT];
   uint4 rd[2][4];
   auto gload = [&](int ti, int set) {
     const int rbi = ti / nkt, kt = ti - rbi * nkt;
+    const bool tile = ti < NT;
+    const int r0 = (rb_first + rbi) * RPB;
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const int c = tid + 256 * i, r = c / (TL::WB / 16), piece = c % (TL::WB / 16);
-      rw[set][i] = ld_stream(row_ptr(rbi, r) + (int64_t)kt * TL::WB + 16 * piece);
+      const int f = min(r0 + (GU ? r % (BR / 2) : r), a.M - 1);
+      const uint32_t o = (uint32_t)((int64_t)f * rb) + (uint32_t)(kt * TL::WB + 16 * piece);
+      rw[set][i] = buf_load<kAuxStream>(GU && i >= WPT / 2 ? res_u : res_g, past(tile, o));
     }
 #pragma unroll
     for (int l = 0; l < 4; ++l)
-      rd[set][l] = dsrc ? *reinterpret_cast<const uint4*>(dsrc + (int64_t)l * a.K + kt * kKT + 16 * pp)
-                        : make_uint4(0u, 0u, 0u, 0u);
+      rd[set][l] = __builtin_bit_cast(uint4, buf_load(res_d, past(tile && d_lane, doff + (uint32_t)(l * a.K + kt * kKT))));
   };
   auto lstore = [&](int buf, int set) {
 #pragma unroll
@@ -738,10 +770,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
       }
     }
   };
-  gload(0, 0);
-  if (NT > 1) gload(1, 1);
-  lstore(0, 0);
-  __syncthreads();
   auto end_of_row_block = [&](int ti) {
     if ((ti + 1) % nkt == 0) {
       finish(ti / nkt);
@@ -751,18 +779,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MD_I8_WAVES
         for (int l = 0; l < 4; ++l) acc[rt][l] = i32x4{0, 0, 0, 0};
     }
   };
-  for (int ti = 0; ti < NT; ti += 2) {
-    if (ti + 2 < NT) gload(ti + 2, 0);
+  // Loop top: LDS buffer 0 holds tile ti, register set 1 tile ti+1; the loop
+  // runs while tile ti+2 exists, so its LDS stores are unconditional, and the
+  // last one or two tiles are computed after it.
+  gload(0, 0);
+  gload(1, 1);
+  lstore(0, 0);
+  __syncthreads();
+  int ti = 0;
+  for (; ti + 2 < NT; ti += 2) {
+    gload(ti + 2, 0);
     compute(0);
     end_of_row_block(ti);
-    if (ti + 1 < NT) lstore(1, 1);
+    lstore(1, 1);
     __syncthreads();
-    if (ti + 1 >= NT) break;
-    if (ti + 3 < NT) gload(ti + 3, 1);
+    gload(ti + 3, 1);
     compute(1);
     end_of_row_block(ti + 1);
-    if (ti + 2 < NT) lstore(0, 0);
+    lstore(0, 0);
     __syncthreads();
+  }
+  compute(0);
+  end_of_row_block(ti);
+  if (ti + 1 < NT) {
+    lstore(1, 1);
+    __syncthreads();
+    compute(1);
+    end_of_row_block(ti + 1);
   }
 }
 
