@@ -32,5 +32,5 @@ def orc_mt():
     import oracle
     if not os.path.exists(oracle.LIB):
         oracle.build()
-    o = oracle.Oracle(threads=min(8, os.cpu_count() or 1))
+    o = oracle.Oracle(threads=min(16, os.cpu_count() or 1))
     return o
