@@ -132,6 +132,28 @@ def test_ffn_special_codes_and_scales(orc_mt, fmt, T):
     assert_within(y.cpu().numpy(), y_ref, S, f"ffn {fmt} T={T}")
 
 
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_1"])
+@pytest.mark.parametrize("T", [17, 48, 100, 128])
+def test_ffn_dense_chunk_token_counts(orc_mt, fmt, T):
+    """A dense FFN over 17..128 tokens on the block formats (the grouped
+    GEMM in dense mode: one launch tile per 16 tokens, the last one ragged),
+    on matrices with special codes and scales and one token 300 times the
+    others, every token against the oracle."""
+    import moe_decode_amd as md
+    import torch
+    rng = np.random.default_rng([104, ("q8_0", "q4_0", "q4_1").index(fmt), T])
+    H, Fw = 1024, 768
+    g, u, d = (_special_matrix(rng, fmt, Fw, H), _special_matrix(rng, fmt, Fw, H), _special_matrix(rng, fmt, H, Fw))
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[T // 2] *= 300.0   # one token far larger than the others
+    ffn = md.FFN("silu", _upload(g), _upload(u), _upload(d))
+    y = md.ffn_forward(ffn, _t(x))
+    torch.cuda.synchronize()
+    y_ref, S = orc_mt.ffn(g, u, d, "silu", x)
+    say(f"[edge dense chunk] {fmt} T={T}")
+    assert_within(y.cpu().numpy(), y_ref, S, f"dense chunk {fmt} T={T}")
+
+
 # ---- canaries ---------------------------------------------------------------
 
 _GUARD = 256  # elements (1 KiB) of guard on each side
