@@ -114,6 +114,7 @@ struct MoeWs {
   size_t x_hi, x_lo, h_hi, h_lo, hs_hi, hs_lo;  // bf16 pairs of the prefill path (block formats)
   size_t x_dig, x_exp, h_dig, h_exp, hs_dig, hs_exp;  // int8 digit planes (per-row formats)
   size_t xs_dig, xs_exp;  // x digits in the shared expert's order
+  size_t xs_hi, xs_lo;    // x as bf16 pairs for the shared expert (its own: it may run on another stream)
   size_t xd, sxd, hd, shd;  // digit planes of x and h for the one-token kernels (routed, shared formats)
   size_t rcopy;             // the residual's copy where y, which it may be, is written before it is added
 };
@@ -179,6 +180,8 @@ MoeWs moe_ws(const md_moe_layer* L, int T) {
       w.hs_exp = take(sizeof(int) * (size_t)T);
       w.xs_dig = take(4 * (size_t)T * H);
       w.xs_exp = take(sizeof(int) * (size_t)T);
+      w.xs_hi = take(2 * (size_t)T * H);
+      w.xs_lo = take(2 * (size_t)T * H);
     }
   }
   w.total = off;
@@ -526,8 +529,12 @@ static SideStream* side_stream() {
     hipStream_t st = nullptr;
     hipEvent_t a = nullptr, b = nullptr;
     if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+    // both streams are on this device: the kernels' own end-of-kernel
+    // releases make their writes visible to the other stream, so the events
+    // skip the system-scope fence (a writeback and invalidation of every
+    // XCD's L2 at each fork and join)
+    const unsigned fl = hipEventDisableTiming | hipEventDisableSystemFence;
+    if (hipEventCreateWithFlags(&a, fl) != hipSuccess || hipEventCreateWithFlags(&b, fl) != hipSuccess) {
       if (a) (void)hipEventDestroy(a);
       (void)hipStreamDestroy(st);
       return nullptr;
@@ -687,15 +694,19 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
   // shared expert: independent of the routing, enqueued first
   ChunkAct xa{nullptr, nullptr, nullptr, nullptr};
   if (!mark(MD_STAGE_SHARED, ev0)) return hip_fail(e, "event record");
+  const md::RouterPlan rp = md::router_plan(T, H, E);
+  // the router GEMM writes the routed experts' bf16 pair of x from the tiles
+  // it stages (one launch less before the grouped GEMMs)
+  const bool pair_by_router = rp.gemm && !row_type(fmt);
   {
     // the activation forms the chunk path's kernels need (enqueued with the
     // shared expert's stage; pointers set up for every stage)
-    const bool need_pair = !row_type(fmt) || (L->has_shared && !row_type(L->shared.gate.type));
+    const bool need_pair = !row_type(fmt);
     const bool need_dig = row_type(fmt);
     if (need_pair) {
       xa.hi = static_cast<u16*>(P(w.x_hi));
       xa.lo = static_cast<u16*>(P(w.x_lo));
-      if (want(MD_STAGE_SHARED)) {
+      if (want(MD_STAGE_SHARED) && !pair_by_router) {
         e = md::launch_split_bf16(x, (int64_t)T * H, static_cast<u16*>(P(w.x_hi)), static_cast<u16*>(P(w.x_lo)),
                                   stream);
         if (e != hipSuccess) return hip_fail(e, "split launch");
@@ -742,6 +753,11 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
       if (e != hipSuccess) return hip_fail(e, "digit launch");
       xs.dig = static_cast<int8_t*>(P(w.xs_dig));
       xs.expo = static_cast<int*>(P(w.xs_exp));
+    } else {  // its own bf16 pair of x, made on its stream
+      xs.hi = static_cast<u16*>(P(w.xs_hi));
+      xs.lo = static_cast<u16*>(P(w.xs_lo));
+      e = md::launch_split_bf16(x, (int64_t)T * H, static_cast<u16*>(P(w.xs_hi)), static_cast<u16*>(P(w.xs_lo)), sst);
+      if (e != hipSuccess) return hip_fail(e, "split launch");
     }
     s = run_ffn_mfma(&L->shared, xs, T, static_cast<float*>(P(w.h_s)), static_cast<u16*>(P(w.hs_hi)),
                      static_cast<u16*>(P(w.hs_lo)), static_cast<int8_t*>(P(w.hs_dig)), static_cast<int*>(P(w.hs_exp)),
@@ -749,10 +765,11 @@ static md_status moe_forward(const md_moe_layer* L, const float* x, int32_t T, f
     if (s != MD_OK) return s;
   }
   if (!mark(MD_STAGE_SHARED, ev1) || !mark(MD_STAGE_ROUTER, ev0)) return hip_fail(e, "event record");
-  const md::RouterPlan rp = md::router_plan(T, H, E);
   double* part = static_cast<double*>(P(w.part));
   if (want(MD_STAGE_ROUTER)) {
-    e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream);
+    e = md::launch_router(x, T, H, L->W_r, E, rp, part, md::DigJob{}, md::DigJob{}, stream,
+                          pair_by_router ? static_cast<u16*>(P(w.x_hi)) : nullptr,
+                          pair_by_router ? static_cast<u16*>(P(w.x_lo)) : nullptr);
     if (e != hipSuccess) return hip_fail(e, "router launch");
   }
   if (!mark(MD_STAGE_ROUTER, ev1) || !mark(MD_STAGE_SELECT, ev0)) return hip_fail(e, "event record");

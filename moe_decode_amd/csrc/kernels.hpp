@@ -99,9 +99,11 @@ int router_splits(int H, int E);
 hipError_t launch_router_part(const float* x, int T, int H, const float* Wr, int E, int S, double* part,
                               const DigJob& j0, const DigJob& j1, hipStream_t st);
 // Also runs the digit jobs j0, j1 (small-T plan only; the GEMM plan rejects
-// them).
+// them).  x_hi, x_lo (GEMM plan only, nullable): also write x as bf16 pairs
+// (hi = bf16(x), lo = bf16(x - hi)) from the tiles the router stages.
 hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, const RouterPlan& p, double* part,
-                         const DigJob& j0, const DigJob& j1, hipStream_t st);
+                         const DigJob& j0, const DigJob& j1, hipStream_t st, unsigned short* x_hi = nullptr,
+                         unsigned short* x_lo = nullptr);
 hipError_t launch_select(const double* part, const RouterPlan& p, const float* bias, int T, int E, int k,
                          float* logits, int* idx, float* gates, hipStream_t st);
 hipError_t launch_dispatch(const int* idx, int T, int E, int k, const DispOut& d, hipStream_t st);

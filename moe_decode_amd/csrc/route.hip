@@ -13,6 +13,8 @@
 
 namespace md {
 
+typedef unsigned short u16;
+
 // -------------------------------------------------------------- router
 
 // Chunk router: logits partials of many tokens as a GEMM on the fp64 matrix
@@ -30,9 +32,14 @@ constexpr int kRKC = 32;  // K per LDS stage
 // D[4 v + lane / 16][lane % 16] in element v.  The next stage's tiles are
 // fetched into registers while a stage is used.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+//
+// x_hi, x_lo (nullable): the blocks of the first expert tile also write the
+// bf16 pair of every x value they stage (together they stage each value
+// once), so the grouped GEMMs' activation forms need no launch of their own.
 __global__ __launch_bounds__(256) void k_router_mfma(const float* __restrict__ x, int T, int H,
                                                      const float* __restrict__ Wr, int E, int Ks,
-                                                     double* __restrict__ part) {
+                                                     double* __restrict__ part, u16* __restrict__ x_hi,
+                                                     u16* __restrict__ x_lo) {
   __shared__ float sw[kRKC][kRG + 1];
   __shared__ float sx[kRKC][kRG + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -65,6 +72,19 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float* __restrict__ x
       sw[4 * c4 + 2][row] = pw[r].z; sw[4 * c4 + 3][row] = pw[r].w;
       sx[4 * c4 + 0][row] = px[r].x; sx[4 * c4 + 1][row] = px[r].y;
       sx[4 * c4 + 2][row] = px[r].z; sx[4 * c4 + 3][row] = px[r].w;
+      if (x_hi && blockIdx.x == 0 && t0 + row < T) {
+        const float v[4] = {px[r].x, px[r].y, px[r].z, px[r].w};
+        u16 h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 b = (__bf16)v[i];
+          h[i] = __builtin_bit_cast(u16, b);
+          l[i] = __builtin_bit_cast(u16, (__bf16)(v[i] - (float)b));
+        }
+        const int64_t o = (int64_t)(t0 + row) * H + kc + 4 * c4;
+        *reinterpret_cast<ushort4*>(x_hi + o) = make_ushort4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<ushort4*>(x_lo + o) = make_ushort4(l[0], l[1], l[2], l[3]);
+      }
     }
     __syncthreads();
     if (kc + kRKC < kbeg + Ks) fetch(kc + kRKC);
@@ -129,11 +149,14 @@ RouterPlan router_plan(int T, int H, int E, bool pairs) {
 }
 
 hipError_t launch_router(const float* x, int T, int H, const float* Wr, int E, const RouterPlan& p, double* part,
-                         const DigJob& j0, const DigJob& j1, hipStream_t st) {
-  if (!p.gemm) return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, st);
-  if (j0.x || j1.x) return hipErrorInvalidValue;
+                         const DigJob& j0, const DigJob& j1, hipStream_t st, u16* x_hi, u16* x_lo) {
+  if (!p.gemm) {
+    if (x_hi || x_lo) return hipErrorInvalidValue;
+    return launch_router_part(x, T, H, Wr, E, p.S, part, j0, j1, st);
+  }
+  if (j0.x || j1.x || (x_hi == nullptr) != (x_lo == nullptr)) return hipErrorInvalidValue;
   const dim3 grid((E + kRG - 1) / kRG, (T + kRG - 1) / kRG, p.S);
-  hipLaunchKernelGGL(k_router_mfma, grid, dim3(256), 0, st, x, T, H, Wr, E, H / p.S, part);
+  hipLaunchKernelGGL(k_router_mfma, grid, dim3(256), 0, st, x, T, H, Wr, E, H / p.S, part, x_hi, x_lo);
   return hipGetLastError();
 }
 
@@ -152,16 +175,18 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ part,
   const int t = blockIdx.x, e = threadIdx.x, lane = threadIdx.x & 63;
   if (e < E) {
     const double* p = part + t * pt + e * pe;
+    // up to 32 slices' partials loaded before the first add (one memory
+    // round trip instead of one per eight), then added in slice order
     double a = 0.0;
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-      double v[8];
+    for (int s = 0; s < S; s += 32) {
+      const int n = S - s < 32 ? S - s : 32;
+      double v[32];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = p[(s + i) * ps];
+      for (int i = 0; i < 32; ++i) v[i] = i < n ? p[(int64_t)(s + i) * ps] : 0.0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a += v[i];
+      for (int i = 0; i < 32; ++i)
+        if (i < n) a += v[i];
     }
-    for (; s < S; ++s) a += p[s * ps];
     if (bias) a += (double)bias[e];
     const float l = (float)a;
     if (logits) logits[(int64_t)t * E + e] = l;
