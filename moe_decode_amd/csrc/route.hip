@@ -234,11 +234,16 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int* __restrict__ idx, 
   __shared__ int cnt[256], poff[256], apos[256], ioff[256];
   __shared__ int s_items;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // one pair per thread (T * k <= 1024, checked at launch); its expert is
+  // read once and kept for the rank pass at the end
+  const int p = threadIdx.x;
+  const bool has_pair = p < T * k;
+  const int my_e = has_pair ? idx[p] : 0;
   for (int i = threadIdx.x; i < 256 * 4; i += 1024) (&mask[0][0])[i] = 0u;
   __syncthreads();
-  for (int p = threadIdx.x; p < T * k; p += 1024) {
+  if (has_pair) {
     const int t = p / k;
-    atomicOr(&mask[idx[p]][t >> 5], 1u << (t & 31));
+    atomicOr(&mask[my_e][t >> 5], 1u << (t & 31));
   }
   __syncthreads();
   if (threadIdx.x < 256) {
@@ -281,8 +286,8 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int* __restrict__ idx, 
       d.items[ioff[e] + i] = make_int4(e, poff[e] + i * kTokTile, poff[e] + cnt[e], 0);
   }
   for (int i = s_items + (int)threadIdx.x; i < d.n_items_max; i += 1024) d.items[i] = make_int4(-1, 0, 0, 0);
-  for (int p = threadIdx.x; p < T * k; p += 1024) {
-    const int t = p / k, e = idx[p];
+  if (has_pair) {
+    const int t = p / k, e = my_e;
     int rank = 0;
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(mask[e][w]);
     rank += __popc(mask[e][t >> 5] & ((1u << (t & 31)) - 1u));
@@ -293,6 +298,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int* __restrict__ idx, 
 }
 
 hipError_t launch_dispatch(const int* idx, int T, int E, int k, const DispOut& d, hipStream_t st) {
+  if (T < 1 || k < 1 || T * k > 1024 || T > 128 || E > 256) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(1024), 0, st, idx, T, E, k, d);
   return hipGetLastError();
 }
