@@ -3,7 +3,9 @@ library's side stream, beside the routing kernels, and joins the caller's
 stream before the combine.  The results must be those of the same kernels on
 the caller's stream alone (the timed entry point never forks), bit for bit,
 also for calls chained without synchronisation, where each call reads the
-previous one's output, and for the residual form."""
+previous one's output, and for the residual form; on the c3 layer (Q4_0
+experts, Q8_0 shared expert) and on a Q8_0 layer with a Q4_1 shared
+expert."""
 import numpy as np
 import pytest
 
@@ -12,6 +14,21 @@ from synth import workloads as W
 from .gpu_common import moe_layer, require_gpu, say
 
 pytestmark = pytest.mark.gpu
+
+# Q8_0 experts with a Q4_1 shared expert (other kernels on both streams)
+_SIDE = W.MoESpec("side_q8_sh_q41", 54, 1536, 512, 16, 2, "gelu_tanh", "q8_0", (1e-3, 1e-2), 0.05, None, (1,),
+                  shared_F=1536, shared_fmt="q4_1", shared_d_range=(1e-3, 2e-2))
+_side_layer = {}
+LAYERS = ["c3", "side_q8_sh_q41"]
+
+
+def _layer(name):
+    if name == "c3":
+        return W.spec("c3"), moe_layer("c3")
+    if name not in _side_layer:
+        from synth.device import device_moe
+        _side_layer[name] = device_moe(_SIDE)
+    return _SIDE, _side_layer[name]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -29,13 +46,13 @@ def _one_stream(md, layer, x, y, idx, gates, ws):
     md.moe_layer_forward_timed(layer, x, "shared", a, b, y=y, idx=idx, gates=gates, workspace=ws)
 
 
+@pytest.mark.parametrize("name", LAYERS)
 @pytest.mark.parametrize("T", [17, 33, 128])
-def test_side_stream_gives_the_same_bits(T):
+def test_side_stream_gives_the_same_bits(name, T):
     import moe_decode_amd as md
     import torch
-    say(f"[side] c3 T={T}")
-    sp = W.spec("c3")
-    layer = moe_layer("c3")
+    say(f"[side] {name} T={T}")
+    sp, layer = _layer(name)
     x = torch.from_numpy(W.moe_x(sp, T)).cuda()
     ws = torch.empty(md.moe_workspace_size(layer, T), dtype=torch.uint8, device="cuda")
     y1, y2 = (torch.empty(T, sp.H, device="cuda") for _ in range(2))
@@ -48,16 +65,16 @@ def test_side_stream_gives_the_same_bits(T):
     assert torch.equal(y1, y2)
 
 
-def test_chained_calls_without_synchronisation():
+@pytest.mark.parametrize("name", LAYERS)
+def test_chained_calls_without_synchronisation(name):
     """Four calls, each on the previous output (through a tanh on the same
     stream, which keeps the values in range), enqueued back to back on one
     stream reusing one workspace, against the same chain on one stream."""
     import moe_decode_amd as md
     import torch
     T, n = 128, 4
-    say(f"[side] c3 chain of {n} x T={T}")
-    sp = W.spec("c3")
-    layer = moe_layer("c3")
+    say(f"[side] {name} chain of {n} x T={T}")
+    sp, layer = _layer(name)
     x0 = torch.from_numpy(W.moe_x(sp, T)).cuda() * 0.25
     ws = torch.empty(md.moe_workspace_size(layer, T), dtype=torch.uint8, device="cuda")
     idx = torch.empty(T, sp.k, dtype=torch.int32, device="cuda")
@@ -79,15 +96,15 @@ def test_chained_calls_without_synchronisation():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_residual_form_on_the_side_stream():
+@pytest.mark.parametrize("name", LAYERS)
+def test_residual_form_on_the_side_stream(name):
     """residual + layer(x) with the residual being y itself, against the
     layer on one stream followed by the add."""
     import moe_decode_amd as md
     import torch
     T = 128
-    say(f"[side] c3 residual T={T}")
-    sp = W.spec("c3")
-    layer = moe_layer("c3")
+    say(f"[side] {name} residual T={T}")
+    sp, layer = _layer(name)
     x = torch.from_numpy(W.moe_x(sp, T)).cuda()
     ws = torch.empty(md.moe_workspace_size(layer, T), dtype=torch.uint8, device="cuda")
     idx = torch.empty(T, sp.k, dtype=torch.int32, device="cuda")
@@ -103,7 +120,8 @@ def test_residual_form_on_the_side_stream():
     assert torch.equal(y, out)
 
 
-def test_graph_capture_takes_the_side_stream_in():
+@pytest.mark.parametrize("name", LAYERS)
+def test_graph_capture_takes_the_side_stream_in(name):
     """A chunk forward captured in a HIP graph from a torch stream (the side
     stream joins the capture through the fork event and leaves it through
     the join), replayed three times with eager forwards of other inputs in
@@ -111,9 +129,8 @@ def test_graph_capture_takes_the_side_stream_in():
     import moe_decode_amd as md
     import torch
     T = 128
-    say(f"[side] c3 graph capture T={T}")
-    sp = W.spec("c3")
-    layer = moe_layer("c3")
+    say(f"[side] {name} graph capture T={T}")
+    sp, layer = _layer(name)
     x = torch.from_numpy(W.moe_x(sp, T)).cuda()
     x_other = torch.tanh(x * 3.0)
     ws = torch.empty(md.moe_workspace_size(layer, T), dtype=torch.uint8, device="cuda")
