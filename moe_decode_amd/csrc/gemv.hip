@@ -21,27 +21,46 @@ namespace md {
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / 64;
 
-template <int FMT, int XT, int L, int R, int B>
-MD_DEV void rows_dot(const uint8_t* const (&rowp)[R], int K, int c0, int c1, int t,
-                     const void* const (&xp)[B], float (&acc)[R][B]) {
+// chunks cs[0..N) of the R rows (all in range) against the activations,
+// their weight loads issued together; sums in chunk order
+template <int FMT, int XT, int R, int B, int N>
+MD_DEV void chunks_dot(const uint8_t* const (&rowp)[R], int K, const int (&cs)[N], const void* const (&xp)[B],
+                       float (&acc)[R][B]) {
   constexpr int W = Fmt<FMT>::WPC;
-#pragma unroll 2
-  for (int c = c0 + t; c < c1; c += L) {
-    u32x4 w[R];
-    float sc[R];
+  u32x4 w[N][R];
+  float sc[N][R], mn[N][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = ld_stream(rowp[r] + 16 * (int64_t)c);
+  for (int u = 0; u < N; ++u)
 #pragma unroll
-    for (int r = 0; r < R; ++r) sc[r] = chunk_scale<FMT>(rowp[r], K, c);
-    float mn[R];
-    if constexpr (FMT == Q4_1) {
+    for (int r = 0; r < R; ++r) w[u][r] = ld_stream(rowp[r] + 16 * (int64_t)cs[u]);
 #pragma unroll
-      for (int r = 0; r < R; ++r) mn[r] = chunk_min_q4_1(rowp[r], K, c);
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      sc[u][r] = chunk_scale<FMT>(rowp[r], K, cs[u]);
+      if constexpr (FMT == Q4_1) mn[u][r] = chunk_min_q4_1(rowp[r], K, cs[u]);
     }
+  // one token, at most 64 activations in all: those of every chunk loaded here too
+  constexpr bool XPRE = B == 1 && N > 1 && N * W <= 64;
+  float xpre[XPRE ? N : 1][W];
+  if constexpr (XPRE) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) load_x<FMT, XT>(xp[0], cs[u], xpre[u]);
+  }
+  // keep every load above issued before the first product (the scheduler
+  // would otherwise interleave them with the products and wait on each)
+  if constexpr (N > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float xv[W];
-      load_x<FMT, XT>(xp[b], c, xv);
+      if constexpr (XPRE) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) xv[i] = xpre[u][i];
+      } else {
+        load_x<FMT, XT>(xp[b], cs[u], xv);
+      }
       float sx = 0.f;  // Q4_1: the block's sum of activations, for its minimum
       if constexpr (FMT == Q4_1) {
 #pragma unroll
@@ -49,12 +68,39 @@ MD_DEV void rows_dot(const uint8_t* const (&rowp)[R], int K, int c0, int c1, int
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float d = dot_chunk<FMT>(w[r], xv);
+        const float d = dot_chunk<FMT>(w[u][r], xv);
         if constexpr (Fmt<FMT>::ROW) acc[r][b] += d;
-        else if constexpr (FMT == Q4_1) acc[r][b] = fmaf(sc[r], d, fmaf(mn[r], sx, acc[r][b]));
-        else acc[r][b] = fmaf(sc[r], d, acc[r][b]);
+        else if constexpr (FMT == Q4_1) acc[r][b] = fmaf(sc[u][r], d, fmaf(mn[u][r], sx, acc[r][b]));
+        else acc[r][b] = fmaf(sc[u][r], d, acc[r][b]);
       }
     }
+  }
+}
+
+// Lane t of a group of L sums chunks c0 + t, c0 + t + L, ... below c1, in
+// order.  One row of one or two tokens (long rows: one row per lane group):
+// passes of 64 weights' chunks (four Q8_0/int8 chunks, two 4-bit ones) with
+// all their loads in flight; two rows of 16-weight chunks for one token: two
+// chunks of each; then the last few chunks one at a time, as for the other
+// shapes, whose loads the loop's unrolling overlaps.
+template <int FMT, int XT, int L, int R, int B>
+MD_DEV void rows_dot(const uint8_t* const (&rowp)[R], int K, int c0, int c1, int t,
+                     const void* const (&xp)[B], float (&acc)[R][B]) {
+  constexpr int W = Fmt<FMT>::WPC;
+  constexpr int U = (R == 1 && B <= 2) ? 64 / W : (R == 2 && B == 1 && W <= 16) ? 2 : 1;
+  int c = c0 + t;
+  if constexpr (U > 1) {
+    for (; c + (U - 1) * L < c1; c += U * L) {
+      int cs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) cs[u] = c + u * L;
+      chunks_dot<FMT, XT, R, B, U>(rowp, K, cs, xp, acc);
+    }
+  }
+#pragma unroll 2
+  for (; c < c1; c += L) {
+    const int cs[1] = {c};
+    chunks_dot<FMT, XT, R, B, 1>(rowp, K, cs, xp, acc);
   }
 }
 
